@@ -1,0 +1,213 @@
+"""Benchmark of the MXFP4 + SiTU routed-MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+
+A step is one call of the whole layer (routing, [MXFP8 quantization],
+FC1 + SiTU, FC2, combine) over one batch of synthetic tokens already
+resident in HBM.  The default workload is the TP8-shard decode batch the
+metric is quoted on (config 1: 64 tokens, hidden 3584, 896 local experts,
+intermediate 384, top-16, w4a16); --config selects another shard shape.
+
+Prints one JSON line: tokens/s, ms per step, the roofline of the dominant
+kernel (algorithmic bytes or flops per launch over its average duration
+from HIP events on the stream it runs on), per-stage times, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
+STAGES = ("route", "quantize", "fc1", "fc2", "combine")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_work(spec, counts, tokens_used):
+    """Bytes and flops the layer must move / compute, per stage."""
+    T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
+    counts = np.asarray(counts, np.int64)
+    A = int(np.count_nonzero(counts))
+    P = int(counts.sum())
+    w4a8 = spec["mode"] == "w4a8"
+    fc1_w = 2 * I * (H // 2 + H // 32)              # packed E2M1 + E8M0 per expert
+    fc2_w = H * (I // 2 + I // 32)
+    x_row = H + H // 32 if w4a8 else 2 * H          # the FC1 input row as the kernel reads it
+    h_row = I + I // 32 if w4a8 else 2 * I
+    work = {
+        "A": A, "P": P,
+        "fc1_bytes": A * fc1_w + tokens_used * x_row + P * h_row,
+        "fc2_bytes": A * fc2_w + P * h_row + P * H * 4,
+        "fc1_flops": 2.0 * P * H * 2 * I,
+        "fc2_flops": 2.0 * P * I * H,
+        "layer_bytes": A * (fc1_w + fc2_w) + T * 2 * H + T * k * 6 + T * H * 4,
+        "quantize_bytes": T * 2 * H + T * (H + H // 32) if w4a8 else 0,
+    }
+    return work
+
+
+def cpu_baseline(inp, spec, budget_s=15.0):
+    """The oracle (float32 mode, as it stands) on a bounded sample of tokens."""
+    from oracle import moe as M
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d.get("num_threads") for d in threadpool_info() if d.get("user_api") == "blas"]
+        threads = int(blas[0]) if blas else os.cpu_count()
+    except Exception:
+        threads = os.cpu_count()
+    cores = len(os.sched_getaffinity(0))
+    T = spec["T"]
+    n = min(T, 4)
+    tokens = np.arange(n)
+    t0 = time.perf_counter()
+    M.moe_forward(inp, local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
+                  act_mode=spec["mode"], precision="f32", tokens=tokens)
+    dt = time.perf_counter() - t0
+    if dt < budget_s / 3 and n < T:
+        n = int(min(T, max(n + 1, n * budget_s / max(dt, 1e-3) * 0.6)))
+        tokens = np.arange(n)
+        t0 = time.perf_counter()
+        M.moe_forward(inp, local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
+                      act_mode=spec["mode"], precision="f32", tokens=tokens)
+        dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the same batch, float32 numpy/OpenBLAS oracle, "
+                      f"{dt:.1f} s wall, {threads} BLAS threads on {cores} host cores"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer computes one TP/EP shard's partial output "
+              f"on one MI355X (the cross-GPU all-reduce is the caller's); --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import block_scaled_mxfp4_amd as B
+    import synthetic as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = S.spec_of(args.config)
+    _log(f"generating inputs for config {args.config} ({spec['name']})")
+    t0 = time.perf_counter()
+    inp = S.generate(spec)
+    _log(f"generated in {time.perf_counter() - t0:.1f} s")
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    packed = inp.get("topk_packed") is not None
+    T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
+    prob = B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
+                          local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
+                          act_mode=spec["mode"], topk_packed=packed, out_dtype="f32")
+    plan = B.situ_moe_plan(prob)
+    tens = dict(hidden_states=d(inp["hidden_states"]), w1=d(inp["w1"]), w1_scale=d(inp["w1_scale"]),
+                w2=d(inp["w2"]), w2_scale=d(inp["w2_scale"]), situ_beta=d(inp["situ_beta"]),
+                situ_linear_beta=d(inp["situ_linear_beta"]), alpha_gate=d(inp["alpha_gate"]),
+                alpha_up=d(inp["alpha_up"]), out=torch.empty((T, H), dtype=torch.float32, device=dev))
+    if packed:
+        tens["topk_packed"] = d(inp["topk_packed"])
+    else:
+        tens["topk_ids"] = d(inp["topk_ids"])
+        tens["topk_weights"] = d(inp["topk_weights"])
+    ts = B.make_tensors(prob, **tens)
+    ws = B.new_workspace(plan, dev)
+    stream = torch.cuda.current_stream(dev)
+    _log(f"plan: fc1={B.situ_moe_tactic_name(plan.fc1_tactic)} fc2={B.situ_moe_tactic_name(plan.fc2_tactic)} "
+         f"block_m={plan.block_m} workspace={plan.workspace_bytes / 2**20:.1f} MiB")
+
+    for _ in range(args.warmup):
+        B.situ_moe_run(plan, ts, ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        B.situ_moe_run_profiled(plan, ts, ws, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / K
+    stage_ms = {}
+    for j, name in enumerate(STAGES):
+        stage_ms[name] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+
+    counts = B.workspace_view(plan, ws, "counts", torch.int32, (spec["E_l"],)).cpu().numpy()
+    inv = B.workspace_view(plan, ws, "inv", torch.int32, (T * k,)).cpu().numpy().reshape(T, k)
+    tokens_used = int(np.count_nonzero((inv >= 0).any(axis=1)))
+    work = algorithmic_work(spec, counts, tokens_used)
+
+    w4a8 = spec["mode"] == "w4a8"
+    dom = "fc1" if stage_ms["fc1"] >= stage_ms["fc2"] else "fc2"
+    if not w4a8:
+        # decode shapes stream the active experts' weights once: HBM-bound
+        achieved = work[f"{dom}_bytes"] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes_per_launch": work[f"{dom}_bytes"], "avg_launch_ms": round(stage_ms[dom], 5)}
+    else:
+        achieved = work[f"{dom}_flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS["mxfp8"]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "algorithmic_flops_per_launch": work[f"{dom}_flops"], "avg_launch_ms": round(stage_ms[dom], 5)}
+    layer_gbs = work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8" if w4a8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{spec['name']}_{spec['mode']}", "tokens": T, "hidden": H, "intermediate": I,
+                   "experts_global": spec["E_g"], "experts_local": spec["E_l"],
+                   "local_expert_offset": spec["off"], "top_k": k, "topk_format": "packed" if packed else "ids+weights",
+                   "active_local_experts": work["A"], "local_pairs": work["P"],
+                   "fc1_tactic": B.situ_moe_tactic_name(plan.fc1_tactic),
+                   "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic)},
+        "roofline": roof,
+        "stage_ms": {kk: round(v, 5) for kk, v in stage_ms.items()},
+        "layer_hbm_gbs": round(layer_gbs, 1),
+        "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(inp, spec)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

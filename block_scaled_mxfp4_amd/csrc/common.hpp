@@ -1,0 +1,125 @@
+// Device helpers shared by the gfx950 kernels of the MXFP4 + SiTU MoE layer.
+//
+// Formats (OCP Microscaling Formats v1.0, "Scale data type" and "Element
+// data types"): E2M1 elements packed two per byte with the low nibble the
+// even element; E8M0 scales 2^(c-127); E4M3 (FN) elements with bias 7,
+// max 448; bf16 is the upper half of an IEEE binary32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace situ {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round a float to the nearest bf16, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E8M0 scale code of an MXFP8 (E4M3) block from the block's |max|:
+// floor(log2(amax)) - 8 + 127, clamped at 0 (an all-zero or tiny block).
+// The exponent field of a float is floor(log2) + 127 for normal values, and
+// every block with a subnormal amax clamps to 0 as well.
+__device__ __forceinline__ uint32_t e8m0_code_for_e4m3(float amax) {
+  int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
+  int c = ef - 8;
+  return (uint32_t)(c < 0 ? 0 : c);
+}
+
+// E4M3 code of v (finite, already divided by the block scale), nearest
+// value with ties to even, saturating to +-448; -0 and values that round
+// to zero give +0.  Exact: every step below is exact in binary32.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of step 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);    // 0..8; 8 is the smallest normal, code 0x08
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;   // -6..8
+    float m = __builtin_ldexpf(a, 3 - e);                     // [8, 16)
+    uint32_t q = (uint32_t)__builtin_rintf(m);                // 8..16
+    if (q == 16u) { q = 8u; e += 1; }
+    code = ((uint32_t)(e + 7) << 3) | (q - 8u);
+  }
+  return code == 0u ? 0u : (code | sign);
+}
+
+// 2^(c-127) as a float for an E8M0 code c in [1, 254]; c = 0 gives 2^-127
+// (a binary32 subnormal) and is built exactly as well.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return c == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(c << 23);
+}
+
+// Eight E2M1 values (one dword, low nibble first) times 2^(c-127) as eight
+// bf16 in four dwords (element 2i in the low half of dword i).  The scaled
+// convert multiplies each E2M1 value by the float scale; the product is
+// exact in bf16 for every scale code the layer's weights carry.
+__device__ __forceinline__ void fp4x8_to_bf16x8(uint32_t w, float scale, uint32_t out[4]) {
+  bf16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  out[0] = __builtin_bit_cast(uint32_t, r0);
+  out[1] = __builtin_bit_cast(uint32_t, r1);
+  out[2] = __builtin_bit_cast(uint32_t, r2);
+  out[3] = __builtin_bit_cast(uint32_t, r3);
+}
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16];
+// the result D[4*(l/16) + i][l%16] sits in element i of lane l.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const uint32_t a[4], const uint32_t b[4], f32x4 c) {
+  bf16x8 av = __builtin_bit_cast(bf16x8, i32x4{(int)a[0], (int)a[1], (int)a[2], (int)a[3]});
+  bf16x8 bv = __builtin_bit_cast(bf16x8, i32x4{(int)b[0], (int)b[1], (int)b[2], (int)b[3]});
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// D(16x16) += (A * 2^sa) (16x128, E2M1) * (B * 2^sb) (128x16, E4M3), fp32 accumulate.
+// Operand layouts, measured on gfx950 with one-hot operands and scales:
+//  - A (E2M1, 4 dwords): lane l holds row l%16, K = 32*(l/16) + e for nibble
+//    e = 0..31, low nibble first;
+//  - B (E4M3, 8 dwords): lane l holds column l%16, K = 16*(l/16) + e in bytes
+//    e = 0..15 and K = 64 + 16*(l/16) + (e - 16) in bytes e = 16..31;
+//  - the E8M0 scale of lane l applies, for both operands, to the K block
+//    32*(l/16) .. +31 of its row (A) or column (B).
+__device__ __forceinline__ f32x4 mfma_scale_fp4_fp8(const uint32_t a[4], const uint32_t b[8], uint32_t sa,
+                                                     uint32_t sb, f32x4 c) {
+  i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+  // format codes: 4 = FP4 E2M1 (A), 0 = FP8 E4M3 (B)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  // 1 / (1 + e^-z) with the hardware exp2 and reciprocal; saturates cleanly
+  // to 0 and 1 because exp2 overflows to +inf and 1/inf = 0.
+  float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)], with each
+// c*tanh(x/c) written as 2c*sigmoid(2x/c) - c so that no tanh is evaluated
+// (the identity the MegaMoE commit "SiTU in the kernel" uses).
+__device__ __forceinline__ float situ_act(float g, float u, float b, float lb, float inv_b, float inv_lb) {
+  float tg = 2.0f * b * sigmoid_fast(2.0f * g * inv_b) - b;
+  float tu = 2.0f * lb * sigmoid_fast(2.0f * u * inv_lb) - lb;
+  return tg * sigmoid_fast(g) * tu;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+}  // namespace situ

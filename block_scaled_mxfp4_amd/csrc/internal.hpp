@@ -1,0 +1,94 @@
+// Internal interfaces between the host planner (situ_moe_api.cpp) and the
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace situ {
+
+constexpr int kMaxLocalExperts = 1024;
+
+struct RouteArgs {
+  const int32_t* ids;      // [T*k] or null when packed
+  const int32_t* packed;   // [T*k] or null
+  int64_t TK;
+  int32_t off, E_l, block_m;
+  int32_t* counts;         // [E_l]
+  int32_t* offsets;        // [E_l+1]
+  int32_t* mtiles;         // [E_l+1]
+  int32_t* tile_expert;    // [max_mtiles]
+  int32_t* perm;           // [TK]
+  int32_t* inv;            // [TK]
+};
+
+struct QuantArgs {
+  const uint16_t* x;       // bf16 [rows, cols]
+  uint8_t* codes;          // [rows, cols]
+  uint8_t* scales;         // [rows, cols/32]
+  int64_t rows;
+  int32_t cols;
+};
+
+// Grouped GEMM arguments shared by FC1 and FC2.  Rows of the A side (the
+// token-expert pairs) are found through the tile list built by the router.
+struct GemmArgs {
+  // activations of the K loop: FC1 reads the token rows x[t] (t = perm[p] / k),
+  // FC2 reads the FC1 output rows h[p] directly.
+  const void* act;            // bf16 [rows, K] or E4M3 codes [rows, K]
+  const uint8_t* act_scale;   // E8M0 [rows, K/32] (fp8 activations only)
+  const int32_t* perm;        // FC1 only: row p -> expanded index
+  int32_t top_k;              // FC1 only
+  const int32_t* offsets;     // [E_l+1]
+  const int32_t* mtiles;      // [E_l+1] (mtiles[E_l] = number of m-tiles)
+  const int32_t* tile_expert; // [max_mtiles]
+  const uint8_t* w;           // MXFP4 [E_l, N_total, K/2]
+  const uint8_t* ws;          // E8M0 [E_l, N_total, K/32]
+  int32_t K;                  // contraction length (H for FC1, I for FC2)
+  int32_t N;                  // FC1: I (gate columns; up rows at I + n); FC2: H
+  int32_t E_l;
+  // FC1 epilogue
+  const float* beta;
+  const float* lbeta;
+  const float* alpha_g;       // may be null
+  const float* alpha_u;       // may be null
+  // outputs
+  void* out;                  // FC1: h bf16 [P, I] or E4M3 [P, I]; FC2: y float [P, H]
+  uint8_t* out_scale;         // FC1 w4a8: E8M0 [P, I/32]
+};
+
+struct CombineArgs {
+  const float* y;             // [P, H]
+  const int32_t* inv;         // [T*k]
+  const uint16_t* weights;    // bf16 [T, k] or null
+  const int32_t* packed;      // [T, k] or null
+  void* out;                  // [T, H]
+  int64_t T;
+  int32_t H, k, out_bf16;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_quant_mxfp8(const QuantArgs& a, hipStream_t s);
+// tactic ids select the activation format and the token tile count
+hipError_t launch_fc1(int tactic, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t launch_fc2(int tactic, const GemmArgs& a, int grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Tactic family: (activation format, token tiles of 16 per m-tile)
+enum Tactic : int32_t {
+  FC1_W4A16_M16 = 0,
+  FC1_W4A16_M64 = 1,
+  FC1_W4A8_M16 = 2,
+  FC1_W4A8_M64 = 3,
+  FC2_W4A16_M16 = 16,
+  FC2_W4A16_M64 = 17,
+  FC2_W4A8_M16 = 18,
+  FC2_W4A8_M64 = 19,
+};
+
+// Workgroup shapes of the grouped GEMMs (4 waves of 64 lanes).
+constexpr int kGemmThreads = 256;
+constexpr int kFc1ColsPerWave = 32;    // gate columns per wave (with the matching up columns)
+constexpr int kFc2RowsPerWave = 64;    // output columns of y per wave
+
+}  // namespace situ

@@ -1,0 +1,436 @@
+// Host side of the C ABI declared in include/situ_moe.h: problem validation,
+// tactic selection, workspace layout and the ordered launch of the layer's
+// kernels on the caller's stream.
+//
+// The validation rules follow the pages: SiTU's beta arrays are required,
+// never defaulted to zero (review of moe_kernels.h / moeOp.cpp in
+// TensorRT-LLM pull request 17865); a tactic outside the family is an error,
+// not a silent fallback (same pull request, the create_moe fallback
+// finding); the FC1 weight has 2*I rows for a gated activation (its
+// "fc1_expert_weights inter size must be 2 times fc2" check); the device
+// architecture is checked rather than assumed (xorl-wheels release notes,
+// "Install and architecture").
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/situ_moe.h"
+#include "internal.hpp"
+
+#ifndef SITU_GIT_REV
+#define SITU_GIT_REV "unknown"
+#endif
+
+namespace {
+
+thread_local std::string g_last_error;
+
+situ_status fail(situ_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+situ_status fail(situ_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct TacticInfo {
+  int32_t id;
+  const char* name;
+  int32_t act_mode;
+  int32_t block_m;
+  bool fc1;
+};
+
+const TacticInfo kTactics[] = {
+    {situ::FC1_W4A16_M16, "fc1_w4a16_bf16mfma_m16", SITU_ACT_W4A16, 16, true},
+    {situ::FC1_W4A16_M64, "fc1_w4a16_bf16mfma_m64", SITU_ACT_W4A16, 64, true},
+    {situ::FC1_W4A8_M16, "fc1_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, true},
+    {situ::FC1_W4A8_M64, "fc1_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, true},
+    {situ::FC2_W4A16_M16, "fc2_w4a16_bf16mfma_m16", SITU_ACT_W4A16, 16, false},
+    {situ::FC2_W4A16_M64, "fc2_w4a16_bf16mfma_m64", SITU_ACT_W4A16, 64, false},
+    {situ::FC2_W4A8_M16, "fc2_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, false},
+    {situ::FC2_W4A8_M64, "fc2_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, false},
+};
+
+const TacticInfo* find_tactic(int32_t id) {
+  for (const auto& t : kTactics)
+    if (t.id == id) return &t;
+  return nullptr;
+}
+
+situ_status validate(const situ_moe_problem* p) {
+  if (!p) return fail(SITU_E_NULL_ARG, "problem is NULL");
+  if (p->num_tokens < 0) return fail(SITU_E_BAD_SHAPE, "num_tokens %d < 0", p->num_tokens);
+  if (p->hidden_size <= 0 || p->hidden_size % 32)
+    return fail(SITU_E_BAD_SHAPE, "hidden_size %d must be a positive multiple of 32", p->hidden_size);
+  if (p->intermediate_size <= 0 || p->intermediate_size % 32)
+    return fail(SITU_E_BAD_SHAPE, "intermediate_size %d must be a positive multiple of 32 (pad the physical size)",
+                p->intermediate_size);
+  if (p->num_experts <= 0 || p->num_experts >= 65536)
+    return fail(SITU_E_BAD_SHAPE, "num_experts %d must be in [1, 65535]", p->num_experts);
+  if (p->local_expert_offset < 0) return fail(SITU_E_BAD_SHAPE, "local_expert_offset %d < 0", p->local_expert_offset);
+  if (p->local_num_experts <= 0) return fail(SITU_E_BAD_SHAPE, "local_num_experts %d <= 0", p->local_num_experts);
+  if ((int64_t)p->local_expert_offset + p->local_num_experts > p->num_experts)
+    return fail(SITU_E_BAD_SHAPE, "local shard [%d, %d) exceeds num_experts %d", p->local_expert_offset,
+                p->local_expert_offset + p->local_num_experts, p->num_experts);
+  if (p->local_num_experts > situ::kMaxLocalExperts)
+    return fail(SITU_E_UNSUPPORTED, "local_num_experts %d > %d", p->local_num_experts, situ::kMaxLocalExperts);
+  if (p->top_k <= 0 || p->top_k > p->num_experts)
+    return fail(SITU_E_BAD_SHAPE, "top_k %d must be in [1, num_experts]", p->top_k);
+  if (p->act_mode != SITU_ACT_W4A16 && p->act_mode != SITU_ACT_W4A8)
+    return fail(SITU_E_UNSUPPORTED, "act_mode %d", p->act_mode);
+  if (p->act_prequantized != 0 && p->act_prequantized != 1)
+    return fail(SITU_E_BAD_SHAPE, "act_prequantized must be 0 or 1");
+  if (p->act_prequantized && p->act_mode != SITU_ACT_W4A8)
+    return fail(SITU_E_UNSUPPORTED, "prequantized (MXFP8) activations need act_mode w4a8");
+  if (p->topk_packed != 0 && p->topk_packed != 1) return fail(SITU_E_BAD_SHAPE, "topk_packed must be 0 or 1");
+  if (p->out_dtype != SITU_OUT_F32 && p->out_dtype != SITU_OUT_BF16)
+    return fail(SITU_E_UNSUPPORTED, "out_dtype %d", p->out_dtype);
+  const int64_t tk = (int64_t)p->num_tokens * p->top_k;
+  if (tk >= (int64_t)1 << 31) return fail(SITU_E_UNSUPPORTED, "num_tokens * top_k = %lld exceeds int32", (long long)tk);
+  return SITU_OK;
+}
+
+// Valid (fc1, fc2) pairs, first-valid first: small groups (decode) take
+// 16-row m-tiles, large groups (prefill) 64-row m-tiles.
+int valid_pairs(const situ_moe_problem* p, int32_t* fc1, int32_t* fc2, int cap) {
+  const bool w4a8 = p->act_mode == SITU_ACT_W4A8;
+  const int32_t m16[2] = {w4a8 ? situ::FC1_W4A8_M16 : situ::FC1_W4A16_M16,
+                          w4a8 ? situ::FC2_W4A8_M16 : situ::FC2_W4A16_M16};
+  const int32_t m64[2] = {w4a8 ? situ::FC1_W4A8_M64 : situ::FC1_W4A16_M64,
+                          w4a8 ? situ::FC2_W4A8_M64 : situ::FC2_W4A16_M64};
+  const double rows_per_expert = (double)p->num_tokens * p->top_k / p->local_num_experts;
+  const int32_t* order[2] = {m16, m64};
+  if (rows_per_expert > 48.0) { order[0] = m64; order[1] = m16; }
+  int n = 0;
+  for (int i = 0; i < 2; ++i) {
+    if (n < cap) { fc1[n] = order[i][0]; fc2[n] = order[i][1]; }
+    ++n;
+  }
+  return n;
+}
+
+struct DeviceInfo {
+  bool checked = false;
+  bool ok = false;
+  int cus = 0;
+  std::string arch;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+situ_status device_check(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(SITU_E_DEVICE, "no current HIP device");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(SITU_E_DEVICE, "hipGetDeviceProperties failed");
+    d.arch = prop.gcnArchName;
+    d.cus = prop.multiProcessorCount;
+    d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.checked = true;
+  }
+  if (!d.ok) return fail(SITU_E_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, d.arch.c_str());
+  *cus = d.cus;
+  return SITU_OK;
+}
+
+situ_status launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SITU_OK;
+  return fail(SITU_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+situ_status check_run_args(const situ_moe_plan_t* plan, const situ_moe_tensors* t, void* ws, uint64_t ws_bytes,
+                           bool route_only) {
+  if (!plan) return fail(SITU_E_NULL_ARG, "plan is NULL");
+  if (!t) return fail(SITU_E_NULL_ARG, "tensors is NULL");
+  const situ_moe_problem& p = plan->prob;
+  situ_status st = validate(&p);
+  if (st != SITU_OK) return st;
+  if (p.num_tokens == 0) return SITU_OK;  // nothing is read or written; empty arrays may be NULL
+  if (p.topk_packed ? !t->topk_packed : (!t->topk_ids || !t->topk_weights))
+    return fail(SITU_E_NULL_ARG, p.topk_packed ? "topk_packed is NULL" : "topk_ids or topk_weights is NULL");
+  if (!route_only) {
+    if (!t->hidden_states) return fail(SITU_E_NULL_ARG, "hidden_states is NULL");
+    if (p.act_prequantized && !t->hidden_states_scale)
+      return fail(SITU_E_MISSING_SCALE, "w4a8 prequantized input needs hidden_states_scale");
+    if (!t->w1 || !t->w1_scale || !t->w2 || !t->w2_scale) return fail(SITU_E_NULL_ARG, "a weight or scale is NULL");
+    if (!t->situ_beta || !t->situ_linear_beta)
+      return fail(SITU_E_NULL_ARG, "SiTU needs situ_beta and situ_linear_beta (no default is substituted)");
+    if (!t->out) return fail(SITU_E_NULL_ARG, "out is NULL");
+  }
+  if (!ws && plan->workspace_bytes) return fail(SITU_E_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < plan->workspace_bytes)
+    return fail(SITU_E_WORKSPACE, "workspace %llu bytes < %llu needed", (unsigned long long)ws_bytes,
+                (unsigned long long)plan->workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(SITU_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return SITU_OK;
+}
+
+template <typename T>
+T* at(void* ws, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+situ::RouteArgs route_args(const situ_moe_plan_t* plan, const situ_moe_tensors* t, void* ws) {
+  const situ_moe_problem& p = plan->prob;
+  situ::RouteArgs r;
+  r.ids = p.topk_packed ? nullptr : t->topk_ids;
+  r.packed = p.topk_packed ? t->topk_packed : nullptr;
+  r.TK = (int64_t)p.num_tokens * p.top_k;
+  r.off = p.local_expert_offset;
+  r.E_l = p.local_num_experts;
+  r.block_m = plan->block_m;
+  r.counts = at<int32_t>(ws, plan->off_counts);
+  r.offsets = at<int32_t>(ws, plan->off_offsets);
+  r.mtiles = at<int32_t>(ws, plan->off_mtiles);
+  r.tile_expert = at<int32_t>(ws, plan->off_tile_expert);
+  r.perm = at<int32_t>(ws, plan->off_perm);
+  r.inv = at<int32_t>(ws, plan->off_inv);
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+situ_status situ_moe_plan(const situ_moe_problem* problem, situ_moe_plan_t* plan) {
+  if (!plan) return fail(SITU_E_NULL_ARG, "plan is NULL");
+  situ_status st = validate(problem);
+  if (st != SITU_OK) return st;
+  const situ_moe_problem& p = *problem;
+  int32_t f1[4], f2[4];
+  const int n = valid_pairs(&p, f1, f2, 4);
+  int32_t t1 = p.tactic_fc1, t2 = p.tactic_fc2;
+  if (t1 == -1 && t2 == -1) {
+    t1 = f1[0];
+    t2 = f2[0];
+  } else if (t1 == -1 || t2 == -1) {
+    for (int i = 0; i < n; ++i)
+      if ((t1 == -1 && f2[i] == t2) || (t2 == -1 && f1[i] == t1)) { t1 = f1[i]; t2 = f2[i]; break; }
+  }
+  bool ok = false;
+  for (int i = 0; i < n; ++i) ok = ok || (f1[i] == t1 && f2[i] == t2);
+  if (!ok) return fail(SITU_E_UNSUPPORTED, "tactic pair (%d, %d) is not valid for this problem", p.tactic_fc1, p.tactic_fc2);
+
+  std::memset(plan, 0, sizeof(*plan));
+  plan->prob = p;
+  plan->fc1_tactic = t1;
+  plan->fc2_tactic = t2;
+  plan->block_m = find_tactic(t1)->block_m;
+  const int64_t T = p.num_tokens, H = p.hidden_size, I = p.intermediate_size, TK = T * p.top_k;
+  const int64_t E_l = p.local_num_experts;
+  const int64_t max_mtiles = (TK + plan->block_m - 1) / plan->block_m + E_l;
+  if (max_mtiles >= (int64_t)1 << 30) return fail(SITU_E_UNSUPPORTED, "too many m-tiles");
+  plan->max_mtiles = (int32_t)max_mtiles;
+  uint64_t off = 0;
+  auto region = [&](uint64_t bytes) {
+    uint64_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  plan->off_counts = region(4 * E_l);
+  plan->off_offsets = region(4 * (E_l + 1));
+  plan->off_mtiles = region(4 * (E_l + 1));
+  plan->off_tile_expert = region(4 * max_mtiles);
+  plan->off_perm = region(4 * TK);
+  plan->off_inv = region(4 * TK);
+  const bool w4a8 = p.act_mode == SITU_ACT_W4A8;
+  const bool quant_here = w4a8 && !p.act_prequantized;
+  plan->off_xq = region(quant_here ? T * H : 0);
+  plan->off_xs = region(quant_here ? T * H / 32 : 0);
+  plan->off_h = region(TK * I * (w4a8 ? 1 : 2));
+  plan->off_hs = region(w4a8 ? TK * I / 32 : 0);
+  plan->off_y = region(TK * H * 4);
+  plan->workspace_bytes = off;
+  return SITU_OK;
+}
+
+situ_status situ_moe_valid_tactics(const situ_moe_problem* problem, int32_t* fc1, int32_t* fc2, int32_t capacity,
+                                   int32_t* count) {
+  situ_status st = validate(problem);
+  if (st != SITU_OK) return st;
+  if (!count || (capacity > 0 && (!fc1 || !fc2))) return fail(SITU_E_NULL_ARG, "output arrays are NULL");
+  int32_t a[8], b[8];
+  const int n = valid_pairs(problem, a, b, 8);
+  for (int i = 0; i < n && i < capacity; ++i) { fc1[i] = a[i]; fc2[i] = b[i]; }
+  *count = n;
+  return SITU_OK;
+}
+
+situ_status situ_moe_route(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors, void* workspace,
+                           uint64_t workspace_bytes, void* hip_stream) {
+  situ_status st = check_run_args(plan, tensors, workspace, workspace_bytes, true);
+  if (st != SITU_OK) return st;
+  int cus = 0;
+  if ((st = device_check(&cus)) != SITU_OK) return st;
+  if (plan->prob.num_tokens == 0) return SITU_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  return launch_status(situ::launch_route(route_args(plan, tensors, workspace), s), "route");
+}
+
+}  // extern "C"
+
+namespace {
+
+situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, void* ws, uint64_t ws_bytes,
+                     void* hip_stream, void* const* events) {
+  situ_status st = check_run_args(plan, t, ws, ws_bytes, false);
+  if (st != SITU_OK) return st;
+  int cus = 0;
+  if ((st = device_check(&cus)) != SITU_OK) return st;
+  const situ_moe_problem& p = plan->prob;
+  if (p.num_tokens == 0) return SITU_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t T = p.num_tokens, H = p.hidden_size, I = p.intermediate_size;
+  const bool w4a8 = p.act_mode == SITU_ACT_W4A8;
+
+  auto mark = [&](int i) -> situ_status {
+    if (!events) return SITU_OK;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    return e == hipSuccess ? SITU_OK : fail(SITU_E_LAUNCH, "hipEventRecord: %s", hipGetErrorString(e));
+  };
+  if ((st = mark(0)) != SITU_OK) return st;
+  situ::RouteArgs ra = route_args(plan, t, ws);
+  if ((st = launch_status(situ::launch_route(ra, s), "route")) != SITU_OK) return st;
+  if ((st = mark(1)) != SITU_OK) return st;
+
+  const void* act = t->hidden_states;
+  const uint8_t* act_scale = t->hidden_states_scale;
+  if (w4a8 && !p.act_prequantized) {
+    situ::QuantArgs q{static_cast<const uint16_t*>(t->hidden_states), at<uint8_t>(ws, plan->off_xq),
+                      at<uint8_t>(ws, plan->off_xs), T, (int32_t)H};
+    if ((st = launch_status(situ::launch_quant_mxfp8(q, s), "quantize")) != SITU_OK) return st;
+    act = q.codes;
+    act_scale = q.scales;
+  }
+  if ((st = mark(2)) != SITU_OK) return st;
+
+  situ::GemmArgs g{};
+  g.offsets = ra.offsets;
+  g.mtiles = ra.mtiles;
+  g.tile_expert = ra.tile_expert;
+  g.E_l = p.local_num_experts;
+  g.beta = t->situ_beta;
+  g.lbeta = t->situ_linear_beta;
+  g.alpha_g = t->alpha_gate;
+  g.alpha_u = t->alpha_up;
+
+  // FC1 + SiTU
+  g.act = act;
+  g.act_scale = w4a8 ? act_scale : nullptr;
+  g.perm = ra.perm;
+  g.top_k = p.top_k;
+  g.w = t->w1;
+  g.ws = t->w1_scale;
+  g.K = (int32_t)H;
+  g.N = (int32_t)I;
+  g.out = at<void>(ws, plan->off_h);
+  g.out_scale = w4a8 ? at<uint8_t>(ws, plan->off_hs) : nullptr;
+  const int64_t fc1_units = I / situ::kFc1ColsPerWave;
+  const int64_t fc1_work = (int64_t)plan->max_mtiles * ((fc1_units + 3) / 4);
+  const int64_t persistent = (int64_t)cus * 4;
+  int grid1 = (int)(fc1_work < persistent ? fc1_work : persistent);
+  if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, grid1, s), "fc1")) != SITU_OK) return st;
+  if ((st = mark(3)) != SITU_OK) return st;
+
+  // FC2
+  g.act = at<void>(ws, plan->off_h);
+  g.act_scale = w4a8 ? at<uint8_t>(ws, plan->off_hs) : nullptr;
+  g.perm = nullptr;
+  g.w = t->w2;
+  g.ws = t->w2_scale;
+  g.K = (int32_t)I;
+  g.N = (int32_t)H;
+  g.out = at<void>(ws, plan->off_y);
+  g.out_scale = nullptr;
+  const int64_t fc2_wgn = (H + 4 * situ::kFc2RowsPerWave - 1) / (4 * situ::kFc2RowsPerWave);
+  const int64_t fc2_work = (int64_t)plan->max_mtiles * fc2_wgn;
+  int grid2 = (int)(fc2_work < persistent ? fc2_work : persistent);
+  if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, grid2, s), "fc2")) != SITU_OK) return st;
+  if ((st = mark(4)) != SITU_OK) return st;
+
+  // combine
+  situ::CombineArgs c{at<float>(ws, plan->off_y), ra.inv, p.topk_packed ? nullptr : t->topk_weights,
+                      p.topk_packed ? t->topk_packed : nullptr, t->out, T, (int32_t)H, p.top_k,
+                      p.out_dtype == SITU_OUT_BF16 ? 1 : 0};
+  if ((st = launch_status(situ::launch_combine(c, s), "combine")) != SITU_OK) return st;
+  return mark(5);
+}
+
+}  // namespace
+
+extern "C" {
+
+situ_status situ_moe_run(const situ_moe_plan_t* plan, const situ_moe_tensors* t, void* ws, uint64_t ws_bytes,
+                         void* hip_stream) {
+  return run_impl(plan, t, ws, ws_bytes, hip_stream, nullptr);
+}
+
+situ_status situ_moe_run_profiled(const situ_moe_plan_t* plan, const situ_moe_tensors* t, void* ws,
+                                  uint64_t ws_bytes, void* hip_stream, void* const* hip_events, int32_t n_events) {
+  if (!hip_events || n_events != 6) return fail(SITU_E_NULL_ARG, "run_profiled needs 6 hipEvent_t handles");
+  for (int i = 0; i < 6; ++i)
+    if (!hip_events[i]) return fail(SITU_E_NULL_ARG, "hip_events[%d] is NULL", i);
+  return run_impl(plan, t, ws, ws_bytes, hip_stream, hip_events);
+}
+
+situ_status situ_moe_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int32_t cols, uint8_t* codes,
+                                    uint8_t* scales, void* hip_stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(SITU_E_BAD_SHAPE, "rows %lld, cols %d (multiple of 32)",
+                                                      (long long)rows, cols);
+  if (rows == 0) return SITU_OK;
+  if (!x_bf16 || !codes || !scales) return fail(SITU_E_NULL_ARG, "a pointer is NULL");
+  int cus = 0;
+  situ_status st = device_check(&cus);
+  if (st != SITU_OK) return st;
+  situ::QuantArgs q{x_bf16, codes, scales, rows, cols};
+  return launch_status(situ::launch_quant_mxfp8(q, static_cast<hipStream_t>(hip_stream)), "quantize");
+}
+
+const char* situ_moe_status_string(situ_status s) {
+  switch (s) {
+    case SITU_OK: return "SITU_OK";
+    case SITU_E_NULL_ARG: return "SITU_E_NULL_ARG";
+    case SITU_E_BAD_SHAPE: return "SITU_E_BAD_SHAPE";
+    case SITU_E_UNSUPPORTED: return "SITU_E_UNSUPPORTED";
+    case SITU_E_MISSING_SCALE: return "SITU_E_MISSING_SCALE";
+    case SITU_E_DEVICE: return "SITU_E_DEVICE";
+    case SITU_E_WORKSPACE: return "SITU_E_WORKSPACE";
+    case SITU_E_LAUNCH: return "SITU_E_LAUNCH";
+  }
+  return "SITU_E_UNKNOWN";
+}
+
+const char* situ_moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* situ_moe_build_info(void) {
+  static const std::string info = [] {
+    std::string s = "situ_moe abi " + std::to_string(SITU_MOE_ABI_VERSION) + "; target gfx950; rev " SITU_GIT_REV
+                    "; tactics:";
+    for (const auto& t : kTactics) s += std::string(" ") + std::to_string(t.id) + "=" + t.name;
+    return s;
+  }();
+  return info.c_str();
+}
+
+const char* situ_moe_tactic_name(int32_t tactic) {
+  const TacticInfo* t = find_tactic(tactic);
+  return t ? t->name : nullptr;
+}
+
+int32_t situ_moe_abi_version(void) { return SITU_MOE_ABI_VERSION; }
+
+}  // extern "C"

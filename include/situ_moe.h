@@ -1,0 +1,182 @@
+/*
+ * situ_moe.h -- C ABI of the MXFP4 + SiTU routed-MoE expert layer on MI355X (gfx950).
+ *
+ * One call computes ONE tensor- or expert-parallel shard's partial output of
+ * a routed Mixture-of-Experts layer whose expert weights are MXFP4 (E2M1
+ * values, one E8M0 scale per 32 elements along K) and whose gated activation
+ * is SiTU.  The contract follows the pages' description of the layer:
+ *
+ *  - "TokenSpeed SiTU" (PyPI page of tokenspeed-situ), "Supported contract":
+ *    BF16 activations (w4a16) or MXFP8 activations with a per-token block
+ *    scale tensor (w4a8); MXFP4 weights; precomputed packed or unpacked
+ *    top-k with GLOBAL expert ids; experts outside the rank's contiguous
+ *    shard [local_expert_offset, local_expert_offset + local_num_experts)
+ *    are dropped and the result is a PARTIAL output that the caller sums
+ *    over the MoE TP/EP group (this library owns no communication).
+ *  - same page, "Activation precision (w4a16 vs w4a8)": in w4a8 the FC1
+ *    output is rounded through MXFP8 and dequantized before a w4a16 FC2.
+ *  - same page, "Runtime API": the caller passes the physical intermediate
+ *    size, the global expert count, the local expert offset and count; the
+ *    default tactic (-1, -1) is the first valid configuration for the
+ *    runtime shape, with no autotuning.
+ *  - "bring up Kimi K3 NVFP4 with CUTLASS and cuteDSL MegaMoE SiTU"
+ *    (TensorRT-LLM pull request 17865), review of test_kimi_k3_situ_moe.py:
+ *    act(g, u) = [beta*tanh(g/beta)*sigmoid(g)] * [lbeta*tanh(u/lbeta)] and
+ *    out[t] += weight[t,s] * (act(g,u) @ w2^T); review of moe_kernels.h /
+ *    moeOp.cpp: SiTU's beta arrays are required, never defaulted.
+ *  - "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT -- Kimi-K3 SiTU" release
+ *    notes, "Changes since 875b7d7": per-expert beta and linear beta; the up
+ *    half rescaled by alpha_up / alpha_gate before the tanh.
+ *
+ * Conventions for every entry point:
+ *  - Plain C.  Pointers marked (device) are HIP device pointers, (host) are
+ *    host pointers.  All arrays are dense, row-major, naturally aligned;
+ *    device arrays of 16 bytes or more per row must be 16-byte aligned.
+ *  - The caller owns every buffer: inputs, the output and the workspace.
+ *    The library allocates no device memory and holds no device state.
+ *  - Every function returns situ_status; no exception crosses the ABI.  On
+ *    a non-OK status, situ_moe_last_error() returns a message for the
+ *    calling thread.
+ *  - Work is enqueued on the given hipStream_t (NULL = the null stream) and
+ *    never synchronized; no device data is read back to the host.
+ */
+#ifndef SITU_MOE_H
+#define SITU_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SITU_MOE_ABI_VERSION 1
+
+typedef enum situ_status {
+  SITU_OK = 0,
+  SITU_E_NULL_ARG = 1,       /* a required pointer is NULL */
+  SITU_E_BAD_SHAPE = 2,      /* sizes inconsistent or out of range */
+  SITU_E_UNSUPPORTED = 3,    /* valid request this library does not implement (incl. a tactic outside the family) */
+  SITU_E_MISSING_SCALE = 4,  /* w4a8 with prequantized input but no hidden_states_scale */
+  SITU_E_DEVICE = 5,         /* no device, or the current device is not gfx950 */
+  SITU_E_WORKSPACE = 6,      /* workspace NULL or smaller than the plan needs */
+  SITU_E_LAUNCH = 7          /* a kernel launch failed */
+} situ_status;
+
+enum { SITU_ACT_W4A16 = 0, SITU_ACT_W4A8 = 1 };
+enum { SITU_OUT_F32 = 0, SITU_OUT_BF16 = 1 };
+
+/* The runtime shape of one shard (host POD). */
+typedef struct situ_moe_problem {
+  int32_t num_tokens;           /* T >= 0 */
+  int32_t hidden_size;          /* H, multiple of 32 */
+  int32_t intermediate_size;    /* physical I of this shard, multiple of 32 */
+  int32_t num_experts;          /* global expert count E_g, 1..65535 */
+  int32_t local_expert_offset;  /* off >= 0 */
+  int32_t local_num_experts;    /* E_l, 1..1024, off + E_l <= E_g */
+  int32_t top_k;                /* k, 1..E_g */
+  int32_t act_mode;             /* SITU_ACT_W4A16 or SITU_ACT_W4A8 (fixed for the process on the pages; per plan here) */
+  int32_t act_prequantized;     /* w4a8 only: 1 = hidden_states are E4M3 codes + E8M0 scales; 0 = bf16, quantized here */
+  int32_t topk_packed;          /* 0 = topk_ids int32 + topk_weights bf16; 1 = topk_packed int32 (bf16 weight << 16 | id) */
+  int32_t out_dtype;            /* SITU_OUT_F32 or SITU_OUT_BF16 (round-to-nearest-even of the fp32 result) */
+  int32_t tactic_fc1;           /* -1 = first valid; else a value from situ_moe_valid_tactics */
+  int32_t tactic_fc2;           /* -1 = first valid */
+} situ_moe_problem;
+
+/* A resolved plan (host POD, reusable, no device state).  The workspace
+ * region offsets are part of the ABI so that tests can inspect the routing
+ * results and intermediates a run leaves in the workspace. */
+typedef struct situ_moe_plan_t {
+  situ_moe_problem prob;
+  int32_t fc1_tactic;           /* resolved tactic ids */
+  int32_t fc2_tactic;
+  int32_t block_m;              /* rows (token-expert pairs) per m-tile */
+  int32_t max_mtiles;           /* upper bound of m-tiles: T*k / block_m + E_l */
+  uint64_t workspace_bytes;     /* bytes the caller must provide */
+  /* byte offsets into the workspace (each 256-byte aligned) */
+  uint64_t off_counts;          /* int32 [E_l]      pairs per local expert */
+  uint64_t off_offsets;         /* int32 [E_l + 1]  exclusive prefix sum of counts */
+  uint64_t off_mtiles;          /* int32 [E_l + 1]  exclusive prefix sum of ceil(counts / block_m) */
+  uint64_t off_tile_expert;     /* int32 [max_mtiles] local expert of each m-tile, in order */
+  uint64_t off_perm;            /* int32 [T*k]      perm[offsets[l] + r] = expanded index t*k+s */
+  uint64_t off_inv;             /* int32 [T*k]      position of pair t*k+s in perm, -1 if not local */
+  uint64_t off_xq;              /* uint8 [T, H]     E4M3 codes of bf16 input (w4a8, not prequantized) */
+  uint64_t off_xs;              /* uint8 [T, H/32]  their E8M0 scales */
+  uint64_t off_h;               /* FC1 output rows in perm order: bf16 [T*k, I] (w4a16) or E4M3 [T*k, I] (w4a8) */
+  uint64_t off_hs;              /* uint8 [T*k, I/32] E8M0 scales of h (w4a8) */
+  uint64_t off_y;               /* float [T*k, H]   FC2 output rows in perm order */
+  uint32_t reserved[8];
+} situ_moe_plan_t;
+
+/* Device tensors of one call.  Shapes use T, H, I, k, E_l of the problem. */
+typedef struct situ_moe_tensors {
+  const void* hidden_states;          /* (device) bf16 [T, H]; or E4M3 codes uint8 [T, H] if act_prequantized */
+  const uint8_t* hidden_states_scale; /* (device) E8M0 uint8 [T, H/32], per token per 32 along H; w4a8 prequantized only */
+  const int32_t* topk_ids;            /* (device) int32 [T, k], GLOBAL ids; any id outside the shard is skipped */
+  const uint16_t* topk_weights;       /* (device) bf16 [T, k] routing weights, applied in the combine */
+  const int32_t* topk_packed;         /* (device) int32 [T, k] = (bf16 weight bits << 16) | (id & 0xFFFF); topk_packed only */
+  const uint8_t* w1;                  /* (device) MXFP4 [E_l, 2I, H/2]: rows [0,I) gate, [I,2I) up; low nibble = even k */
+  const uint8_t* w1_scale;            /* (device) E8M0 [E_l, 2I, H/32] */
+  const uint8_t* w2;                  /* (device) MXFP4 [E_l, H, I/2] */
+  const uint8_t* w2_scale;            /* (device) E8M0 [E_l, H, I/32] */
+  const float* situ_beta;             /* (device) float [E_l], required */
+  const float* situ_linear_beta;      /* (device) float [E_l], required */
+  const float* alpha_gate;            /* (device) float [E_l] or NULL (= 1.0) */
+  const float* alpha_up;              /* (device) float [E_l] or NULL (= 1.0) */
+  void* out;                          /* (device) [T, H] float or bf16 per out_dtype; every element is written */
+} situ_moe_tensors;
+
+/* Validate a problem and resolve its tactics, block size and workspace
+ * layout.  Host only; needs no device.  Returns SITU_E_BAD_SHAPE or
+ * SITU_E_UNSUPPORTED on a problem it cannot serve, never a silent fallback. */
+situ_status situ_moe_plan(const situ_moe_problem* problem, situ_moe_plan_t* plan);
+
+/* List the (fc1, fc2) tactic pairs valid for a problem, first-valid first
+ * ("Runtime API": the tactic list of get_valid_k3_situ_configs).  Writes at
+ * most `capacity` pairs to fc1[] / fc2[] (host) and the total to *count. */
+situ_status situ_moe_valid_tactics(const situ_moe_problem* problem, int32_t* fc1, int32_t* fc2,
+                                   int32_t capacity, int32_t* count);
+
+/* Run the whole layer: shard filter and routing, [MXFP8 quantize of bf16
+ * input in w4a8], FC1 + alpha + SiTU, FC2, weighted combine into `out`.
+ * Asynchronous on `hip_stream`; capture-safe (no host synchronization, no
+ * allocation).  Calls sharing one workspace must not overlap in time. */
+situ_status situ_moe_run(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors,
+                         void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* situ_moe_run that also records caller-created hipEvent_t handles on the
+ * stream at the stage boundaries, for timing each kernel on the stream it
+ * runs on: [0] before routing, [1] after routing, [2] after the MXFP8
+ * quantization (recorded right after [1] when there is none), [3] after
+ * FC1, [4] after FC2, [5] after the combine.  n_events must be 6.  The
+ * kernels and results are exactly those of situ_moe_run. */
+situ_status situ_moe_run_profiled(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors,
+                                  void* workspace, uint64_t workspace_bytes, void* hip_stream,
+                                  void* const* hip_events, int32_t n_events);
+
+/* The routing stage alone: fills counts, offsets, mtiles, perm and inv in
+ * the workspace (offsets in the plan).  Reads only the top-k tensors. */
+situ_status situ_moe_route(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors,
+                           void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* MXFP8 quantization of a bf16 matrix [rows, cols] (cols multiple of 32),
+ * per row per 32 consecutive columns, by the OCP MX v1.0 rule: scale code =
+ * floor(log2(block amax)) - 8 + 127 clamped to [0, 254] (0 for an all-zero
+ * block), element = E4M3 round-to-nearest-even of x / 2^(code-127),
+ * saturating to +-448.  codes uint8 [rows, cols], scales uint8 [rows, cols/32]
+ * (all device).  Input NaN/Inf give unspecified codes. */
+situ_status situ_moe_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int32_t cols,
+                                    uint8_t* codes, uint8_t* scales, void* hip_stream);
+
+const char* situ_moe_status_string(situ_status status);
+const char* situ_moe_last_error(void);
+/* Human-readable build description: ABI version, gfx target, tactic family. */
+const char* situ_moe_build_info(void);
+/* Name of a tactic id, or NULL if the id is not in the family. */
+const char* situ_moe_tactic_name(int32_t tactic);
+int32_t situ_moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SITU_MOE_H */

@@ -1,0 +1,271 @@
+"""GPU parity of the HIP layer against the CPU oracle, through the C ABI.
+
+Bit-exact: routing (counts, offsets, perm, inv) and the MXFP8 quantizer.
+Within the parity bar (cosine >= 0.9995, max-abs <= 1e-2 x RMS of the oracle,
+fp32 outputs): the whole layer, on small shapes that span several tiles and
+ragged tails, and on every benchmark workload at full size with the launch
+configuration the benchmark times (sampled tokens, plus properties that hold
+for every token).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_mxfp4_amd as B
+import synthetic as S
+from oracle import formats as F
+from oracle import moe as M
+
+from gpu_helpers import config_inputs, dev, oracle_out, parity, run_layer, ws_region
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("device:", torch.cuda.get_device_name(0), B.situ_moe_build_info(), flush=True)
+
+
+SMALL = {
+    "tiny": dict(S.CONFIGS[0]),
+    "ragged": dict(T=37, H=96, I=96, E_g=13, E_l=5, off=4, k=3, seed=31),
+    "ragged_packed": dict(T=29, H=160, I=32, E_g=40, E_l=9, off=30, k=4, seed=32, packed=True),
+    "wide": dict(T=50, H=512, I=320, E_g=12, E_l=12, off=0, k=6, seed=33, skew=True),
+    "many_rows": dict(T=300, H=256, I=64, E_g=4, E_l=3, off=1, k=2, seed=34),
+}
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_route_bit_exact(cfg):
+    inp = S.generate(cfg, weights=False)
+    s = inp["spec"]
+    T, k = s["T"], s["k"]
+    packed = inp.get("topk_packed") is not None
+    prob = B.make_problem(num_tokens=T, hidden_size=s["H"], intermediate_size=s["I"], num_experts=s["E_g"],
+                          local_expert_offset=s["off"], local_num_experts=s["E_l"], top_k=k,
+                          act_mode=s["mode"], topk_packed=packed)
+    plan = B.situ_moe_plan(prob)
+    ws = B.new_workspace(plan)
+    d = {}
+    if packed:
+        d["topk_packed"] = dev(inp["topk_packed"])
+    else:
+        d["topk_ids"] = dev(inp["topk_ids"])
+        d["topk_weights"] = dev(inp["topk_weights"])
+    ts = B.SituMoeTensors(**{key: v.data_ptr() for key, v in d.items()})
+    B.situ_moe_route(plan, ts, ws)
+    torch.cuda.synchronize()
+    counts, offsets, perm, inv = M.route(M.topk_of(inp)[0], s["off"], s["E_l"])
+    E = s["E_l"]
+    P = int(offsets[-1])
+    assert np.array_equal(ws_region(plan, ws, "counts", torch.int32, (E,)), counts)
+    assert np.array_equal(ws_region(plan, ws, "offsets", torch.int32, (E + 1,)), offsets)
+    assert np.array_equal(ws_region(plan, ws, "perm", torch.int32, (P,)), perm)
+    assert np.array_equal(ws_region(plan, ws, "inv", torch.int32, (T * k,)), inv)
+    # the m-tile list: exclusive prefix of ceil(counts / block_m), one entry per tile
+    bm = plan.block_m
+    mt = np.zeros(E + 1, np.int64)
+    mt[1:] = np.cumsum((counts + bm - 1) // bm)
+    assert np.array_equal(ws_region(plan, ws, "mtiles", torch.int32, (E + 1,)), mt)
+    te = ws_region(plan, ws, "tile_expert", torch.int32, (int(mt[-1]),))
+    assert np.array_equal(te, np.repeat(np.arange(E), (counts + bm - 1) // bm))
+    print(f"config {cfg}: P={P} active={int((counts > 0).sum())} max={int(counts.max())}", flush=True)
+
+
+def test_route_out_of_range_and_negative_ids():
+    rng = np.random.default_rng(41)
+    T, k, E_g, off, E_l = 333, 7, 1000, 300, 1000 - 300
+    ids = rng.integers(-50, 1100, size=(T, k)).astype(np.int32)
+    ids[5] = 299                     # a token with no local slot
+    prob = B.make_problem(num_tokens=T, hidden_size=64, intermediate_size=32, num_experts=E_g,
+                          local_expert_offset=off, local_num_experts=E_l, top_k=k)
+    plan = B.situ_moe_plan(prob)
+    ws = B.new_workspace(plan)
+    ti = dev(ids)
+    tw = dev(np.zeros((T, k), np.uint16))
+    B.situ_moe_route(plan, B.SituMoeTensors(topk_ids=ti.data_ptr(), topk_weights=tw.data_ptr()), ws)
+    torch.cuda.synchronize()
+    counts, offsets, perm, inv = M.route(ids, off, E_l)
+    assert np.array_equal(ws_region(plan, ws, "counts", torch.int32, (E_l,)), counts)
+    assert np.array_equal(ws_region(plan, ws, "perm", torch.int32, (int(offsets[-1]),)), perm)
+    assert np.array_equal(ws_region(plan, ws, "inv", torch.int32, (T * k,)), inv)
+
+
+# ------------------------------------------------------------------ quantizer
+
+def _quant_gpu(x_bits):
+    rows, cols = x_bits.shape
+    x = dev(x_bits)
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    B.situ_moe_quantize_mxfp8(x, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def test_quantize_mxfp8_bit_exact_edge_blocks():
+    rng = np.random.default_rng(42)
+    rows, cols = 257, 32 * 12
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-140, 120, size=(rows, cols // 32)).astype(np.float32)).repeat(32, axis=1)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    bits[0, :32] = 0                               # all-zero block
+    bits[1, :32] = 0x8000                          # all negative-zero block
+    bits[2, :32] = 0x0001                          # smallest bf16 subnormal
+    for i, p in enumerate(range(-20, 20, 5)):      # amax exactly a power of two, and just below
+        bits[3 + i, :32] = (np.float32(2.0 ** p).view(np.uint32) >> 16)
+        bits[3 + i, 32:64] = ((np.float32(2.0 ** p).view(np.uint32) >> 16) - 1)
+    bits[12, :32] = rng.integers(0, 65536, 32)     # random patterns (drop NaN/Inf below)
+    exp = (bits >> 7) & 0xFF
+    bits = np.where(exp == 0xFF, bits & 0x807F, bits).astype(np.uint16)
+    # blocks that saturate: amax / 2^e in (448, 512)
+    bits[13, :32] = (np.float32(500.0).view(np.uint32) >> 16)
+    bits[13, 1] = (np.float32(1.0).view(np.uint32) >> 16)
+    codes, scales = _quant_gpu(bits)
+    want_c, want_s = F.mx_quantize(F.bf16_to_f64(bits), "e4m3")
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(codes, want_c)
+
+
+def test_quantize_mxfp8_bit_exact_prefill_activations():
+    inp = S.generate(3, weights=False)
+    codes, scales = _quant_gpu(inp["hidden_states"])
+    want_c, want_s = F.mx_quantize(F.bf16_to_f64(inp["hidden_states"]), "e4m3")
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(codes, want_c)
+
+
+# ------------------------------------------------------------------ the layer, small shapes
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
+@pytest.mark.parametrize("bm", [16, 64])
+def test_layer_parity_small(name, mode, bm):
+    spec = S.spec_of(SMALL[name])
+    inp = S.generate(spec)
+    tac = {("w4a16", 16): (0, 16), ("w4a16", 64): (1, 17), ("w4a8", 16): (2, 18), ("w4a8", 64): (3, 19)}[(mode, bm)]
+    got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tac)
+    ref = oracle_out(inp, spec, mode=mode)
+    parity(got, ref["out"], f"{name} {mode} m{bm}")
+    # tokens with no local slot are exact (+0) zero rows
+    none = np.all(ref["inv"].reshape(spec["T"], spec["k"]) < 0, axis=1)
+    assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "wide"])
+def test_w4a8_prequantized_equals_library_quantized(name):
+    spec = S.spec_of(SMALL[name])
+    inp = S.generate(spec)
+    a, *_ = run_layer(inp, spec, mode="w4a8", prequantized=True)
+    b, *_ = run_layer(inp, spec, mode="w4a8", prequantized=False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    parity(a, oracle_out(inp, spec, mode="w4a8", prequantized=True)["out"], f"{name} prequantized")
+
+
+@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
+def test_intermediate_h_matches_oracle(mode):
+    spec = S.spec_of(SMALL["wide"])
+    inp = S.generate(spec)
+    got, plan, ws, _ = run_layer(inp, spec, mode=mode)
+    ref = oracle_out(inp, spec, mode=mode, keep=True)
+    P, I = int(ref["offsets"][-1]), spec["I"]
+    if mode == "w4a16":
+        h = ws_region(plan, ws, "h", torch.int16, (P, I)).view(np.uint16)
+        hg = F.bf16_to_f64(h)
+    else:
+        hc = ws_region(plan, ws, "h", torch.uint8, (P, I))
+        hs = ws_region(plan, ws, "hs", torch.uint8, (P, I // 32))
+        hg = F.mx_dequantize(hc, hs, "e4m3")
+    hr = np.zeros((P, I))
+    hr[ref["pairs"]] = ref["h"]
+    # one element-grid step at most (a rounding decision may differ by one ulp)
+    step = 2.0 ** -7 if mode == "w4a16" else 2.0 ** -3
+    rel = np.abs(hg - hr) / np.maximum(np.abs(hr), 1e-3 * np.sqrt(np.mean(hr ** 2)))
+    assert np.mean(rel <= 1e-6) > 0.97, np.mean(rel <= 1e-6)
+    assert np.max(rel) <= step * 1.01 + 1e-6
+    y = ws_region(plan, ws, "y", torch.float32, (P, spec["H"]))
+    yr = np.zeros_like(y, dtype=np.float64)
+    yr[ref["pairs"]] = ref["y"]
+    parity(y, yr, f"y {mode}")
+
+
+def test_bf16_output_is_rne_of_fp32_output():
+    spec = S.spec_of(SMALL["wide"])
+    inp = S.generate(spec)
+    f, *_ = run_layer(inp, spec, out_dtype="f32")
+    b, *_ = run_layer(inp, spec, out_dtype="bf16")
+    assert np.array_equal(b, F.f32_to_bf16_rne(f))
+
+
+def test_deterministic_bitwise():
+    spec = S.spec_of(SMALL["many_rows"])
+    inp = S.generate(spec)
+    for mode in ("w4a16", "w4a8"):
+        a, *_ = run_layer(inp, spec, mode=mode)
+        b, *_ = run_layer(inp, spec, mode=mode)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_empty_cases():
+    spec = S.spec_of(dict(T=0, H=64, I=32, E_g=4, E_l=4, k=2, seed=1))
+    inp = S.generate(spec)
+    got, *_ = run_layer(inp, spec)
+    assert got.shape == (0, 64)
+    # every id outside the shard: the output is all exact zeros
+    spec = S.spec_of(dict(T=20, H=64, I=32, E_g=16, E_l=4, off=12, k=3, seed=2))
+    inp = S.generate(spec)
+    inp["topk_ids"] = np.minimum(inp["topk_ids"], 11).astype(np.int32)
+    got, *_ = run_layer(inp, spec)
+    assert np.all(got == 0)
+
+
+def test_ep_shards_sum_to_unsharded_on_gpu():
+    full = S.spec_of(dict(T=40, H=256, I=64, E_g=16, E_l=16, off=0, k=4, seed=51))
+    inp = S.generate(full)
+    ref, *_ = run_layer(inp, full)
+    total = np.zeros_like(ref, dtype=np.float64)
+    for r in range(4):
+        sl = slice(4 * r, 4 * r + 4)
+        shard = dict(inp)
+        for key in ("w1", "w1_scale", "w2", "w2_scale", "situ_beta", "situ_linear_beta", "alpha_gate", "alpha_up"):
+            shard[key] = inp[key][sl]
+        spec = dict(full, off=4 * r, E_l=4)
+        out, *_ = run_layer(shard, spec)
+        total += out
+    parity(total, ref, "sum of 4 EP shards vs unsharded")
+
+
+def test_alpha_null_means_one():
+    spec = S.spec_of(SMALL["ragged"])
+    inp = S.generate(spec)
+    inp1 = dict(inp, alpha_gate=None, alpha_up=None)
+    got, *_ = run_layer(inp1, spec)
+    inp2 = dict(inp, alpha_gate=np.ones(spec["E_l"], np.float32), alpha_up=np.ones(spec["E_l"], np.float32))
+    want, *_ = run_layer(inp2, spec)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_layer_parity_full_size(cfg):
+    inp = config_inputs(cfg)
+    spec = inp["spec"]
+    got, plan, ws, _ = run_layer(inp, spec)
+    T = spec["T"]
+    rng = np.random.default_rng(100 + cfg)
+    tokens = np.arange(T) if T <= 16 else np.sort(rng.choice(T, 12, replace=False))
+    ref = oracle_out(inp, spec, tokens=tokens)
+    parity(got[tokens], ref["out"], f"config {cfg} ({spec['name']}) sampled tokens")
+    none = np.all(ref["inv"].reshape(T, spec["k"]) < 0, axis=1)
+    assert np.all(got[none] == 0)
+    assert np.all(np.isfinite(got))
+    # every token with a local slot got a non-zero row
+    assert np.all(np.any(got[~none] != 0, axis=1))
+    print(f"config {cfg}: plan fc1={B.situ_moe_tactic_name(plan.fc1_tactic)} "
+          f"fc2={B.situ_moe_tactic_name(plan.fc2_tactic)} block_m={plan.block_m} "
+          f"no-local tokens={int(none.sum())}", flush=True)
