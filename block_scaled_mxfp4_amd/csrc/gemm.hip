@@ -313,28 +313,410 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
   }
 }
 
-hipError_t launch_fc1(int tactic, const GemmArgs& a, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  switch (tactic) {
-    case FC1_W4A16_M16: hipLaunchKernelGGL((fc1_kernel<false, 1>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC1_W4A16_M64: hipLaunchKernelGGL((fc1_kernel<false, 4>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC1_W4A8_M16: hipLaunchKernelGGL((fc1_kernel<true, 1>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC1_W4A8_M64: hipLaunchKernelGGL((fc1_kernel<true, 4>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+// ---------------------------------------------------------------------------
+// Decode-shaped variant (16-row m-tiles).  A group holds one to ten rows, so
+// the kernel is a weight stream and is tuned for the bytes it keeps in
+// flight and the requests it makes:
+//  - the waves of a workgroup split the K steps of one unit into contiguous
+//    ranges, so consecutive loads of a wave cover whole 128-byte lines of
+//    its weight rows;
+//  - each wave keeps the weights of its next kDecodeDepth steps in flight
+//    while it converts and multiplies the current one (a ring of register
+//    buffers, rotated by unrolling);
+//  - the unit's E8M0 scales (its rows are contiguous in the scale tensor)
+//    are staged in LDS once per work item with 16-byte loads; one byte per
+//    lane per tile per step straight from memory costs a request each and
+//    measured ~30 % of the achievable stream rate;
+//  - the activation pieces travel in the same ring as the weights: they come
+//    from L2, but loading them just in time stalled every step on its latency;
+//  - partial sums meet in LDS in a fixed order (bitwise reproducible).
+// FC1 units are 32 gate + 32 up rows; FC2 units are 64 output rows.
+//
+// Loads go through buffer resources: 32-bit offsets from a per-expert (or
+// per-tensor) base, and an offset past the resource's size reads zeros, which
+// masks K tails, missing tokens and rows past H without per-dword selects.
+
+constexpr uint32_t kOob = 0x80000000u;   // an offset past every resource: reads 0
+
+// K steps in flight per wave, and the occupancy the register budget
+// targets (waves per SIMD).
+#ifndef SITU_DECODE_DEPTH
+#define SITU_DECODE_DEPTH 1
+#endif
+#ifndef SITU_DECODE_WAVES
+#define SITU_DECODE_WAVES 3
+#endif
+constexpr int kDecodeDepth = SITU_DECODE_DEPTH;
+constexpr int kDecodeWavesPerSimd = SITU_DECODE_WAVES;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// voff carries the per-lane offset (kOob masks the lane); soff is a
+// wave-uniform offset added to it (a tile's row delta), only ever used for
+// rows that exist, so the range check never depends on it.
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+struct DecodeGeo {
+  __amdgpu_buffer_rsrc_t wr, xr, xsr;
+  uint32_t w_row;          // byte offset of this lane's row of tile 0 in the expert's weights
+  uint32_t w_delta[4];     // tile q rows relative to tile 0, in weight bytes (uniform)
+  const uint8_t* s_lds;    // this unit's staged scales: [4 tiles x 16 rows][nkb]
+  uint32_t x_row;          // byte offset of this lane's activation row (kOob if none)
+  uint32_t xs_row;
+  int nkb, g, r, ntiles;
+};
+
+// One K step's operands for a wave: four 16-row weight tiles (16 bytes of
+// E2M1 per lane each) and the activation piece of this lane's token.
+template <bool FP8>
+struct Step {
+  uint4 w[4];
+  uint4 x[FP8 ? 2 : 4];
+  uint32_t xs;
+};
+
+template <bool FP8>
+__device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int j) {
+  const int kb = 4 * j + d.g;
+  const bool kin = kb < d.nkb;
+  const uint32_t wo = kin ? d.w_row + (uint32_t)kb * 16u : kOob;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    b.w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
+  if constexpr (!FP8) {
+    const uint32_t xo = (kin && d.x_row != kOob) ? d.x_row + (uint32_t)kb * 64u : kOob;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b.x[c] = bload16(d.xr, xo + 16u * c);
+    b.xs = 127u;
+  } else {
+    // E4M3 operand: bytes 0..15 are K 128j + 16g .. +15 (block 4j + g/2), bytes
+    // 16..31 are K 128j + 64 + 16g .. +15 (block 4j + 2 + g/2); see mfma_scale_fp4_fp8
+    const bool has = d.x_row != kOob;
+    const uint32_t lo = (has && 4 * j + (d.g >> 1) < d.nkb) ? d.x_row + 128u * j + 16u * d.g : kOob;
+    const uint32_t hi = (has && 4 * j + 2 + (d.g >> 1) < d.nkb) ? d.x_row + 128u * j + 64u + 16u * d.g : kOob;
+    b.x[0] = bload16(d.xr, lo);
+    b.x[1] = bload16(d.xr, hi);
+    b.xs = (has && kin) ? bload8(d.xsr, d.xs_row + (uint32_t)kb) : 127u;
   }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo& d, int j, f32x4 acc[4]) {
+  const int kb = 4 * j + d.g;
+  const bool kin = kb < d.nkb;
+  uint32_t sv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sv[q] = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sc = e8m0_to_f32(sv[q]);
+      uint32_t wb[16];
+      fp4x8_to_bf16x8(b.w[q].x, sc, wb + 0);
+      fp4x8_to_bf16x8(b.w[q].y, sc, wb + 4);
+      fp4x8_to_bf16x8(b.w[q].z, sc, wb + 8);
+      fp4x8_to_bf16x8(b.w[q].w, sc, wb + 12);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const uint32_t xb[4] = {b.x[qq].x, b.x[qq].y, b.x[qq].z, b.x[qq].w};
+        acc[q] = mfma_bf16_16x16x32(wb + 4 * qq, xb, acc[q]);
+      }
+    }
+  } else {
+    const uint32_t xb[8] = {b.x[0].x, b.x[0].y, b.x[0].z, b.x[0].w, b.x[1].x, b.x[1].y, b.x[1].z, b.x[1].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t av[4] = {b.w[q].x, b.w[q].y, b.w[q].z, b.w[q].w};
+      acc[q] = mfma_scale_fp4_fp8(av, xb, sv[q], b.xs, acc[q]);
+    }
+  }
+}
+
+// Dynamic LDS of a decode launch: staged scales of the workgroup's units,
+// then the split-K partial sums.
+__host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int nkb) {
+  return (uint32_t)(units_per_wg * 64 * nkb + 15) / 16u * 16u;
+}
+__host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb) {
+  return decode_lds_scales(4 / ksplit, nkb) + (ksplit > 1 ? 4u * 4u * kWave * 16u : 0u);
+}
+
+template <bool FP8, bool FC1, int KSPLIT>
+__global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm_kernel(GemmArgs a) {
+  constexpr int UNITS_PER_WG = 4 / KSPLIT;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int ks = wave % KSPLIT;
+  const int uw = wave / KSPLIT;
+  const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
+  const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
+  const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
+  const int total = a.mtiles[a.E_l] * n_wgn;
+  const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
+  const int n_rows = FC1 ? 2 * a.N : a.N;          // weight rows per expert
+  // contiguous K range of this wave
+  const int per = (steps + KSPLIT - 1) / KSPLIT;
+  const int j_begin = min(steps, ks * per);
+  const int j_end = min(steps, j_begin + per);
+  const int my_steps = j_end - j_begin;
+  f32x4* red = reinterpret_cast<f32x4*>(lds + decode_lds_scales(UNITS_PER_WG, nkb));   // [4 waves][4][64]
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int mt = w / n_wgn;
+    const int unit0 = (w % n_wgn) * UNITS_PER_WG;
+    const int unit = unit0 + uw;
+    const bool active = unit < units;  // uniform per wave; idle waves still meet the barriers
+    const int l = a.tile_expert[mt];
+    const int p0 = a.offsets[l] + (mt - a.mtiles[l]) * 16;
+    const int p1 = min(a.offsets[l + 1], p0 + 16);
+    const int p = p0 + r;
+    const bool valid = p < p1;
+
+    // stage the scales of the workgroup's units in LDS (16-byte loads)
+    {
+      const size_t sexp = (size_t)n_rows * nkb;
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ws + (size_t)l * sexp, (uint32_t)sexp);
+      const int chunks_per_unit = 4 * nkb;       // 64 rows x nkb bytes / 16
+      for (int c = threadIdx.x; c < UNITS_PER_WG * chunks_per_unit; c += kGemmThreads) {
+        const int u = c / chunks_per_unit, cc = c % chunks_per_unit;
+        uint32_t src;
+        if constexpr (FC1) {
+          const int half = cc / (2 * nkb), within = cc % (2 * nkb);
+          const int row = (half ? a.N : 0) + (unit0 + u) * kFc1ColsPerWave;
+          src = (unit0 + u < units) ? (uint32_t)row * nkb + 16u * within : kOob;
+        } else {
+          src = (uint32_t)(unit0 + u) * kFc2RowsPerWave * nkb + 16u * cc;   // rows past H read 0
+        }
+        *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * nkb + 16 * cc) = bload16(sr, src);
+      }
+    }
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    DecodeGeo d;
+    int n0 = 0, ntiles = 4;
+    Step<FP8> buf[kDecodeDepth + 1];
+    if (active) {
+      const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+      d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
+      d.nkb = nkb;
+      d.g = g;
+      d.r = r;
+      uint32_t dr[4];
+      if constexpr (FC1) {
+        n0 = unit * kFc1ColsPerWave;
+        dr[0] = 0; dr[1] = 16; dr[2] = a.N; dr[3] = a.N + 16;
+      } else {
+        n0 = unit * kFc2RowsPerWave;
+        ntiles = min(4, (a.N - n0) / 16);
+        dr[0] = 0; dr[1] = 16; dr[2] = 32; dr[3] = 48;
+      }
+      d.ntiles = ntiles;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
+      d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2);
+      d.s_lds = lds + (size_t)uw * 64 * nkb;
+      if constexpr (FC1) {
+        const uint32_t t = valid ? (uint32_t)(a.perm[p] / a.top_k) : 0u;
+        d.xr = make_rsrc(a.act, 0x7fffffff);
+        d.x_row = valid ? t * arow_bytes : kOob;
+        d.xsr = make_rsrc(FP8 ? a.act_scale : a.act, 0x7fffffff);
+        d.xs_row = t * (uint32_t)nkb;
+      } else {
+        d.xr = make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
+        d.x_row = valid ? (uint32_t)r * arow_bytes : kOob;
+        d.xsr = make_rsrc(FP8 ? a.act_scale + (size_t)p0 * nkb : static_cast<const uint8_t*>(a.act),
+                          16u * (uint32_t)nkb);
+        d.xs_row = (uint32_t)r * (uint32_t)nkb;
+      }
+      // first kDecodeDepth steps of weights go out before the scale barrier
+#pragma unroll
+      for (int u = 0; u < kDecodeDepth; ++u)
+        if (u < my_steps) load_step<FP8>(buf[u], d, j_begin + u);
+    }
+    __syncthreads();   // staged scales visible
+
+    if (active) {
+      // K loop over this wave's range: the weights of the next kDecodeDepth
+      // steps are in flight while the current one is computed; a ring of
+      // kDecodeDepth + 1 register buffers rotated by unrolling (compile-time
+      // indices); sched_barrier(0) keeps each prefetch ahead of its compute.
+      constexpr int NB = kDecodeDepth + 1;
+      for (int i = 0; i < my_steps; i += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (i + u < my_steps) {
+            if (i + u + kDecodeDepth < my_steps)
+              load_step<FP8>(buf[(u + kDecodeDepth) % NB], d, j_begin + i + u + kDecodeDepth);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step<FP8>(buf[u], d, j_begin + i + u, acc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+
+    // split-K reduction in a fixed order
+    bool lead = active;
+    if constexpr (KSPLIT > 1) {
+      if (active && ks != 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(wave * 4 + q) * kWave + lane] = acc[q];
+      }
+      __syncthreads();
+      lead = active && ks == 0;
+      if (lead) {
+#pragma unroll
+        for (int s2 = 1; s2 < KSPLIT; ++s2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] += red[((wave + s2) * 4 + q) * kWave + lane];
+      }
+    }
+
+    if (lead) {
+      if constexpr (FC1) {
+        const int I = a.N;
+        const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
+        const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
+        const float bb = a.beta[l], lb = a.lbeta[l];
+        const float inv_b = 1.0f / bb, inv_lb = 1.0f / lb;
+        float hv[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, inv_b, inv_lb);
+        if constexpr (!FP8) {
+          if (valid) {
+            uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
+              const uint32_t hi = f32_to_bf16_rne(hv[half][2]) | (f32_to_bf16_rne(hv[half][3]) << 16);
+              *reinterpret_cast<uint2*>(hrow + 16 * half) = make_uint2(lo, hi);
+            }
+          }
+        } else {
+          float amax = 0.0f;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(hv[half][i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+          if (valid) {
+            const uint32_t code = e8m0_code_for_e4m3(amax);
+            const int sh = 127 - (int)code;
+            uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              uint32_t packed = 0;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__builtin_ldexpf(hv[half][i], sh)) << (8 * i);
+              *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
+            }
+            if (g == 0) a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
+          }
+        }
+      } else {
+        if (valid) {
+          float* yrow = static_cast<float*>(a.out) + (int64_t)p * a.N + n0 + 4 * g;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q < ntiles) *reinterpret_cast<f32x4*>(yrow + 16 * q) = acc[q];
+        }
+      }
+    }
+    __syncthreads();   // staged scales and partial sums are reused by the next work item
+  }
+}
+
+// K split for the decode kernels: long K loops are shared by the four waves.
+#ifndef SITU_DECODE_KSPLIT_MIN_STEPS
+#define SITU_DECODE_KSPLIT_MIN_STEPS 8
+#endif
+static int decode_ksplit(int K) {
+  const int steps = (K / 32 + 3) / 4;
+  const int m = SITU_DECODE_KSPLIT_MIN_STEPS;   // steps per wave below which K is not split further
+  return steps >= 4 * m ? 4 : (steps >= 2 * m ? 2 : 1);
+}
+
+// Resident workgroups per CU of a kernel (from its register and LDS use),
+// queried once per kernel; a persistent grid is sized to what fits.
+using GemmKernel = void (*)(GemmArgs);
+
+template <GemmKernel KERNEL>
+static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hipStream_t s, uint32_t lds_bytes = 0) {
+  // occupancy depends on the dynamic LDS size; cache per size
+  static int per_cu = 0;
+  static uint32_t per_cu_lds = 0xffffffffu;
+  if (per_cu_lds != lds_bytes) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERNEL, kGemmThreads, lds_bytes) != hipSuccess || n < 1) n = 1;
+    per_cu = n;
+    per_cu_lds = lds_bytes;
+  }
+  const int64_t cap = (int64_t)cus * per_cu;
+  const int grid = (int)(work < cap ? work : cap);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(kGemmThreads), lds_bytes, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fc2(int tactic, const GemmArgs& a, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+template <bool FP8, bool FC1>
+hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
+  switch (decode_ksplit(a.K)) {
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32));
+  }
+}
+
+// Work items of one launch, upper bound: m-tiles x column units per workgroup.
+static int64_t work_items(bool fc1, bool decode, const GemmArgs& a, int max_mtiles) {
+  int64_t units, per_wg;
+  if (fc1) units = a.N / kFc1ColsPerWave;
+  else units = (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
+  per_wg = decode ? 4 / decode_ksplit(a.K) : 4;
+  return (int64_t)max_mtiles * ((units + per_wg - 1) / per_wg);
+}
+
+hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
+  const bool decode = tactic == FC1_W4A16_M16 || tactic == FC1_W4A8_M16;
+  const int64_t work = work_items(true, decode, a, max_mtiles);
   switch (tactic) {
-    case FC2_W4A16_M16: hipLaunchKernelGGL((fc2_kernel<false, 1>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC2_W4A16_M64: hipLaunchKernelGGL((fc2_kernel<false, 4>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC2_W4A8_M16: hipLaunchKernelGGL((fc2_kernel<true, 1>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
-    case FC2_W4A8_M64: hipLaunchKernelGGL((fc2_kernel<true, 4>), dim3(grid), dim3(kGemmThreads), 0, s, a); break;
+    case FC1_W4A16_M16: return launch_decode<false, true>(a, work, cus, s);
+    case FC1_W4A16_M64: return launch_persistent<fc1_kernel<false, 4>>(a, work, cus, s);
+    case FC1_W4A8_M16: return launch_decode<true, true>(a, work, cus, s);
+    case FC1_W4A8_M64: return launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
+  const bool decode = tactic == FC2_W4A16_M16 || tactic == FC2_W4A8_M16;
+  const int64_t work = work_items(false, decode, a, max_mtiles);
+  switch (tactic) {
+    case FC2_W4A16_M16: return launch_decode<false, false>(a, work, cus, s);
+    case FC2_W4A16_M64: return launch_persistent<fc2_kernel<false, 4>>(a, work, cus, s);
+    case FC2_W4A8_M16: return launch_decode<true, false>(a, work, cus, s);
+    case FC2_W4A8_M64: return launch_persistent<fc2_kernel<true, 4>>(a, work, cus, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace situ

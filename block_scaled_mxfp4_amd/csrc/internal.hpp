@@ -70,8 +70,9 @@ struct CombineArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_quant_mxfp8(const QuantArgs& a, hipStream_t s);
 // tactic ids select the activation format and the token tile count
-hipError_t launch_fc1(int tactic, const GemmArgs& a, int grid, hipStream_t s);
-hipError_t launch_fc2(int tactic, const GemmArgs& a, int grid, hipStream_t s);
+// The GEMM launchers size a persistent grid from the m-tile bound and the CU count.
+hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
+hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // Tactic family: (activation format, token tiles of 16 per m-tile)

@@ -339,11 +339,7 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.N = (int32_t)I;
   g.out = at<void>(ws, plan->off_h);
   g.out_scale = w4a8 ? at<uint8_t>(ws, plan->off_hs) : nullptr;
-  const int64_t fc1_units = I / situ::kFc1ColsPerWave;
-  const int64_t fc1_work = (int64_t)plan->max_mtiles * ((fc1_units + 3) / 4);
-  const int64_t persistent = (int64_t)cus * 4;
-  int grid1 = (int)(fc1_work < persistent ? fc1_work : persistent);
-  if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, grid1, s), "fc1")) != SITU_OK) return st;
+  if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, plan->max_mtiles, cus, s), "fc1")) != SITU_OK) return st;
   if ((st = mark(3)) != SITU_OK) return st;
 
   // FC2
@@ -356,10 +352,7 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.N = (int32_t)H;
   g.out = at<void>(ws, plan->off_y);
   g.out_scale = nullptr;
-  const int64_t fc2_wgn = (H + 4 * situ::kFc2RowsPerWave - 1) / (4 * situ::kFc2RowsPerWave);
-  const int64_t fc2_work = (int64_t)plan->max_mtiles * fc2_wgn;
-  int grid2 = (int)(fc2_work < persistent ? fc2_work : persistent);
-  if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, grid2, s), "fc2")) != SITU_OK) return st;
+  if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, plan->max_mtiles, cus, s), "fc2")) != SITU_OK) return st;
   if ((st = mark(4)) != SITU_OK) return st;
 
   // combine
