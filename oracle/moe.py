@@ -28,19 +28,14 @@ What is computed, step by step, and where each step comes from:
 5. Rounding point R1 after FC1: w4a16 rounds h to bf16; w4a8 quantizes h to
    MXFP8 (per 32 along I) and dequantizes it ("the FC1 fp8 output is
    dequantized to bf16 before FC2").
-6. FC2 down product.  y is fp32 in w4a16.  In w4a8 it is rounded to bf16
-   (rounding point R2): the w4a8 chain's FC2 kernels are named
-   Bfloat16_MxE2m1MxE4m3 on the "TokenSpeed SiTU" page (bundle contents),
-   i.e. bf16 output from MxE2m1 weights and MxE4m3 activations, the same
-   naming that gives FC1 its MxE4m3 (MXFP8) output.  The pages name no
-   output dtype for the w4a16 FC2, so y stays fp32 there.
+6. FC2 down product, y in fp32.
 7. Combine: out[t] = sum over local slots, in slot order, of w[t, s] * y.
    Tokens with no local slot give an exact zero row.
 
 Precision modes.  "f64" (the parity reference): every product and sum in
 float64, rounded to float32 at each point where the layer holds float32
-(acc, g, u, h, y, out).  With rounding=False the rounding points R1 and R2
-are skipped too, giving the exact real-number result used by the shard-sum
+(acc, g, u, h, y, out).  With rounding=False the rounding points R1 are
+skipped too, giving the exact real-number result used by the shard-sum
 invariants.  "f32": float32 BLAS, the timed CPU baseline.
 
 Pins (tests/test_oracle_moe.py): brute-force dense unrouted MoE on tiny
@@ -241,10 +236,7 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
         else:
             hq = np.asarray(h, np.float64)
         W2d = F.dequant_mxfp4(w2[l], w2s[l]).astype(dt)            # [H, I]
-        y = rnd(hq.astype(dt) @ W2d.T)                             # [n, H]
-        if rounding and act_mode == "w4a8":                        # R2: bf16 FC2 output
-            y = F.bf16_to_f64(F.f32_to_bf16_rne(_f32(y))).astype(dt)
-        Y[compact[pos]] = y
+        Y[compact[pos]] = rnd(hq.astype(dt) @ W2d.T)               # [n, H]
         if keep_intermediates:
             Hq[compact[pos]] = hq
             Acc[compact[pos]] = acc

@@ -327,25 +327,3 @@ def test_fc1_output_rounding_point(mode):
                 err = np.abs(blocks[q, b] - xb[q, b]) / sc
                 clip = np.maximum(np.abs(xb[q, b]) / sc - 448.0, 0.0)   # OCP rule saturates at 448
                 assert np.all(err <= np.maximum(np.maximum(m, 2.0 ** -6) * 2.0 ** -4, clip) + 1e-6)
-
-
-def test_w4a8_fc2_output_is_bf16():
-    # R2: in w4a8 the FC2 rows are bf16 before the combine; in w4a16 they stay fp32.
-    spec = _spec(T=8, k=3, E_g=6, E_l=6, H=256, I=64, mode="w4a8", seed=28)
-    inp = S.generate(spec)
-    r = _fwd(inp, spec, act_mode="w4a8", keep_intermediates=True)
-    y = r["y"]
-    assert np.array_equal(F.bf16_to_f64(F.f32_to_bf16_rne(y.astype(np.float32))), y)
-    r16 = _fwd(inp, spec, act_mode="w4a16", keep_intermediates=True)
-    y16 = r16["y"]
-    assert not np.array_equal(F.bf16_to_f64(F.f32_to_bf16_rne(y16.astype(np.float32))), y16)
-    # the combine of bf16 rows equals the weighted slot sum of those rows
-    ids, w = M.topk_of(inp)
-    pos = {int(p): q for q, p in enumerate(r["pairs"])}
-    for t in range(spec["T"]):
-        want = np.zeros(spec["H"])
-        for s_ in range(spec["k"]):
-            p = int(r["inv"][t * spec["k"] + s_])
-            if p >= 0:
-                want += w[t, s_] * y[pos[p]]
-        assert np.allclose(r["out"][t], want, rtol=1e-6, atol=1e-9)

@@ -55,7 +55,7 @@ MOE_PINS = [TM.test_routed_equals_dense_unrouted_moe, TM.test_golden_per_token_s
             TM.test_w4a8_activation_scale_applied_once, TM.test_fc1_products_integer_exact,
             TM.test_situ_large_beta_is_swiglu, TM.test_situ_zeros_and_bounds,
             TM.test_situ_with_k3_constants_matches_mpmath_free_closed_form,
-            TM.test_tp_shards_sum_to_unsharded, TM.test_w4a8_fc2_output_is_bf16]
+            TM.test_tp_shards_sum_to_unsharded]
 
 MOE_MUTATIONS = [
     ("sigmoid of the squashed gate", "(beta * np.tanh(g / beta) * sigmoid(g))",
@@ -70,7 +70,6 @@ MOE_MUTATIONS = [
     ("token index from wrong divisor", "rows_t = perm[pos] // k", "rows_t = perm[pos] % T"),
     ("combine weight of wrong slot", "out[has] += wts[tokens[has], s][:, None]", "out[has] += wts[tokens[has], 0][:, None]"),
     ("no bf16 rounding of h", "hq = F.bf16_to_f64(F.f32_to_bf16_rne(_f32(h)))", "hq = np.asarray(h, np.float64)"),
-    ("no bf16 rounding of the w4a8 FC2 rows", 'if rounding and act_mode == "w4a8":', "if False:"),
     ("activation scale applied twice",
      "return F.mx_dequantize(codes, scales, \"e4m3\"), codes, scales",
      "return F.mx_dequantize(codes, scales, \"e4m3\") * F.mx_dequantize(np.full_like(codes, 0x38), scales, \"e4m3\"), codes, scales"),
