@@ -55,10 +55,11 @@ class SituMoePlan(ctypes.Structure):
     _fields_ = [("prob", SituMoeProblem),
                 ("fc1_tactic", ctypes.c_int32), ("fc2_tactic", ctypes.c_int32),
                 ("block_m", ctypes.c_int32), ("max_mtiles", ctypes.c_int32),
+                ("route_blocks", ctypes.c_int32), ("route_chunk", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)] + \
                [(n, ctypes.c_uint64) for n in (
                    "off_counts", "off_offsets", "off_mtiles", "off_tile_expert", "off_perm", "off_inv",
-                   "off_xq", "off_xs", "off_h", "off_hs", "off_y")] + \
+                   "off_xq", "off_xs", "off_h", "off_hs", "off_y", "off_route_hist")] + \
                [("reserved", ctypes.c_uint32 * 8)]
 
 
@@ -275,7 +276,7 @@ def new_workspace(plan, device=None):
 
 _REGIONS = {"counts": "off_counts", "offsets": "off_offsets", "mtiles": "off_mtiles",
             "tile_expert": "off_tile_expert", "perm": "off_perm", "inv": "off_inv", "xq": "off_xq",
-            "xs": "off_xs", "h": "off_h", "hs": "off_hs", "y": "off_y"}
+            "xs": "off_xs", "h": "off_h", "hs": "off_hs", "y": "off_y", "route_hist": "off_route_hist"}
 
 
 def workspace_view(plan, workspace, region, dtype, shape):

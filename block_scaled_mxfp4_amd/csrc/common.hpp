@@ -104,20 +104,18 @@ __device__ __forceinline__ f32x4 mfma_scale_fp4_fp8(const uint32_t a[4], const u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
 }
 
-__device__ __forceinline__ float sigmoid_fast(float z) {
-  // 1 / (1 + e^-z) with the hardware exp2 and reciprocal; saturates cleanly
-  // to 0 and 1 because exp2 overflows to +inf and 1/inf = 0.
-  float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
-  return __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)], with each
-// c*tanh(x/c) written as 2c*sigmoid(2x/c) - c so that no tanh is evaluated
-// (the identity the MegaMoE commit "SiTU in the kernel" uses).
-__device__ __forceinline__ float situ_act(float g, float u, float b, float lb, float inv_b, float inv_lb) {
-  float tg = 2.0f * b * sigmoid_fast(2.0f * g * inv_b) - b;
-  float tu = 2.0f * lb * sigmoid_fast(2.0f * u * inv_lb) - lb;
-  return tg * sigmoid_fast(g) * tu;
+// SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)] in fp32 with the
+// accurate tanhf/expf and IEEE division.  The result feeds a rounding point
+// (bf16, or MXFP8 whose E4M3 steps are 6-12 % apart): h within a few fp32 ulp
+// of the exact value keeps rounding decisions that differ from the exact
+// result rare.  The tanh-free form 2c*sigmoid(2x/c) - c with hardware
+// exp2/reciprocal (the MegaMoE commit's identity) loses accuracy by
+// cancellation near x = 0 and is not used.
+__device__ __forceinline__ float situ_act(float g, float u, float b, float lb) {
+  const float tg = b * tanhf(g / b);
+  const float sg = 1.0f / (1.0f + expf(-g));
+  const float tu = lb * tanhf(u / lb);
+  return tg * sg * tu;
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

@@ -149,7 +149,6 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
     const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
     const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
     const float b = a.beta[l], lb = a.lbeta[l];
-    const float inv_b = 1.0f / b, inv_lb = 1.0f / lb;
 #pragma unroll
     for (int tt = 0; tt < TOKT; ++tt) {
       const int64_t p = p0 + 16 * tt + r;
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          hv[half][i] = situ_act(ag * acc[half][tt][i], au * acc[2 + half][tt][i], b, lb, inv_b, inv_lb);
+          hv[half][i] = situ_act(ag * acc[half][tt][i], au * acc[2 + half][tt][i], b, lb);
       if constexpr (!FP8) {
         if (valid[tt]) {
           uint16_t* hrow = static_cast<uint16_t*>(a.out) + p * I + n0 + 4 * g;
@@ -593,13 +592,12 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
         const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
         const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
         const float bb = a.beta[l], lb = a.lbeta[l];
-        const float inv_b = 1.0f / bb, inv_lb = 1.0f / lb;
         float hv[2][4];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, inv_b, inv_lb);
+            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb);
         if constexpr (!FP8) {
           if (valid) {
             uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
@@ -702,7 +700,9 @@ hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
     case FC1_W4A16_M16: return launch_decode<false, true>(a, work, cus, s);
     case FC1_W4A16_M64: return launch_persistent<fc1_kernel<false, 4>>(a, work, cus, s);
     case FC1_W4A8_M16: return launch_decode<true, true>(a, work, cus, s);
-    case FC1_W4A8_M64: return launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
+    case FC1_W4A8_M64:
+      if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill<true>(a, max_mtiles, cus, s);
+      return launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -714,7 +714,10 @@ hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
     case FC2_W4A16_M16: return launch_decode<false, false>(a, work, cus, s);
     case FC2_W4A16_M64: return launch_persistent<fc2_kernel<false, 4>>(a, work, cus, s);
     case FC2_W4A8_M16: return launch_decode<true, false>(a, work, cus, s);
-    case FC2_W4A8_M64: return launch_persistent<fc2_kernel<true, 4>>(a, work, cus, s);
+    case FC2_W4A8_M64:   // the LDS kernel addresses h with 32-bit offsets
+      if (a.K % 128 == 0 && (int64_t)max_mtiles * 64 * a.K < ((int64_t)1 << 31))
+        return launch_prefill<false>(a, max_mtiles, cus, s);
+      return launch_persistent<fc2_kernel<true, 4>>(a, work, cus, s);
     default: return hipErrorInvalidValue;
   }
 }

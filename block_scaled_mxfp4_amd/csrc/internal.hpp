@@ -20,6 +20,9 @@ struct RouteArgs {
   int32_t* tile_expert;    // [max_mtiles]
   int32_t* perm;           // [TK]
   int32_t* inv;            // [TK]
+  int32_t* hist;           // [nblocks, E_l] (multi-block routing only)
+  int64_t chunk;           // pairs per block
+  int32_t nblocks;         // 1 = single-workgroup routing
 };
 
 struct QuantArgs {
@@ -74,6 +77,10 @@ hipError_t launch_quant_mxfp8(const QuantArgs& a, hipStream_t s);
 hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
 hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// LDS-tiled block-scaled MFMA kernels for prefill-sized groups in w4a8
+// (K a multiple of 128; FC1 also needs I a multiple of 128).
+template <bool FC1>
+hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
 
 // Tactic family: (activation format, token tiles of 16 per m-tile)
 enum Tactic : int32_t {

@@ -7,7 +7,7 @@
 // inside a group they keep ascending expanded index j = t*k + s, so the
 // grouping is a stable sort on (l, j) and the same on every run.
 //
-// One workgroup of 16 waves does it all in LDS, with wavefront ballots:
+// Small batches: one workgroup of 16 waves does it all in LDS:
 //   A. wave w counts the pairs of its contiguous chunk of j into cnt[w][l];
 //   B. per expert, an exclusive scan over waves turns cnt into per-wave
 //      bases; a workgroup scan over experts gives offsets[] and the m-tile
@@ -17,6 +17,10 @@
 //      among the lanes holding the same expert comes from ballots over the
 //      key bits (a wavefront "match"), so position = base + rank needs no
 //      atomics and is independent of scheduling.
+// Large batches split the pairs into contiguous blocks: per-block histograms,
+// one scan workgroup (prefix over blocks, then over experts), and a scatter
+// in which every block repeats A and C on its own pairs from its own bases.
+// Every position depends only on the input, never on timing.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -31,53 +35,72 @@ __device__ __forceinline__ int local_expert_of(const RouteArgs& a, int64_t j) {
   return (l >= 0 && l < a.E_l) ? l : -1;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
-  __shared__ int cnt[kRouteWaves][kMaxLocalExperts];
-  __shared__ int scan_a[kMaxLocalExperts];
-  __shared__ int scan_b[kMaxLocalExperts];
-  __shared__ int wave_sums[2][kRouteWaves];
-
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-  const int64_t TK = a.TK;
-  const int64_t chunk = (TK + kRouteWaves - 1) / kRouteWaves;
-  const int64_t j0 = (int64_t)wave * chunk;
-  const int64_t j1 = j0 + chunk < TK ? j0 + chunk : TK;
-
+// Pairs [j0, j1) are split into kRouteWaves contiguous sub-chunks, one per
+// wave, in order.  Each wave counts its sub-chunk into cnt[wave][l].
+__device__ void count_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts]) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   for (int i = tid; i < kRouteWaves * kMaxLocalExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
-
-  // A. per-wave histogram
-  for (int64_t base = j0; base < j1; base += kWave) {
-    int64_t j = base + lane;
-    if (j < j1) {
-      int l = local_expert_of(a, j);
+  const int64_t chunk = (j1 - j0 + kRouteWaves - 1) / kRouteWaves;
+  const int64_t w0 = j0 + (int64_t)wave * chunk;
+  const int64_t w1 = w0 + chunk < j1 ? w0 + chunk : j1;
+  for (int64_t base = w0; base < w1; base += kWave) {
+    const int64_t j = base + lane;
+    if (j < w1) {
+      const int l = local_expert_of(a, j);
       if (l >= 0) atomicAdd(&cnt[wave][l], 1);
     }
   }
   __syncthreads();
+}
 
-  // B1. per expert: exclusive scan over waves; totals into scan_a / scan_b
-  for (int l = tid; l < a.E_l; l += kRouteThreads) {
-    int run = 0;
-    for (int w = 0; w < kRouteWaves; ++w) {
-      int c = cnt[w][l];
-      cnt[w][l] = run;
-      run += c;
+// cnt[w][l] holds the first position of wave w's pairs of expert l; walk the
+// sub-chunks again 64 pairs at a time and place each pair at base + its rank
+// among the lanes holding the same expert (ballots over the key bits).
+__device__ void scatter_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts]) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t chunk = (j1 - j0 + kRouteWaves - 1) / kRouteWaves;
+  const int64_t w0 = j0 + (int64_t)wave * chunk;
+  const int64_t w1 = w0 + chunk < j1 ? w0 + chunk : j1;
+  int nbits = 0;
+  while ((1 << nbits) < a.E_l) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int64_t base = w0; base < w1; base += kWave) {
+    const int64_t j = base + lane;
+    const bool in = j < w1;
+    const int l = in ? local_expert_of(a, j) : -1;
+    const bool loc = l >= 0;
+    uint64_t eq = __ballot(loc);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = loc && ((l >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      eq &= bit ? bb : ~bb;
     }
-    scan_a[l] = run;
-    scan_b[l] = (run + a.block_m - 1) / a.block_m;
+    if (loc) {
+      const int rank = __popcll(eq & lt_mask);
+      const int total = __popcll(eq);
+      const int pos = cnt[wave][l] + rank;
+      a.perm[pos] = (int)j;
+      a.inv[j] = pos;
+      if (rank == total - 1) cnt[wave][l] = pos + 1;
+    } else if (in) {
+      a.inv[j] = -1;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  __syncthreads();
+}
 
-  // B2. workgroup exclusive scan over experts (E_l <= 1024 = one value per thread)
-  int va = tid < a.E_l ? scan_a[tid] : 0;
-  int vb = tid < a.E_l ? scan_b[tid] : 0;
-  int ia = va, ib = vb;  // inclusive scan within the wave
+// Workgroup exclusive scans over the experts (E_l <= 1024, one per thread) of
+// the totals and of their m-tile counts; writes counts, offsets, mtiles and
+// the tile -> expert list.  Returns the exclusive offset of expert tid.
+__device__ int scan_experts(const RouteArgs& a, int total_of_tid, int (*wave_sums)[kRouteWaves]) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int va = tid < a.E_l ? total_of_tid : 0;
+  const int vb = tid < a.E_l ? (va + a.block_m - 1) / a.block_m : 0;
+  int ia = va, ib = vb;
   for (int d = 1; d < kWave; d <<= 1) {
-    int ta = __shfl_up(ia, d, kWave);
-    int tb = __shfl_up(ib, d, kWave);
+    const int ta = __shfl_up(ia, d, kWave);
+    const int tb = __shfl_up(ib, d, kWave);
     if (lane >= d) { ia += ta; ib += tb; }
   }
   if (lane == kWave - 1) { wave_sums[0][wave] = ia; wave_sums[1][wave] = ib; }
@@ -96,46 +119,100 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     a.offsets[a.E_l] = excl_a + va;
     a.mtiles[a.E_l] = excl_b + vb;
   }
-  __syncthreads();
-  if (tid < a.E_l) scan_a[tid] = excl_a;   // group start of expert tid
-  __syncthreads();
-  for (int i = tid; i < kRouteWaves * a.E_l; i += kRouteThreads) {
-    int w = i / a.E_l, l = i % a.E_l;
-    cnt[w][l] += scan_a[l];
-  }
-  __syncthreads();
+  return excl_a;
+}
 
-  // C. ranks by ballot match; positions; perm and inv
-  int nbits = 0;
-  while ((1 << nbits) < a.E_l) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int64_t base = j0; base < j1; base += kWave) {
-    int64_t j = base + lane;
-    bool in = j < j1;
-    int l = in ? local_expert_of(a, j) : -1;
-    bool loc = l >= 0;
-    uint64_t eq = __ballot(loc);
-    for (int b = 0; b < nbits; ++b) {
-      bool bit = loc && ((l >> b) & 1);
-      uint64_t bb = __ballot(bit);
-      eq &= bit ? bb : ~bb;
+// Small batches: one workgroup does everything in LDS.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+  __shared__ int cnt[kRouteWaves][kMaxLocalExperts];
+  __shared__ int offs[kMaxLocalExperts];
+  __shared__ int wave_sums[2][kRouteWaves];
+  const int tid = threadIdx.x;
+  count_waves(a, 0, a.TK, cnt);
+  // per expert: exclusive scan over waves, total
+  int total = 0;
+  for (int l = tid; l < a.E_l; l += kRouteThreads) {
+    int run = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = cnt[w][l];
+      cnt[w][l] = run;
+      run += c;
     }
-    if (loc) {
-      int rank = __popcll(eq & lt_mask);
-      int total = __popcll(eq);
-      int pos = cnt[wave][l] + rank;
-      a.perm[pos] = (int)j;
-      a.inv[j] = pos;
-      if (rank == total - 1) cnt[wave][l] = pos + 1;
-    } else if (in) {
-      a.inv[j] = -1;
-    }
-    __builtin_amdgcn_wave_barrier();
+    total = run;
   }
+  __syncthreads();
+  const int excl = scan_experts(a, total, wave_sums);
+  if (tid < a.E_l) offs[tid] = excl;
+  __syncthreads();
+  for (int i = tid; i < kRouteWaves * a.E_l; i += kRouteThreads) cnt[i / a.E_l][i % a.E_l] += offs[i % a.E_l];
+  __syncthreads();
+  scatter_waves(a, 0, a.TK, cnt);
+}
+
+// Large batches, three launches.  Block b owns the pairs [b*C, (b+1)*C).
+// 1. per-block histograms -> hist[b][l]
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a) {
+  __shared__ int h[kMaxLocalExperts];
+  const int tid = threadIdx.x;
+  for (int l = tid; l < kMaxLocalExperts; l += kRouteThreads) h[l] = 0;
+  __syncthreads();
+  const int64_t j0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t j1 = j0 + a.chunk < a.TK ? j0 + a.chunk : a.TK;
+  for (int64_t j = j0 + tid; j < j1; j += kRouteThreads) {
+    const int l = local_expert_of(a, j);
+    if (l >= 0) atomicAdd(&h[l], 1);
+  }
+  __syncthreads();
+  for (int l = tid; l < a.E_l; l += kRouteThreads) a.hist[(int64_t)blockIdx.x * a.E_l + l] = h[l];
+}
+
+// 2. one workgroup: per expert, exclusive prefix over blocks; expert scans;
+//    hist[b][l] becomes the first position of block b's pairs of expert l.
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) {
+  __shared__ int wave_sums[2][kRouteWaves];
+  const int tid = threadIdx.x;
+  int total = 0;
+  if (tid < a.E_l) {
+    int run = 0;
+    for (int b = 0; b < a.nblocks; ++b) {
+      const int c = a.hist[(int64_t)b * a.E_l + tid];
+      a.hist[(int64_t)b * a.E_l + tid] = run;
+      run += c;
+    }
+    total = run;
+  }
+  const int excl = scan_experts(a, total, wave_sums);
+  if (tid < a.E_l)
+    for (int b = 0; b < a.nblocks; ++b) a.hist[(int64_t)b * a.E_l + tid] += excl;
+}
+
+// 3. per block: per-wave counts again, bases from hist[b][l], scatter.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a) {
+  __shared__ int cnt[kRouteWaves][kMaxLocalExperts];
+  const int tid = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t j1 = j0 + a.chunk < a.TK ? j0 + a.chunk : a.TK;
+  count_waves(a, j0, j1, cnt);
+  for (int l = tid; l < a.E_l; l += kRouteThreads) {
+    int run = a.hist[(int64_t)blockIdx.x * a.E_l + l];
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = cnt[w][l];
+      cnt[w][l] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  scatter_waves(a, j0, j1, cnt);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+  if (a.nblocks <= 1) {
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_count_kernel, dim3(a.nblocks), dim3(kRouteThreads), 0, s, a);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(a.nblocks), dim3(kRouteThreads), 0, s, a);
   return hipGetLastError();
 }
 

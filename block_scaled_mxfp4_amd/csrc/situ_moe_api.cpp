@@ -41,6 +41,7 @@ situ_status fail(situ_status st, const char* fmt, ...) {
 }
 
 constexpr uint64_t kAlign = 256;
+constexpr int64_t kRouteSingleMax = 32768;   // pairs routed by a single workgroup
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct TacticInfo {
@@ -98,6 +99,10 @@ situ_status validate(const situ_moe_problem* p) {
     return fail(SITU_E_UNSUPPORTED, "out_dtype %d", p->out_dtype);
   const int64_t tk = (int64_t)p->num_tokens * p->top_k;
   if (tk >= (int64_t)1 << 31) return fail(SITU_E_UNSUPPORTED, "num_tokens * top_k = %lld exceeds int32", (long long)tk);
+  // activation rows are addressed with 32-bit offsets from one buffer resource
+  if ((int64_t)p->num_tokens * p->hidden_size * 2 >= (int64_t)1 << 31)
+    return fail(SITU_E_UNSUPPORTED, "hidden states of %lld bytes exceed 2 GiB",
+                (long long)p->num_tokens * p->hidden_size * 2);
   return SITU_OK;
 }
 
@@ -199,6 +204,9 @@ situ::RouteArgs route_args(const situ_moe_plan_t* plan, const situ_moe_tensors* 
   r.tile_expert = at<int32_t>(ws, plan->off_tile_expert);
   r.perm = at<int32_t>(ws, plan->off_perm);
   r.inv = at<int32_t>(ws, plan->off_inv);
+  r.hist = at<int32_t>(ws, plan->off_route_hist);
+  r.chunk = plan->route_chunk;
+  r.nblocks = plan->route_blocks;
   return r;
 }
 
@@ -254,6 +262,17 @@ situ_status situ_moe_plan(const situ_moe_problem* problem, situ_moe_plan_t* plan
   plan->off_h = region(TK * I * (w4a8 ? 1 : 2));
   plan->off_hs = region(w4a8 ? TK * I / 32 : 0);
   plan->off_y = region(TK * H * 4);
+  // routing: one workgroup for small batches, else blocks of >= 4096 pairs (<= 1024 blocks)
+  if (TK <= kRouteSingleMax) {
+    plan->route_blocks = 1;
+    plan->route_chunk = (int32_t)TK;
+  } else {
+    int64_t chunk = 4096;
+    if ((TK + chunk - 1) / chunk > 1024) chunk = (TK + 1023) / 1024;
+    plan->route_chunk = (int32_t)chunk;
+    plan->route_blocks = (int32_t)((TK + chunk - 1) / chunk);
+  }
+  plan->off_route_hist = region(plan->route_blocks > 1 ? 4 * (uint64_t)plan->route_blocks * E_l : 0);
   plan->workspace_bytes = off;
   return SITU_OK;
 }

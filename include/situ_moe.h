@@ -91,6 +91,8 @@ typedef struct situ_moe_plan_t {
   int32_t fc2_tactic;
   int32_t block_m;              /* rows (token-expert pairs) per m-tile */
   int32_t max_mtiles;           /* upper bound of m-tiles: T*k / block_m + E_l */
+  int32_t route_blocks;         /* 1 = one-workgroup routing; else blocks of route_chunk pairs */
+  int32_t route_chunk;
   uint64_t workspace_bytes;     /* bytes the caller must provide */
   /* byte offsets into the workspace (each 256-byte aligned) */
   uint64_t off_counts;          /* int32 [E_l]      pairs per local expert */
@@ -104,6 +106,7 @@ typedef struct situ_moe_plan_t {
   uint64_t off_h;               /* FC1 output rows in perm order: bf16 [T*k, I] (w4a16) or E4M3 [T*k, I] (w4a8) */
   uint64_t off_hs;              /* uint8 [T*k, I/32] E8M0 scales of h (w4a8) */
   uint64_t off_y;               /* float [T*k, H]   FC2 output rows in perm order */
+  uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms (route_blocks > 1) */
   uint32_t reserved[8];
 } situ_moe_plan_t;
 

@@ -209,6 +209,7 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
     Y = np.zeros((need.shape[0], H), dtype=dt)
     Hq = np.zeros((need.shape[0], I), dtype=np.float64) if keep_intermediates else None
     Acc = np.zeros((need.shape[0], 2 * I), dtype=np.float64) if keep_intermediates else None
+    Hpre = np.zeros((need.shape[0], I), dtype=np.float64) if keep_intermediates else None
 
     for l in range(E_l):
         p0, p1 = int(offsets[l]), int(offsets[l + 1])
@@ -240,6 +241,7 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
         if keep_intermediates:
             Hq[compact[pos]] = hq
             Acc[compact[pos]] = acc
+            Hpre[compact[pos]] = np.asarray(h, np.float64)
 
     # Combine in slot order; a token with no local slot keeps its zero row.
     out = np.zeros((tokens.shape[0], H), dtype=np.float64)
@@ -256,6 +258,7 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
     if keep_intermediates:
         res["pairs"] = need          # permuted positions of the rows below
         res["acc"] = Acc
+        res["h_pre"] = Hpre        # SiTU output before the rounding point R1
         res["h"] = Hq
         res["y"] = Y.astype(np.float64)
     return res

@@ -77,16 +77,104 @@ def oracle_out(inp, spec, mode=None, tokens=None, prequantized=False, keep=False
                          act_mode=mode, act_prequantized=prequantized, tokens=tokens, keep_intermediates=keep)
 
 
-def parity(got, want, what=""):
+# Relative distance to a rounding midpoint below which either rounding of an
+# element of h is a correct result: the GPU computes h in fp32 within a few
+# ulp (~1e-7) of the oracle's correctly rounded value, so 2^-16 leaves a wide
+# margin while excusing only elements that sit on a rounding boundary.
+AMBIGUITY = 2.0 ** -16
+
+
+def _bf16_ambiguity(v):
+    """Size of the other bf16 rounding choice of v where v is within
+    AMBIGUITY of a bf16 rounding midpoint, else 0."""
+    v = np.asarray(v, np.float64)
+    q = F.bf16_to_f64(F.f32_to_bf16_rne(v.astype(np.float32)))
+    a = np.abs(v)
+    ulp = np.ldexp(1.0, F.floor_log2(np.where(a > 0, a, 1.0)) - 7)
+    amb = (a > 0) & (ulp / 2 - np.abs(v - q) <= AMBIGUITY * a)
+    return np.where(amb, ulp, 0.0)
+
+
+def _mxfp8_ambiguity(v):
+    """The same for MXFP8 rows (32-element blocks along the last axis): an
+    element near an E4M3 rounding midpoint under its block scale, or a whole
+    block whose max is within AMBIGUITY of a power of two (two candidate
+    E8M0 scales), may round either way."""
+    v = np.asarray(v, np.float64)
+    n, I = v.shape
+    codes, sc = F.mx_quantize(v, "e4m3")
+    q = F.mx_dequantize(codes, sc, "e4m3")
+    scale = np.repeat(F.decode_e8m0(sc), 32, axis=-1)
+    s = v / scale
+    a = np.abs(s)
+    spacing = np.where(a < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, F.floor_log2(np.where(a > 0, a, 1.0)) - 3))
+    amb = (a > 0) & (a < 448.0) & (spacing / 2 - np.abs(s - q / scale) <= AMBIGUITY * a)
+    d = np.where(amb, spacing * scale, 0.0)
+    # block scale ambiguity
+    blocks = np.abs(v).reshape(n, I // 32, 32).max(-1)
+    m = blocks / np.ldexp(1.0, F.floor_log2(np.where(blocks > 0, blocks, 1.0)))
+    near = (blocks > 0) & ((m - 1.0 <= AMBIGUITY) | (2.0 - m <= 2 * AMBIGUITY))
+    if near.any():
+        for sgn in (-1, 1):
+            alt_sc = np.clip(sc.astype(np.int64) + sgn, 0, 254).astype(np.uint8)
+            alt_scale = np.repeat(F.decode_e8m0(alt_sc), 32, axis=-1)
+            alt_q = F.mx_dequantize(F.encode_e4m3(v / alt_scale), alt_sc, "e4m3")
+            dd = np.abs(alt_q - q) * np.repeat(near, 32, axis=-1)
+            d = np.maximum(d, dd)
+    return d
+
+
+def rounding_allowance(inp, spec, ref, mode):
+    """Per-output-element bound of how far a correct result may differ from
+    the oracle's because of the rounding point after FC1 alone (see
+    AMBIGUITY).  ref must come from oracle_out(..., keep=True).  Zero for
+    almost every element."""
+    hpre = ref["h_pre"]
+    d = _bf16_ambiguity(hpre) if mode == "w4a16" else _mxfp8_ambiguity(hpre)
+    tokens = ref["tokens"]
+    A = np.zeros((tokens.shape[0], spec["H"]))
+    rows = np.nonzero(d.any(axis=1))[0]
+    if rows.size == 0:
+        return A
+    pairs = ref["pairs"]
+    offsets = ref["offsets"]
+    ids, wts = M.topk_of(inp)
+    k = spec["k"]
+    inv = ref["inv"].reshape(-1, k)
+    effect = {}
+    for q in rows:
+        p = int(pairs[q])
+        l = int(np.searchsorted(offsets, p, side="right") - 1)
+        W2 = np.abs(F.dequant_mxfp4(inp["w2"][l], inp["w2_scale"][l]))
+        effect[p] = W2 @ d[q]
+    for i, t in enumerate(tokens):
+        for s_ in range(k):
+            p = int(inv[t, s_])
+            if p in effect:
+                A[i] += abs(wts[t, s_]) * effect[p]
+    return A
+
+
+def parity(got, want, what="", allowance=None):
+    """The parity bar: cosine >= 0.9995 and max-abs <= 1e-2 x RMS(oracle), on
+    the fp32 outputs; where allowance is given, the part of an element's
+    difference that a legitimately different rounding decision explains
+    (rounding_allowance) is not counted against max-abs."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     rms = np.sqrt(np.mean(want ** 2))
-    maxabs = np.max(np.abs(got - want)) if got.size else 0.0
+    diff = np.abs(got - want)
+    raw = np.max(diff) if got.size else 0.0
+    if allowance is not None:
+        diff = np.maximum(diff - allowance, 0.0)
+    maxabs = np.max(diff) if got.size else 0.0
     denom = np.linalg.norm(got) * np.linalg.norm(want)
     cos = float(np.dot(got.ravel(), want.ravel()) / denom) if denom > 0 else (1.0 if maxabs == 0 else 0.0)
-    msg = f"{what}: cosine {cos:.7f}, max-abs {maxabs:.3e} = {maxabs / max(rms, 1e-300):.2e} x RMS {rms:.3e}"
+    n_amb = int(np.count_nonzero(allowance)) if allowance is not None else 0
+    msg = (f"{what}: cosine {cos:.7f}, max-abs {maxabs:.3e} = {maxabs / max(rms, 1e-300):.2e} x RMS {rms:.3e}"
+           f" (raw {raw / max(rms, 1e-300):.2e}; {n_amb} elements with a rounding allowance)")
     print(msg, flush=True)
     assert cos >= COS_MIN, msg
     assert maxabs <= MAXABS_FRAC * rms, msg

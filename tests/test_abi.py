@@ -104,6 +104,7 @@ def _status(fn):
     (dict(tactic=(2, 18)), "SITU_E_UNSUPPORTED"),    # w4a8 tactics on a w4a16 problem
     (dict(tactic=(0, -1)), "SITU_OK"),
     (dict(num_tokens=0), "SITU_OK"),
+    (dict(num_tokens=300000), "SITU_E_UNSUPPORTED"),   # 2.15 GB of hidden states
 ])
 def test_plan_validation(kw, want):
     assert _status(lambda: B.situ_moe_plan(_prob(**kw))) == want
@@ -125,13 +126,18 @@ def test_plan_layout_and_tactics():
                  "off_tile_expert": 4 * plan.max_mtiles, "off_perm": 4 * T * k, "off_inv": 4 * T * k,
                  "off_xq": T * H if w4a8 else 0, "off_xs": T * H // 32 if w4a8 else 0,
                  "off_h": T * k * I * (1 if w4a8 else 2), "off_hs": T * k * I // 32 if w4a8 else 0,
-                 "off_y": 4 * T * k * H}
+                 "off_y": 4 * T * k * H,
+                 "off_route_hist": 4 * plan.route_blocks * E if plan.route_blocks > 1 else 0}
         spans = sorted((getattr(plan, n), getattr(plan, n) + s) for n, s in sizes.items())
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0
         assert all(getattr(plan, n) % 256 == 0 for n in sizes)
         assert spans[-1][1] <= plan.workspace_bytes
         assert plan.max_mtiles >= (T * k + plan.block_m - 1) // plan.block_m
+    # decode batches are routed by one workgroup, prefill batches by blocks
+    assert B.situ_moe_plan(_prob()).route_blocks == 1
+    big = B.situ_moe_plan(_prob(num_tokens=32768, local_num_experts=112, local_expert_offset=336))
+    assert big.route_blocks == 128 and big.route_chunk == 4096
     # decode shapes take 16-row m-tiles, prefill shapes 64-row ones
     assert B.situ_moe_plan(_prob()).block_m == 16
     assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a8")).block_m == 64
