@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
     const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
     const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
     const float b = a.beta[l], lb = a.lbeta[l];
+    const float rb = 1.0f / b, rlb = 1.0f / lb;
 #pragma unroll
     for (int tt = 0; tt < TOKT; ++tt) {
       const int64_t p = p0 + 16 * tt + r;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          hv[half][i] = situ_act(ag * acc[half][tt][i], au * acc[2 + half][tt][i], b, lb);
+          hv[half][i] = situ_act(ag * acc[half][tt][i], au * acc[2 + half][tt][i], b, lb, rb, rlb);
       if constexpr (!FP8) {
         if (valid[tt]) {
           uint16_t* hrow = static_cast<uint16_t*>(a.out) + p * I + n0 + 4 * g;
@@ -592,12 +593,13 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
         const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
         const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
         const float bb = a.beta[l], lb = a.lbeta[l];
+        const float rb = 1.0f / bb, rlb = 1.0f / lb;
         float hv[2][4];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb);
+            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, rb, rlb);
         if constexpr (!FP8) {
           if (valid) {
             uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;

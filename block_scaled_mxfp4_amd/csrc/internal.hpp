@@ -18,6 +18,7 @@ struct RouteArgs {
   int32_t* offsets;        // [E_l+1]
   int32_t* mtiles;         // [E_l+1]
   int32_t* tile_expert;    // [max_mtiles]
+  int32_t* tile_rows;      // [max_mtiles, 2] (p0, p1) of each m-tile
   int32_t* perm;           // [TK]
   int32_t* inv;            // [TK]
   int32_t* hist;           // [nblocks, E_l] (multi-block routing only)
@@ -45,6 +46,7 @@ struct GemmArgs {
   const int32_t* offsets;     // [E_l+1]
   const int32_t* mtiles;      // [E_l+1] (mtiles[E_l] = number of m-tiles)
   const int32_t* tile_expert; // [max_mtiles]
+  const int32_t* tile_rows;   // [max_mtiles, 2] first / one-past-last pair of each m-tile
   const uint8_t* w;           // MXFP4 [E_l, N_total, K/2]
   const uint8_t* ws;          // E8M0 [E_l, N_total, K/32]
   int32_t K;                  // contraction length (H for FC1, I for FC2)

@@ -13,8 +13,14 @@
 //  - per 128-wide K step the workgroup stages 16 KB of weights, 8 KB of
 //    activations and their scales in LDS, laid out as the MFMA fragments
 //    themselves (lane l's 16 bytes at 16*l), so the fragment reads are
-//    conflict-free ds_read_b128; two LDS stages, and the global loads of
-//    step j+2 travel in registers while step j is multiplied;
+//    conflict-free ds_read_b128;
+//  - the stages are filled by LDS DMA (buffer_load ... lds): global data goes
+//    straight to LDS without passing through registers, so a ring of
+//    kPfStages stages keeps kPfStages - 1 K steps in flight while one is
+//    multiplied.  Each stage is its own LDS array, which lets the compiler
+//    wait for exactly the DMA that filled the stage being read; the
+//    workgroup barrier that publishes a stage waits on this wave's DMA count
+//    explicitly (all loads return in order);
 //  - work items are ordered expert-major with the 64-row m-tiles fastest,
 //    so consecutive items reuse one weight tile, and each XCD walks its own
 //    contiguous range of items (blockIdx % 8 picks the XCD), keeping a
@@ -22,6 +28,7 @@
 // K must be a multiple of 128 (H = 3584 is 28 steps; I = 384 or 3072); the
 // planner routes other shapes to the 16-row kernels.
 #include "common.hpp"
+#include "dma.hpp"
 #include "internal.hpp"
 
 namespace situ {
@@ -35,229 +42,353 @@ constexpr int kStageB = 4 * 2048;
 constexpr int kStageSA = kPfRows * 4;
 constexpr int kStageSB = kPfTok * 4;
 constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;   // 25856 bytes
+#ifndef SITU_PF_STAGES
+#define SITU_PF_STAGES 3
+#endif
+constexpr int kPfStages = SITU_PF_STAGES;    // 3 x 25856 B: two workgroups per CU
+static_assert(kPfStages >= 2 && kPfStages <= 4, "stage ring of 2..4");
+// Whether a stage wait may count output stores issued after the stage's DMA
+// (only sound if stores and loads leave the vector-memory counter in issue
+// order); 0 = count DMAs only, which also waits for those stores.
+#ifndef SITU_PF_COUNT_STORES
+#define SITU_PF_COUNT_STORES 0
+#endif
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-  v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-constexpr uint32_t kOobPf = 0x80000000u;   // past every resource: reads 0
-
-// What one thread loads for one K step (then writes to LDS).
-struct PfRegs {
-  uint4 a[4];     // 4 weight tiles' fragments of this lane
-  uint4 b[2];     // lo / hi halves of one activation tile's fragment
-  uint32_t sa;    // scale dword (4 K blocks) of weight row `tid`
-  uint32_t sb;    // scale dword of token `tid` (tid < 64)
-};
+constexpr uint32_t kOobPf = kOobOff;
 
 struct PfGeo {
-  __amdgpu_buffer_rsrc_t wr, sr, xr, xsr;
+  v4i wr, sr, xr, xsr;
   uint32_t a_row[4];   // byte offset of this lane's row in each of its 4 weight tiles
-  uint32_t sa_row;     // scale row offset of weight row `tid`
+  uint32_t sa_row;     // scale row offset of weight row 64*wave + lane
   uint32_t b_row;      // byte offset of this lane's activation row (kOobPf if none)
-  uint32_t sb_row;     // scale row offset of token `tid` (kOobPf if none)
+  uint32_t sb_row;     // scale row offset of the same token (kOobPf if none)
   int g;
 };
 
-__device__ __forceinline__ void pf_load(PfRegs& rg, const PfGeo& d, int j) {
+// This wave's share of one K step, as kPfDmas DMA instructions: its 4 weight
+// tiles, the lo / hi halves of its token tile, the scale dwords of weight
+// rows 64*wave .. +63 and of tokens 16*wave .. +15 (lanes 0..15).  A lane
+// past the data reads zeros; a DMA writes lane l's bytes at dst + size * l.
+constexpr int kPfDmas = 8;
+__device__ __forceinline__ void pf_issue(uint32_t st, const PfGeo& d, int j, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rg.a[i] = ld16(d.wr, d.a_row[i] + (uint32_t)(4 * j + d.g) * 16u);
+  for (int i = 0; i < 4; ++i) dma16(d.wr, st + (4 * wave + i) * 1024, d.a_row[i] + (uint32_t)(4 * j + d.g) * 16u);
   const uint32_t lo = d.b_row == kOobPf ? kOobPf : d.b_row + 128u * j + 16u * d.g;
-  rg.b[0] = ld16(d.xr, lo);
-  rg.b[1] = ld16(d.xr, lo == kOobPf ? kOobPf : lo + 64u);
-  rg.sa = ld4(d.sr, d.sa_row + 4u * j);
-  rg.sb = ld4(d.xsr, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
+  dma16(d.xr, st + kStageA + wave * 2048, lo);
+  dma16(d.xr, st + kStageA + wave * 2048 + 1024, lo == kOobPf ? kOobPf : lo + 64u);
+  dma4(d.sr, st + kStageA + kStageB + wave * 256, d.sa_row + 4u * j);
+  if (lane < 16)
+    dma4(d.xsr, st + kStageA + kStageB + kStageSA + wave * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
 }
 
-__device__ __forceinline__ void pf_store(uint8_t* st, const PfRegs& rg, int wave, int lane, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + (4 * wave + i) * 1024 + lane * 16) = rg.a[i];
-  *reinterpret_cast<uint4*>(st + kStageA + wave * 2048 + lane * 16) = rg.b[0];
-  *reinterpret_cast<uint4*>(st + kStageA + wave * 2048 + 1024 + lane * 16) = rg.b[1];
-  *reinterpret_cast<uint32_t*>(st + kStageA + kStageB + tid * 4) = rg.sa;
-  if (tid < kPfTok) *reinterpret_cast<uint32_t*>(st + kStageA + kStageB + kStageSA + tid * 4) = rg.sb;
+// `after` = K steps whose DMAs this wave issued after the one to wait for;
+// `st`: the previous item's NST output stores were also issued after it.
+template <int NST>
+__device__ __forceinline__ void step_barrier(int after, bool st) {
+  if (st) {
+    if (after >= 2) dma_barrier<2 * kPfDmas + NST>();
+    else if (after == 1) dma_barrier<kPfDmas + NST>();
+    else dma_barrier<NST>();
+  } else {
+    if (after >= 2) dma_barrier<2 * kPfDmas>();
+    else if (after == 1) dma_barrier<kPfDmas>();
+    else dma_barrier<0>();
+  }
 }
 
-// One K step of one wave: 8 weight tiles x 2 token tiles of MFMAs.
+// One K step of one wave: 8 weight tiles x 2 token tiles of MFMAs.  All of
+// the step's fragment reads are issued before the first MFMA, so each MFMA
+// pair waits only for its own weight fragment while the later reads are in
+// flight (one register set per fragment: 58 VGPRs).
 __device__ __forceinline__ void pf_compute(const uint8_t* st, bool fc1, int wn, int wm, int lane, f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4;
-  uint32_t bf[2][8], sb[2];
+  uint4 blo[2], bhi[2];
+  uint32_t sb[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int tile = 2 * wm + tt;
-    const uint4 lo = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + lane * 16);
-    const uint4 hi = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + 1024 + lane * 16);
-    bf[tt][0] = lo.x; bf[tt][1] = lo.y; bf[tt][2] = lo.z; bf[tt][3] = lo.w;
-    bf[tt][4] = hi.x; bf[tt][5] = hi.y; bf[tt][6] = hi.z; bf[tt][7] = hi.w;
+    blo[tt] = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + lane * 16);
+    bhi[tt] = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + 1024 + lane * 16);
     sb[tt] = st[kStageA + kStageB + kStageSA + (16 * tile + r) * 4 + g];
   }
+  uint4 av[8];
+  uint32_t sa[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     // FC1: gate tiles 4wn..4wn+3 then the matching up tiles 8+4wn..; FC2: tiles 8wn..8wn+7
     const int tile = fc1 ? (i < 4 ? 4 * wn + i : 8 + 4 * wn + (i - 4)) : 8 * wn + i;
-    const uint4 av = *reinterpret_cast<const uint4*>(st + tile * 1024 + lane * 16);
-    const uint32_t a4[4] = {av.x, av.y, av.z, av.w};
-    const uint32_t sa = st[kStageA + kStageB + (16 * tile + r) * 4 + g];
+    av[i] = *reinterpret_cast<const uint4*>(st + tile * 1024 + lane * 16);
+    sa[i] = st[kStageA + kStageB + (16 * tile + r) * 4 + g];
+  }
+  uint32_t bf[2][8];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa, sb[tt], acc[i][tt]);
+  for (int tt = 0; tt < 2; ++tt) {
+    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
+    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
+  }
+  // keep that order: the scheduler would otherwise sink each read to its
+  // MFMA pair to save registers, exposing every read's latency
+  __builtin_amdgcn_sched_group_barrier(0x100, 22, 0);   // 22 LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
+}
+
+// Work item -> expert, n-tile and pair range; items are ordered expert-major
+// with the m-tiles of one n-tile fastest.
+struct PfItem {
+  int l, nt, p0, p1;
+};
+__device__ __forceinline__ PfItem pf_item(const GemmArgs& a, int it, int n_tiles) {
+  const cptr te = (cptr)a.tile_expert, mt = (cptr)a.mtiles, of = (cptr)a.offsets;
+  PfItem x;
+  x.l = te[it / n_tiles];
+  const int m0 = mt[x.l], m_l = mt[x.l + 1] - m0;
+  const int rr = it - m0 * n_tiles;
+  x.nt = rr / m_l;
+  x.p0 = of[x.l] + (rr % m_l) * kPfTok;
+  x.p1 = min(of[x.l + 1], x.p0 + kPfTok);
+  return x;
+}
+// Activation row of this lane's token (token tile `wave_u`, token r): FC1
+// reads x[perm[p] / k], FC2 reads h[p]; -1 past the group.  The 16 perm
+// entries of a token tile come in one scalar load (the perm region is padded
+// by a tile's worth of entries past its end).
+template <bool FC1>
+__device__ __forceinline__ int32_t pf_act_row(const GemmArgs& a, const PfItem& x, int wave_u, int r) {
+  const int base = x.p0 + 16 * wave_u;
+  if (base + r >= x.p1) return -1;
+  if constexpr (!FC1) return base + r;
+  const cptr pp = (cptr)a.perm + base;
+  int32_t v = pp[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    const int32_t w = pp[i];
+    v = r == i ? w : v;
+  }
+  return v / a.top_k;
+}
+
+// Load geometry of one item for this thread.
+template <bool FC1>
+__device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, int32_t trow, int tid, int wave, int r,
+                                        int g) {
+  const int K = a.K, nkb = K / 32;
+  const int n_rows = FC1 ? 2 * a.N : a.N;
+  PfGeo d;
+  d.g = g;
+  const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * n_rows * nkb, (uint32_t)(n_rows * nkb));
+  const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
+  // weight rows of the 4 tiles this thread loads (tiles 4*wave .. 4*wave+3)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * wave + i;
+    const int row = FC1 ? (t < 8 ? n0 + 16 * t : a.N + n0 + 16 * (t - 8)) + r : n0 + 16 * t + r;
+    d.a_row[i] = (uint32_t)row * (uint32_t)(K / 2);       // rows past H (FC2) read zeros
+  }
+  const int srow = FC1 ? (tid < 128 ? n0 + tid : a.N + n0 + tid - 128) : n0 + tid;
+  d.sa_row = (uint32_t)srow * (uint32_t)nkb;
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  d.b_row = trow >= 0 ? (uint32_t)trow * (uint32_t)K : kOobPf;
+  d.sb_row = trow >= 0 ? (uint32_t)trow * (uint32_t)nkb : kOobPf;
+  return d;
+}
+
+// Output stores as inline assembly too, a fixed number per wave and item
+// (lanes with nothing to store use an offset past the buffer, which drops
+// the write), so that the waits of the next item's first steps can count
+// them.  The compiler's hazard checks do not look inside inline assembly, so
+// these carry their own: the data must not come straight from an MFMA (whose
+// result may still be in flight), so st16 takes it through a VALU add (+0
+// turns -0 into +0) that the compiler orders after the MFMA, with two wait
+// states before the store reads it; and a store reads its data registers
+// after issue, so wait states follow it before any later write of them.
+__device__ __forceinline__ void st16(const v4i& r, uint32_t voff, f32x4 v) {
+  const f32x4 w = v + 0.0f;
+  asm volatile("s_nop 1\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void st4(const v4i& r, uint32_t voff, uint32_t v) {
+  asm volatile("buffer_store_dword %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
+}
+__device__ __forceinline__ void st1(const v4i& r, uint32_t voff, uint32_t v) {
+  asm volatile("buffer_store_byte %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
+}
+constexpr int kPfStoresFc1 = 12;   // 2 token tiles x 2 MXFP8 blocks x (2 code dwords + 1 scale byte)
+constexpr int kPfStoresFc2 = 16;   // 2 token tiles x 8 row tiles of fp32
+
+// FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
+// FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
+template <bool FC1>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
+                                            int r, int g) {
+  const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
+  if constexpr (FC1) {
+    const int I = a.N;
+    const cptr ag_p = (cptr)a.alpha_g, au_p = (cptr)a.alpha_u;
+    const float ag = a.alpha_g ? __builtin_bit_cast(float, ag_p[x.l]) : 1.0f;
+    const float au = a.alpha_u ? __builtin_bit_cast(float, au_p[x.l]) : 1.0f;
+    const float bb = __builtin_bit_cast(float, ((cptr)a.beta)[x.l]);
+    const float lb = __builtin_bit_cast(float, ((cptr)a.lbeta)[x.l]);
+    const float rb = 1.0f / bb, rlb = 1.0f / lb;
+    const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(kPfTok * I));
+    const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(kPfTok * (I / 32)));
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int pr = 32 * wm + 16 * tt + r;          // row within the m-tile
+      const bool valid = x.p0 + pr < x.p1;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {          // two 32-column MXFP8 blocks per wave
+        float hv[2][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 2 * blk + h2;
+            hv[h2][e] = situ_act(ag * acc[i][tt][e], au * acc[4 + i][tt][e], bb, lb, rb, rlb);
+            amax = fmaxf(amax, fabsf(hv[h2][e]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
+        const uint32_t code = e8m0_code_for_e4m3(amax);
+        const int sh = 127 - (int)code;
+        uint32_t packed[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          packed[h2] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) packed[h2] |= e4m3_encode(__builtin_ldexpf(hv[h2][e], sh)) << (8 * e);
+        }
+        const uint32_t ho = valid ? (uint32_t)(pr * I + col0 + 4 * g) : kOobPf;
+        st4(hr, ho, packed[0]);
+        st4(hr, valid ? ho + 16u : kOobPf, packed[1]);
+        st1(sr, (valid && g == 0) ? (uint32_t)(pr * (I / 32) + col0 / 32) : kOobPf, code);
+      }
+    }
+  } else {
+    const int H = a.N;
+    const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kPfTok * H * 4));
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int pr = 32 * wm + 16 * tt + r;
+      const bool valid = x.p0 + pr < x.p1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row0 = n0 + 16 * (8 * wn + i);
+        st16(yr, (valid && row0 < H) ? (uint32_t)(pr * H + row0 + 4 * g) * 4u : kOobPf, acc[i][tt]);
+      }
+    }
   }
 }
 
 }  // namespace
 
 template <bool FC1>
-__global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];   // 2 stages
+__global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gemm_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t st0[kStage];
+  __shared__ __align__(16) uint8_t st1[kStage];
+#if SITU_PF_STAGES > 2
+  __shared__ __align__(16) uint8_t st2[kStage];
+#endif
+#if SITU_PF_STAGES > 3
+  __shared__ __align__(16) uint8_t st3[kStage];
+#endif
+#if SITU_PF_STAGES == 2
+  uint8_t* const stg[kPfStages] = {st0, st1};
+#elif SITU_PF_STAGES == 3
+  uint8_t* const stg[kPfStages] = {st0, st1, st2};
+#else
+  uint8_t* const stg[kPfStages] = {st0, st1, st2, st3};
+#endif
+  constexpr int NST = FC1 ? kPfStoresFc1 : kPfStoresFc2;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int r = lane & 15, g = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
-  const int K = a.K, nkb = K / 32, steps = K / 128;
+  const int K = a.K, steps = K / 128;
   const int n_tiles = FC1 ? a.N / 128 : (a.N + kPfRows - 1) / kPfRows;
   const int total = a.mtiles[a.E_l] * n_tiles;
-  const int n_rows = FC1 ? 2 * a.N : a.N;
   // XCD-aware walk: workgroup b runs on XCD b % 8; each XCD takes a contiguous
   // range of items so consecutive items (same weight tile) share its L2.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
   const int chunk = (total + 7) / 8;
   const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  for (int it = i_begin + slot; it < i_end; it += per_xcd_wgs) {
-    // item -> (expert, n-tile, m-tile of the expert), m fastest
-    const int l = a.tile_expert[it / n_tiles];
-    const int m_l = a.mtiles[l + 1] - a.mtiles[l];
-    const int rr = it - a.mtiles[l] * n_tiles;
-    const int nt = rr / m_l, m = rr % m_l;
-    const int p0 = a.offsets[l] + m * kPfTok;
-    const int p1 = min(a.offsets[l + 1], p0 + kPfTok);
-
-    PfGeo d;
-    d.g = g;
-    const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
-    d.wr = rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
-    d.sr = rsrc(a.ws + (size_t)l * n_rows * nkb, (uint32_t)(n_rows * nkb));
-    const int n0 = FC1 ? nt * 128 : nt * kPfRows;
-    // weight rows of the 4 tiles this thread loads (tiles 4*wave .. 4*wave+3)
+  // The ring restarts at stage 0 for every item; the next item's first
+  // kPfStages - 1 stages are requested before this item's output stores, so
+  // their latency overlaps the epilogue.  `stores_after` marks an item whose
+  // first stages were requested before the previous item's NST stores: the
+  // waits of its first steps count those stores too.
+  int it = i_begin + slot;
+  PfItem cur{0, 0, 0, 0};
+  PfGeo d{};
+  if (it < i_end) {
+    cur = pf_item(a, it, n_tiles);
+    d = pf_geo<FC1>(a, cur, pf_act_row<FC1>(a, cur, wave_u, r), tid, wave, r, g);
+    lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * wave + i;
-      const int row = FC1 ? (t < 8 ? n0 + 16 * t : a.N + n0 + 16 * (t - 8)) + r : n0 + 16 * t + r;
-      d.a_row[i] = (uint32_t)row * (uint32_t)(K / 2);       // rows past H (FC2) read zeros
+    for (int u = 0; u < kPfStages - 1; ++u)
+      if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
+  }
+  bool stores_after = false;
+  for (; it < i_end; it += per_xcd_wgs) {
+    // the next item's geometry (scalar loads) while the first stages load
+    const int it_next = it + per_xcd_wgs;
+    PfItem nxt{0, 0, 0, 0};
+    int32_t trow2 = -1;
+    if (it_next < i_end) {
+      nxt = pf_item(a, it_next, n_tiles);
+      trow2 = pf_act_row<FC1>(a, nxt, wave_u, r);
     }
-    {
-      const int row = FC1 ? (tid < 128 ? n0 + tid : a.N + n0 + tid - 128) : n0 + tid;
-      d.sa_row = (uint32_t)row * (uint32_t)nkb;
-    }
-    // activation rows: this thread loads token tile `wave`, token r of it
-    {
-      const int p = p0 + 16 * wave + r;
-      const bool ok = p < p1;
-      int64_t trow = 0;
-      if (ok) trow = FC1 ? (int64_t)(a.perm[p] / a.top_k) : (int64_t)p;
-      d.xr = rsrc(a.act, 0x7fffffff);
-      d.b_row = ok ? (uint32_t)(trow * K) : kOobPf;
-      const int ps = p0 + tid;
-      const bool oks = tid < kPfTok && ps < p1;
-      int64_t srow = 0;
-      if (oks) srow = FC1 ? (int64_t)(a.perm[ps] / a.top_k) : (int64_t)ps;
-      d.xsr = rsrc(a.act_scale, 0x7fffffff);
-      d.sb_row = oks ? (uint32_t)(srow * nkb) : kOobPf;
-    }
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    PfRegs rg;
-    pf_load(rg, d, 0);
-    pf_store(lds, rg, wave, lane, tid);
-    if (steps > 1) pf_load(rg, d, 1);
-    __syncthreads();
-    for (int j = 0; j < steps; ++j) {
-      uint8_t* cur = lds + (j & 1) * kStage;
-      uint8_t* nxt = lds + ((j + 1) & 1) * kStage;
-      pf_compute(cur, FC1, wn, wm, lane, acc);
-      if (j + 1 < steps) {
-        pf_store(nxt, rg, wave, lane, tid);
-        if (j + 2 < steps) pf_load(rg, d, j + 2);
-      }
-      __syncthreads();
-    }
-
-    // epilogue
-    if constexpr (FC1) {
-      const int I = a.N;
-      const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
-      const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
-      const float bb = a.beta[l], lb = a.lbeta[l];
+    for (int j0 = 0; j0 < steps; j0 += kPfStages) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int p = p0 + 32 * wm + 16 * tt + r;
-        const bool valid = p < p1;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {      // two 32-column MXFP8 blocks per wave
-          float hv[2][4];
-          float amax = 0.0f;
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 2 * blk + h2;
-              hv[h2][e] = situ_act(ag * acc[i][tt][e], au * acc[4 + i][tt][e], bb, lb);
-              amax = fmaxf(amax, fabsf(hv[h2][e]));
-            }
-          amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-          amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-          const int col0 = n0 + 64 * wn + 32 * blk;     // first gate column of this block
-          if (valid) {
-            const uint32_t code = e8m0_code_for_e4m3(amax);
-            const int sh = 127 - (int)code;
-            uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + col0 + 4 * g;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              uint32_t packed = 0;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) packed |= e4m3_encode(__builtin_ldexpf(hv[h2][e], sh)) << (8 * e);
-              *reinterpret_cast<uint32_t*>(hrow + 16 * h2) = packed;
-            }
-            if (g == 0) a.out_scale[(int64_t)p * (I / 32) + col0 / 32] = (uint8_t)code;
-          }
-        }
-      }
-    } else {
-      const int H = a.N;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int p = p0 + 32 * wm + 16 * tt + r;
-        if (p >= p1) continue;
-        float* yrow = static_cast<float*>(a.out) + (int64_t)p * H;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row0 = n0 + 16 * (8 * wn + i);
-          if (row0 >= H) continue;                 // uniform: H is a multiple of 16
-          *reinterpret_cast<f32x4*>(yrow + row0 + 4 * g) = acc[i][tt];
+      for (int u = 0; u < kPfStages; ++u) {
+        const int j = j0 + u;
+        if (j < steps) {
+          step_barrier<NST>(min(kPfStages - 2, steps - 1 - j), SITU_PF_COUNT_STORES && stores_after && j < kPfStages - 1);
+          if (j + kPfStages - 1 < steps)
+            pf_issue(lds_addr_of(stg[(u + kPfStages - 1) % kPfStages]), d, j + kPfStages - 1, wave, lane);
+          pf_compute(stg[u], FC1, wn, wm, lane, acc);
         }
       }
     }
+
+    // every wave is done with the stages: request the next item's first ones
+    lds_barrier();
+    if (it_next < i_end) {
+      d = pf_geo<FC1>(a, nxt, trow2, tid, wave, r, g);
+#pragma unroll
+      for (int u = 0; u < kPfStages - 1; ++u)
+        if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
+    }
+    pf_epilogue<FC1>(a, cur, acc, wn, wm, r, g);   // exactly NST stores per wave
+    stores_after = true;
+    cur = nxt;
   }
 }
-
-uint32_t prefill_lds_bytes() { return 2 * kStage; }
 
 template <bool FC1>
 hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
   static int per_cu = 0;
   if (!per_cu) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_gemm_kernel<FC1>, kGemmThreads, 2 * kStage) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_gemm_kernel<FC1>, kGemmThreads, 0) !=
             hipSuccess || n < 1)
       n = 1;
     per_cu = n;
@@ -267,7 +398,7 @@ hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_
   int64_t grid = (int64_t)cus * per_cu;
   if (grid > work) grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_gemm_kernel<FC1>, dim3((unsigned)grid), dim3(kGemmThreads), 2 * kStage, s, a);
+  hipLaunchKernelGGL(prefill_gemm_kernel<FC1>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -113,7 +113,11 @@ __device__ int scan_experts(const RouteArgs& a, int total_of_tid, int (*wave_sum
     a.counts[tid] = va;
     a.offsets[tid] = excl_a;
     a.mtiles[tid] = excl_b;
-    for (int m = 0; m < vb; ++m) a.tile_expert[excl_b + m] = tid;
+    for (int m = 0; m < vb; ++m) {
+      a.tile_expert[excl_b + m] = tid;
+      a.tile_rows[2 * (excl_b + m)] = excl_a + m * a.block_m;
+      a.tile_rows[2 * (excl_b + m) + 1] = min(excl_a + va, excl_a + (m + 1) * a.block_m);
+    }
   }
   if (tid == a.E_l - 1) {
     a.offsets[a.E_l] = excl_a + va;

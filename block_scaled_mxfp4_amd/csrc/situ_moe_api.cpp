@@ -202,6 +202,7 @@ situ::RouteArgs route_args(const situ_moe_plan_t* plan, const situ_moe_tensors* 
   r.offsets = at<int32_t>(ws, plan->off_offsets);
   r.mtiles = at<int32_t>(ws, plan->off_mtiles);
   r.tile_expert = at<int32_t>(ws, plan->off_tile_expert);
+  r.tile_rows = at<int32_t>(ws, plan->off_tile_rows);
   r.perm = at<int32_t>(ws, plan->off_perm);
   r.inv = at<int32_t>(ws, plan->off_inv);
   r.hist = at<int32_t>(ws, plan->off_route_hist);
@@ -253,7 +254,8 @@ situ_status situ_moe_plan(const situ_moe_problem* problem, situ_moe_plan_t* plan
   plan->off_offsets = region(4 * (E_l + 1));
   plan->off_mtiles = region(4 * (E_l + 1));
   plan->off_tile_expert = region(4 * max_mtiles);
-  plan->off_perm = region(4 * TK);
+  plan->off_tile_rows = region(8 * max_mtiles);
+  plan->off_perm = region(4 * (TK + 64));   // a 64-row tile may read its perm entries past the end
   plan->off_inv = region(4 * TK);
   const bool w4a8 = p.act_mode == SITU_ACT_W4A8;
   const bool quant_here = w4a8 && !p.act_prequantized;
@@ -341,6 +343,7 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.offsets = ra.offsets;
   g.mtiles = ra.mtiles;
   g.tile_expert = ra.tile_expert;
+  g.tile_rows = ra.tile_rows;
   g.E_l = p.local_num_experts;
   g.beta = t->situ_beta;
   g.lbeta = t->situ_linear_beta;

@@ -107,7 +107,8 @@ typedef struct situ_moe_plan_t {
   uint64_t off_hs;              /* uint8 [T*k, I/32] E8M0 scales of h (w4a8) */
   uint64_t off_y;               /* float [T*k, H]   FC2 output rows in perm order */
   uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms (route_blocks > 1) */
-  uint32_t reserved[8];
+  uint64_t off_tile_rows;       /* int32 [max_mtiles, 2] first and one-past-last perm position of each m-tile */
+  uint32_t reserved[6];
 } situ_moe_plan_t;
 
 /* Device tensors of one call.  Shapes use T, H, I, k, E_l of the problem. */

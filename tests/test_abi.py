@@ -123,11 +123,12 @@ def test_plan_layout_and_tactics():
         T, k, E, H, I = p.num_tokens, p.top_k, p.local_num_experts, p.hidden_size, p.intermediate_size
         w4a8 = p.act_mode == B.ACT_W4A8
         sizes = {"off_counts": 4 * E, "off_offsets": 4 * (E + 1), "off_mtiles": 4 * (E + 1),
-                 "off_tile_expert": 4 * plan.max_mtiles, "off_perm": 4 * T * k, "off_inv": 4 * T * k,
+                 "off_tile_expert": 4 * plan.max_mtiles, "off_perm": 4 * (T * k + 64), "off_inv": 4 * T * k,
                  "off_xq": T * H if w4a8 else 0, "off_xs": T * H // 32 if w4a8 else 0,
                  "off_h": T * k * I * (1 if w4a8 else 2), "off_hs": T * k * I // 32 if w4a8 else 0,
                  "off_y": 4 * T * k * H,
-                 "off_route_hist": 4 * plan.route_blocks * E if plan.route_blocks > 1 else 0}
+                 "off_route_hist": 4 * plan.route_blocks * E if plan.route_blocks > 1 else 0,
+                 "off_tile_rows": 8 * plan.max_mtiles}
         spans = sorted((getattr(plan, n), getattr(plan, n) + s) for n, s in sizes.items())
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0

@@ -76,6 +76,11 @@ def test_route_bit_exact(cfg):
     assert np.array_equal(ws_region(plan, ws, "mtiles", torch.int32, (E + 1,)), mt)
     te = ws_region(plan, ws, "tile_expert", torch.int32, (int(mt[-1]),))
     assert np.array_equal(te, np.repeat(np.arange(E), (counts + bm - 1) // bm))
+    # each m-tile's pair range: block_m rows from its expert's offset, the last one ragged
+    tr = ws_region(plan, ws, "tile_rows", torch.int32, (int(mt[-1]), 2))
+    first = offsets[te] + (np.arange(int(mt[-1])) - mt[te]) * bm
+    assert np.array_equal(tr[:, 0], first)
+    assert np.array_equal(tr[:, 1], np.minimum(offsets[te + 1], first + bm))
     print(f"config {cfg}: P={P} active={int((counts > 0).sum())} max={int(counts.max())}", flush=True)
 
 
