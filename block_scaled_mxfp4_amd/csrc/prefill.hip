@@ -222,13 +222,15 @@ __device__ __forceinline__ void st1(const v4i& r, uint32_t voff, uint32_t v) {
   asm volatile("buffer_store_byte %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
 }
 constexpr int kPfStoresFc1 = 12;   // 2 token tiles x 2 MXFP8 blocks x (2 code dwords + 1 scale byte)
-constexpr int kPfStoresFc2 = 16;   // 2 token tiles x 8 row tiles of fp32
+constexpr int kPfStoresFc2 = 16;   // 2 token tiles x 2 column halves x 4 row groups of fp32
+static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
 template <bool FC1>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
-                                            int r, int g) {
+                                            int wave, int lane, uint8_t* scratch) {
+  const int r = lane & 15, g = lane >> 4;
   const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
   if constexpr (FC1) {
     const int I = a.N;
@@ -275,18 +277,32 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
       }
     }
   } else {
+    // y rows leave through LDS: a 16-token x 64-column block of the wave's
+    // tiles is written in the MFMA layout and read back row by row, so that
+    // each store instruction writes 4 tokens x 256 contiguous bytes (full
+    // cache lines) instead of 16 tokens x 64 bytes.  scratch = 4352 bytes of
+    // this wave's, in the stage the next item's first requests leave free.
     const int H = a.N;
     const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kPfTok * H * 4));
+    constexpr int kRowPitch = 64 * 4 + 16;          // padded: the tile writes hit 16 distinct bank groups
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int pr = 32 * wm + 16 * tt + r;
-      const bool valid = x.p0 + pr < x.p1;
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row0 = n0 + 16 * (8 * wn + i);
-        st16(yr, (valid && row0 < H) ? (uint32_t)(pr * H + row0 + 4 * g) * 4u : kOobPf, acc[i][tt]);
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(scratch + r * kRowPitch + (16 * i + 4 * g) * 4) = acc[4 * half + i][tt];
+        const int tok = lane >> 4, chunk = lane & 15;
+        const int col = n0 + 16 * 8 * wn + 64 * half + 4 * chunk;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = 4 * k + tok;                  // token within the 16-token tile
+          const f32x4 v = *reinterpret_cast<const f32x4*>(scratch + t * kRowPitch + 16 * chunk);
+          const int pr = 32 * wm + 16 * tt + t;
+          const bool ok = x.p0 + pr < x.p1 && col < H;
+          st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
+        }
       }
-    }
   }
 }
 
@@ -377,7 +393,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
       for (int u = 0; u < kPfStages - 1; ++u)
         if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
     }
-    pf_epilogue<FC1>(a, cur, acc, wn, wm, r, g);   // exactly NST stores per wave
+    // exactly NST stores per wave; the last stage is free for FC2's transpose
+    pf_epilogue<FC1>(a, cur, acc, wn, wm, wave, lane, stg[kPfStages - 1] + wave * 4352);
     stores_after = true;
     cur = nxt;
   }
