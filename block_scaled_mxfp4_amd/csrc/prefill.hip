@@ -38,7 +38,10 @@ namespace {
 constexpr int kPfRows = 256;      // weight rows per work item
 constexpr int kPfTok = 64;        // token rows per work item (the m-tile)
 constexpr int kStageA = 16 * 1024;
-constexpr int kStageB = 4 * 2048;
+// activation tile: 2 DMA blocks of 8 tokens x 128 B (full cache lines),
+// 128 B apart so that the fragment reads of 16 tokens hit distinct banks
+constexpr int kTileB = 2 * (1024 + 128);
+constexpr int kStageB = 4 * kTileB;
 constexpr int kStageSA = kPfRows * 4;
 constexpr int kStageSB = kPfTok * 4;
 constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;   // 25856 bytes
@@ -60,9 +63,9 @@ struct PfGeo {
   v4i wr, sr, xr, xsr;
   uint32_t a_row[4];   // byte offset of this lane's row in each of its 4 weight tiles
   uint32_t sa_row;     // scale row offset of weight row 64*wave + lane
-  uint32_t b_row;      // byte offset of this lane's activation row (kOobPf if none)
-  uint32_t sb_row;     // scale row offset of the same token (kOobPf if none)
-  int g;
+  uint32_t b_row[2];   // activation row of token l/8 (+8 for the second block) of the wave's tile (kOobPf: none)
+  uint32_t sb_row;     // scale row offset of token l%16 (kOobPf if none)
+  int g, lane;
 };
 
 // This wave's share of one K step, as kPfDmas DMA instructions: its 4 weight
@@ -73,9 +76,14 @@ constexpr int kPfDmas = 8;
 __device__ __forceinline__ void pf_issue(uint32_t st, const PfGeo& d, int j, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16(d.wr, st + (4 * wave + i) * 1024, d.a_row[i] + (uint32_t)(4 * j + d.g) * 16u);
-  const uint32_t lo = d.b_row == kOobPf ? kOobPf : d.b_row + 128u * j + 16u * d.g;
-  dma16(d.xr, st + kStageA + wave * 2048, lo);
-  dma16(d.xr, st + kStageA + wave * 2048 + 1024, lo == kOobPf ? kOobPf : lo + 64u);
+  // activations: lane l moves 16-byte chunk (l%8) ^ (l/8) of token 8h + l/8 (h = block),
+  // so each instruction reads 8 whole 128-byte K slices and a token's chunk c
+  // lands in slot c ^ (token % 8) of its row
+  const uint32_t chunk = (uint32_t)(((d.lane & 7) ^ (d.lane >> 3)) * 16);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    dma16(d.xr, st + kStageA + wave * kTileB + h * (1024 + 128),
+          d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * j + chunk);
   dma4(d.sr, st + kStageA + kStageB + wave * 256, d.sa_row + 4u * j);
   if (lane < 16)
     dma4(d.xsr, st + kStageA + kStageB + kStageSA + wave * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
@@ -107,8 +115,10 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, bool fc1, int wn, 
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int tile = 2 * wm + tt;
-    blo[tt] = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + lane * 16);
-    bhi[tt] = *reinterpret_cast<const uint4*>(st + kStageA + tile * 2048 + 1024 + lane * 16);
+    // token r: K 16g.. (chunk g) and K 64 + 16g.. (chunk 4 + g), in their swizzled slots
+    const uint8_t* row = st + kStageA + tile * kTileB + (r >> 3) * (1024 + 128) + (r & 7) * 128;
+    blo[tt] = *reinterpret_cast<const uint4*>(row + 16 * (g ^ (r & 7)));
+    bhi[tt] = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ (r & 7)));
     sb[tt] = st[kStageA + kStageB + kStageSA + (16 * tile + r) * 4 + g];
   }
   uint4 av[8];
@@ -154,33 +164,55 @@ __device__ __forceinline__ PfItem pf_item(const GemmArgs& a, int it, int n_tiles
   x.p1 = min(of[x.l + 1], x.p0 + kPfTok);
   return x;
 }
-// Activation row of this lane's token (token tile `wave_u`, token r): FC1
-// reads x[perm[p] / k], FC2 reads h[p]; -1 past the group.  The 16 perm
-// entries of a token tile come in one scalar load (the perm region is padded
-// by a tile's worth of entries past its end).
+// Activation rows of the tokens this lane touches in its wave's token tile
+// (tile `wave_u`): token l%16 (its scale dword) and tokens l/8, 8 + l/8
+// (its 16-byte chunks).  FC1 reads x[perm[p] / k], FC2 reads h[p]; -1 past
+// the group.  The tile's 16 perm entries come in one scalar load (the perm
+// region is padded by a tile's worth of entries past its end).
+struct PfRows {
+  int32_t t_s, t_a, t_b;
+};
 template <bool FC1>
-__device__ __forceinline__ int32_t pf_act_row(const GemmArgs& a, const PfItem& x, int wave_u, int r) {
+__device__ __forceinline__ PfRows pf_act_rows(const GemmArgs& a, const PfItem& x, int wave_u, int lane) {
   const int base = x.p0 + 16 * wave_u;
-  if (base + r >= x.p1) return -1;
-  if constexpr (!FC1) return base + r;
-  const cptr pp = (cptr)a.perm + base;
-  int32_t v = pp[0];
+  const int i_s = lane & 15, i_a = lane >> 3, i_b = 8 + (lane >> 3);
+  PfRows t{-1, -1, -1};
+  if (base >= x.p1) return t;                       // uniform: the whole tile is past the group
+  if constexpr (!FC1) {
+    t.t_s = base + i_s;
+    t.t_a = base + i_a;
+    t.t_b = base + i_b;
+  } else {
+    typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+    const i32x16 win = *(const __attribute__((address_space(4))) i32x16*)((cptr)a.perm + base);
+    int32_t vs = win[0], va = win[0], vb = win[8];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    const int32_t w = pp[i];
-    v = r == i ? w : v;
+    for (int i = 1; i < 16; ++i) vs = i_s == i ? win[i] : vs;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      va = i_a == i ? win[i] : va;
+      vb = i_b == 8 + i ? win[8 + i] : vb;
+    }
+    t.t_s = vs / a.top_k;
+    t.t_a = va / a.top_k;
+    t.t_b = vb / a.top_k;
   }
-  return v / a.top_k;
+  if (base + i_s >= x.p1) t.t_s = -1;
+  if (base + i_a >= x.p1) t.t_a = -1;
+  if (base + i_b >= x.p1) t.t_b = -1;
+  return t;
 }
 
 // Load geometry of one item for this thread.
 template <bool FC1>
-__device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, int32_t trow, int tid, int wave, int r,
-                                        int g) {
+__device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int tid, int wave,
+                                        int lane) {
+  const int r = lane & 15, g = lane >> 4;
   const int K = a.K, nkb = K / 32;
   const int n_rows = FC1 ? 2 * a.N : a.N;
   PfGeo d;
   d.g = g;
+  d.lane = lane;
   const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
   d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
   d.sr = rsrc4(a.ws + (size_t)x.l * n_rows * nkb, (uint32_t)(n_rows * nkb));
@@ -196,8 +228,9 @@ __device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, int3
   d.sa_row = (uint32_t)srow * (uint32_t)nkb;
   d.xr = rsrc4(a.act, 0x7fffffff);
   d.xsr = rsrc4(a.act_scale, 0x7fffffff);
-  d.b_row = trow >= 0 ? (uint32_t)trow * (uint32_t)K : kOobPf;
-  d.sb_row = trow >= 0 ? (uint32_t)trow * (uint32_t)nkb : kOobPf;
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)K : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)nkb : kOobPf;
   return d;
 }
 
@@ -351,7 +384,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
   PfGeo d{};
   if (it < i_end) {
     cur = pf_item(a, it, n_tiles);
-    d = pf_geo<FC1>(a, cur, pf_act_row<FC1>(a, cur, wave_u, r), tid, wave, r, g);
+    d = pf_geo<FC1>(a, cur, pf_act_rows<FC1>(a, cur, wave_u, lane), tid, wave, lane);
     lds_barrier();
 #pragma unroll
     for (int u = 0; u < kPfStages - 1; ++u)
@@ -362,10 +395,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
     // the next item's geometry (scalar loads) while the first stages load
     const int it_next = it + per_xcd_wgs;
     PfItem nxt{0, 0, 0, 0};
-    int32_t trow2 = -1;
+    PfRows trow2{-1, -1, -1};
     if (it_next < i_end) {
       nxt = pf_item(a, it_next, n_tiles);
-      trow2 = pf_act_row<FC1>(a, nxt, wave_u, r);
+      trow2 = pf_act_rows<FC1>(a, nxt, wave_u, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -388,7 +421,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
     // every wave is done with the stages: request the next item's first ones
     lds_barrier();
     if (it_next < i_end) {
-      d = pf_geo<FC1>(a, nxt, trow2, tid, wave, r, g);
+      d = pf_geo<FC1>(a, nxt, trow2, tid, wave, lane);
 #pragma unroll
       for (int u = 0; u < kPfStages - 1; ++u)
         if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
