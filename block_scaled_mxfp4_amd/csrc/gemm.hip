@@ -705,6 +705,9 @@ hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
     case FC1_W4A8_M64:
       if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill<true>(a, max_mtiles, cus, s);
       return launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
+    case FC1_W4A8_M128:   // offered only where K and N are multiples of 128
+      if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill_wide<true>(a, max_mtiles, cus, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -720,6 +723,10 @@ hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
       if (a.K % 128 == 0 && (int64_t)max_mtiles * 64 * a.K < ((int64_t)1 << 31))
         return launch_prefill<false>(a, max_mtiles, cus, s);
       return launch_persistent<fc2_kernel<true, 4>>(a, work, cus, s);
+    case FC2_W4A8_M128:
+      if (a.K % 128 == 0 && (int64_t)max_mtiles * 128 * a.K < ((int64_t)1 << 31))
+        return launch_prefill_wide<false>(a, max_mtiles, cus, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -83,6 +83,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // (K a multiple of 128; FC1 also needs I a multiple of 128).
 template <bool FC1>
 hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
+template <bool FC1>
+hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s);
 
 // Tactic family: (activation format, token tiles of 16 per m-tile)
 enum Tactic : int32_t {
@@ -90,10 +92,12 @@ enum Tactic : int32_t {
   FC1_W4A16_M64 = 1,
   FC1_W4A8_M16 = 2,
   FC1_W4A8_M64 = 3,
+  FC1_W4A8_M128 = 4,
   FC2_W4A16_M16 = 16,
   FC2_W4A16_M64 = 17,
   FC2_W4A8_M16 = 18,
   FC2_W4A8_M64 = 19,
+  FC2_W4A8_M128 = 20,
 };
 
 // Workgroup shapes of the grouped GEMMs (4 waves of 64 lanes).

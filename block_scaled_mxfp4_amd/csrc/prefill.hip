@@ -260,7 +260,7 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
-template <bool FC1>
+template <bool FC1, int TOK = kPfTok>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
                                             int wave, int lane, uint8_t* scratch) {
   const int r = lane & 15, g = lane >> 4;
@@ -273,8 +273,8 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     const float bb = __builtin_bit_cast(float, ((cptr)a.beta)[x.l]);
     const float lb = __builtin_bit_cast(float, ((cptr)a.lbeta)[x.l]);
     const float rb = 1.0f / bb, rlb = 1.0f / lb;
-    const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(kPfTok * I));
-    const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(kPfTok * (I / 32)));
+    const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(TOK * I));
+    const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int pr = 32 * wm + 16 * tt + r;          // row within the m-tile
@@ -316,7 +316,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     // cache lines) instead of 16 tokens x 64 bytes.  scratch = 4352 bytes of
     // this wave's, in the stage the next item's first requests leave free.
     const int H = a.N;
-    const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kPfTok * H * 4));
+    const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
     constexpr int kRowPitch = 64 * 4 + 16;          // padded: the tile writes hit 16 distinct bank groups
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -432,6 +432,239 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
     cur = nxt;
   }
 }
+
+// ---------------------------------------------------------------------------
+// Wide prefill kernel: 256 weight rows x 128 tokens per item, 8 waves (each
+// 128 rows x 32 tokens, the same 8 x 2 MFMA tiles), stages of two K steps.
+// With two K steps a weight row contributes 128 contiguous bytes per stage,
+// so the weight DMAs also move whole cache lines (8 rows x 128 B per
+// instruction, swizzled like the activations); the larger token tile halves
+// the weight bytes staged per MFMA.  Two stages of 73 KB: one workgroup per
+// CU.  Routed with 128-row m-tiles.
+namespace {
+
+constexpr int kWRows = 256, kWTok = 128, kWThreads = 512;
+constexpr int kWTileSw = 2 * (1024 + 128);                 // one 16-row (or 16-token) swizzled tile
+constexpr int kWStA = 0;                                    // 16 weight tiles
+constexpr int kWStB = kWStA + 16 * kWTileSw;                // [2 steps][8 token tiles]
+constexpr int kWStSA = kWStB + 16 * kWTileSw;               // [2 steps][256 rows] scale dwords
+constexpr int kWStSB = kWStSA + 2 * kWRows * 4;             // [8 token tiles][2 steps][16 tokens]
+constexpr int kWStage = kWStSB + kWTok * 2 * 4;             // 74752 bytes
+constexpr int kWDmas = 10;                                  // DMAs per wave per stage
+
+struct PwGeo {
+  v4i wr, sr, xr, xsr;
+  uint32_t a_row[2][2];  // [tile][block]: row offset of this lane's row (kOobPf: none)
+  uint32_t sa_row;       // scale row of weight row 64*(wave&3) + lane
+  uint32_t b_row[2];     // activation rows of tokens 16*wave + l/8 (+8)
+  uint32_t sb_row;       // scale row of token 16*wave + l%16
+  int wave, lane, K;
+};
+
+template <bool FC1>
+__device__ __forceinline__ int pw_wrow(const GemmArgs& a, int n0, int t) {   // first row of weight tile t
+  return FC1 ? (t < 8 ? n0 + 16 * t : a.N + n0 + 16 * (t - 8)) : n0 + 16 * t;
+}
+
+template <bool FC1>
+__device__ __forceinline__ PwGeo pw_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
+  const int K = a.K, nkb = K / 32;
+  const int n_rows = FC1 ? 2 * a.N : a.N;
+  PwGeo d;
+  d.wave = wave;
+  d.lane = lane;
+  d.K = K;
+  const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * n_rows * nkb, (uint32_t)(n_rows * nkb));
+  const int n0 = FC1 ? x.nt * 128 : x.nt * kWRows;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = pw_wrow<FC1>(a, n0, 2 * wave + i) + 8 * h + (lane >> 3);
+      d.a_row[i][h] = (FC1 || row < a.N) ? (uint32_t)row * (uint32_t)(K / 2) : kOobPf;
+    }
+  {
+    const int q = wave & 3, row_in = 64 * q + lane;            // weight row 0..255 of the item
+    const int row = FC1 ? (row_in < 128 ? n0 + row_in : a.N + n0 + row_in - 128) : n0 + row_in;
+    d.sa_row = (FC1 || row < a.N) ? (uint32_t)row * (uint32_t)nkb : kOobPf;
+  }
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)K : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)nkb : kOobPf;
+  return d;
+}
+
+// This wave's kWDmas DMAs of stage J (K steps 2J and 2J + 1; a step past K reads zeros).
+__device__ __forceinline__ void pw_issue(uint32_t st, const PwGeo& d, int J) {
+  const int w = d.wave, l = d.lane;
+  const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
+  const uint32_t half_row = (uint32_t)d.K / 2u;              // bytes of a weight row
+  const uint32_t ka = 128u * J + chunk;                      // weight bytes: 2 K steps per row
+  const int steps = d.K / 128;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(d.wr, st + kWStA + (2 * w + i) * kWTileSw + h * (1024 + 128),
+            (d.a_row[i][h] == kOobPf || ka >= half_row) ? kOobPf : d.a_row[i][h] + ka);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(d.xr, st + kWStB + (8 * s + w) * kWTileSw + h * (1024 + 128),
+            (d.b_row[h] == kOobPf || 2 * J + s >= steps) ? kOobPf : d.b_row[h] + 128u * (2 * J + s) + chunk);
+  {
+    const int s = w >> 2;
+    dma4(d.sr, st + kWStSA + s * 1024 + (w & 3) * 256,
+         (d.sa_row == kOobPf || 2 * J + s >= steps) ? kOobPf : d.sa_row + 4u * (2 * J + s));
+  }
+  if (l < 32) {
+    const int s = l >> 4;
+    dma4(d.xsr, st + kWStSB + w * 128,
+         (d.sb_row == kOobPf || 2 * J + s >= steps) ? kOobPf : d.sb_row + 4u * (2 * J + s));
+  }
+}
+
+// K step s of a stage for one wave: 8 weight tiles x 2 token tiles of MFMAs.
+__device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, int wn, int wm, int lane,
+                                           f32x4 acc[8][2]) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
+  uint4 blo[2], bhi[2];
+  uint32_t sb[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tile = 2 * wm + tt;
+    const uint8_t* row = st + kWStB + (8 * s + tile) * kWTileSw + rowoff;
+    blo[tt] = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
+    bhi[tt] = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ rr));
+    sb[tt] = st[kWStSB + tile * 128 + s * 64 + r * 4 + g];
+  }
+  uint4 av[8];
+  uint32_t sa[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tile = fc1 ? (i < 4 ? 4 * wn + i : 8 + 4 * wn + (i - 4)) : 8 * wn + i;
+    av[i] = *reinterpret_cast<const uint4*>(st + kWStA + tile * kWTileSw + rowoff + 16 * ((4 * s + g) ^ rr));
+    sa[i] = st[kWStSA + s * 1024 + (16 * tile + r) * 4 + g];
+  }
+  uint32_t bf[2][8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
+    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 22, 0);   // the step's LDS reads first
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then its MFMAs
+}
+
+// Item -> expert, n-tile and pair range (128-row routing tiles, exact ranges
+// from the router's table); items ordered expert-major, m-tiles fastest.
+__device__ __forceinline__ PfItem pw_item(const GemmArgs& a, int it, int n_tiles) {
+  const cptr te = (cptr)a.tile_expert, mt = (cptr)a.mtiles, tr = (cptr)a.tile_rows;
+  PfItem x;
+  x.l = te[it / n_tiles];
+  const int m0 = mt[x.l], m_l = mt[x.l + 1] - m0;
+  const int rr = it - m0 * n_tiles;
+  x.nt = rr / m_l;
+  const int m = m0 + rr % m_l;
+  x.p0 = tr[2 * m];
+  x.p1 = tr[2 * m + 1];
+  return x;
+}
+
+}  // namespace
+
+template <bool FC1>
+__global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t st0[kWStage];
+  __shared__ __align__(16) uint8_t st1[kWStage];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int K = a.K, steps = K / 128, n_st = (steps + 1) / 2;
+  const int n_tiles = FC1 ? a.N / 128 : (a.N + kWRows - 1) / kWRows;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_tiles;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
+  const int chunk = (total + 7) / 8;
+  const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // Two stages per item: stage 0 is requested before the previous item's
+  // output stores (so its latency overlaps them), stage J + 1 while stage J
+  // is multiplied.
+  int it = i_begin + slot;
+  PfItem cur{0, 0, 0, 0};
+  PwGeo d{};
+  if (it < i_end) {
+    cur = pw_item(a, it, n_tiles);
+    d = pw_geo<FC1>(a, cur, pf_act_rows<FC1>(a, cur, wave_u, lane), wave, lane);
+    lds_barrier();
+    pw_issue(lds_addr_of(st0), d, 0);
+  }
+  for (; it < i_end; it += per_xcd_wgs) {
+    const int it_next = it + per_xcd_wgs;
+    PfItem nxt{0, 0, 0, 0};
+    PfRows trow2{-1, -1, -1};
+    if (it_next < i_end) {
+      nxt = pw_item(a, it_next, n_tiles);
+      trow2 = pf_act_rows<FC1>(a, nxt, wave_u, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int J0 = 0; J0 < n_st; J0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int J = J0 + u;
+        if (J < n_st) {
+          dma_barrier<0>();                                  // stage J has landed everywhere
+          if (J + 1 < n_st) pw_issue(lds_addr_of(u ? st0 : st1), d, J + 1);
+          const uint8_t* stc = u ? st1 : st0;
+          pw_compute(stc, 0, FC1, wn, wm, lane, acc);
+          if (2 * J + 1 < steps) pw_compute(stc, 1, FC1, wn, wm, lane, acc);
+        }
+      }
+    }
+
+    // every wave is done with the stages: request the next item's first one
+    lds_barrier();
+    if (it_next < i_end) {
+      d = pw_geo<FC1>(a, nxt, trow2, wave, lane);
+      pw_issue(lds_addr_of(st0), d, 0);
+    }
+    // the second stage is free for FC2's output transpose
+    pf_epilogue<FC1, kWTok>(a, cur, acc, wn, wm, wave, lane, st1 + wave * 4352);
+    cur = nxt;
+  }
+}
+
+template <bool FC1>
+hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
+  const int n_tiles = FC1 ? a.N / 128 : (a.N + kWRows - 1) / kWRows;
+  const int64_t work = (int64_t)max_mtiles * n_tiles;
+  int64_t grid = cus;                                        // one workgroup per CU
+  if (grid > work) grid = (work + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_wide_kernel<FC1>, dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_prefill_wide<true>(const GemmArgs&, int, int, hipStream_t);
+template hipError_t launch_prefill_wide<false>(const GemmArgs&, int, int, hipStream_t);
 
 template <bool FC1>
 hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {

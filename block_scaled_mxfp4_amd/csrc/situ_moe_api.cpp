@@ -42,6 +42,7 @@ situ_status fail(situ_status st, const char* fmt, ...) {
 
 constexpr uint64_t kAlign = 256;
 constexpr int64_t kRouteSingleMax = 32768;   // pairs routed by a single workgroup
+constexpr double kWideRowsPerExpert = 192.0; // mean group size above which 128-row m-tiles come first
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct TacticInfo {
@@ -57,10 +58,12 @@ const TacticInfo kTactics[] = {
     {situ::FC1_W4A16_M64, "fc1_w4a16_bf16mfma_m64", SITU_ACT_W4A16, 64, true},
     {situ::FC1_W4A8_M16, "fc1_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, true},
     {situ::FC1_W4A8_M64, "fc1_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, true},
+    {situ::FC1_W4A8_M128, "fc1_w4a8_scalemfma_m128", SITU_ACT_W4A8, 128, true},
     {situ::FC2_W4A16_M16, "fc2_w4a16_bf16mfma_m16", SITU_ACT_W4A16, 16, false},
     {situ::FC2_W4A16_M64, "fc2_w4a16_bf16mfma_m64", SITU_ACT_W4A16, 64, false},
     {situ::FC2_W4A8_M16, "fc2_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, false},
     {situ::FC2_W4A8_M64, "fc2_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, false},
+    {situ::FC2_W4A8_M128, "fc2_w4a8_scalemfma_m128", SITU_ACT_W4A8, 128, false},
 };
 
 const TacticInfo* find_tactic(int32_t id) {
@@ -107,18 +110,30 @@ situ_status validate(const situ_moe_problem* p) {
 }
 
 // Valid (fc1, fc2) pairs, first-valid first: small groups (decode) take
-// 16-row m-tiles, large groups (prefill) 64-row m-tiles.
+// 16-row m-tiles, large groups (prefill) 64-row m-tiles, and in w4a8 very
+// large groups 128-row m-tiles (the wide kernel: K and the intermediate size
+// multiples of 128, h addressable with 32-bit offsets).
 int valid_pairs(const situ_moe_problem* p, int32_t* fc1, int32_t* fc2, int cap) {
   const bool w4a8 = p->act_mode == SITU_ACT_W4A8;
   const int32_t m16[2] = {w4a8 ? situ::FC1_W4A8_M16 : situ::FC1_W4A16_M16,
                           w4a8 ? situ::FC2_W4A8_M16 : situ::FC2_W4A16_M16};
   const int32_t m64[2] = {w4a8 ? situ::FC1_W4A8_M64 : situ::FC1_W4A16_M64,
                           w4a8 ? situ::FC2_W4A8_M64 : situ::FC2_W4A16_M64};
-  const double rows_per_expert = (double)p->num_tokens * p->top_k / p->local_num_experts;
-  const int32_t* order[2] = {m16, m64};
-  if (rows_per_expert > 48.0) { order[0] = m64; order[1] = m16; }
+  const int32_t m128[2] = {situ::FC1_W4A8_M128, situ::FC2_W4A8_M128};
+  const int64_t TK = (int64_t)p->num_tokens * p->top_k;
+  const int64_t mt128 = (TK + 127) / 128 + p->local_num_experts;
+  const bool wide = w4a8 && p->hidden_size % 128 == 0 && p->intermediate_size % 128 == 0 &&
+                    mt128 * 128 * p->intermediate_size < ((int64_t)1 << 31);
+  const double rows_per_expert = (double)TK / p->local_num_experts;
+  const int32_t* order[3] = {m16, m64, m128};
+  int n_order = wide ? 3 : 2;
+  if (wide && rows_per_expert > kWideRowsPerExpert) {
+    order[0] = m128; order[1] = m64; order[2] = m16;
+  } else if (rows_per_expert > 48.0) {
+    order[0] = m64; order[1] = m16;
+  }
   int n = 0;
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < n_order; ++i) {
     if (n < cap) { fc1[n] = order[i][0]; fc2[n] = order[i][1]; }
     ++n;
   }

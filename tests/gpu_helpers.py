@@ -124,34 +124,49 @@ def _mxfp8_ambiguity(v):
     return d
 
 
-def rounding_allowance(inp, spec, ref, mode):
-    """Per-output-element bound of how far a correct result may differ from
-    the oracle's because of the rounding point after FC1 alone (see
-    AMBIGUITY).  ref must come from oracle_out(..., keep=True).  Zero for
-    almost every element."""
+def _pair_effects(inp, spec, ref, mode):
+    """{pair index: bound of the change of that pair's FC2 output y} for the
+    pairs whose h holds an element on a rounding boundary (see AMBIGUITY)."""
     hpre = ref["h_pre"]
     d = _bf16_ambiguity(hpre) if mode == "w4a16" else _mxfp8_ambiguity(hpre)
-    tokens = ref["tokens"]
-    A = np.zeros((tokens.shape[0], spec["H"]))
     rows = np.nonzero(d.any(axis=1))[0]
-    if rows.size == 0:
-        return A
     pairs = ref["pairs"]
     offsets = ref["offsets"]
-    ids, wts = M.topk_of(inp)
-    k = spec["k"]
-    inv = ref["inv"].reshape(-1, k)
     effect = {}
     for q in rows:
         p = int(pairs[q])
         l = int(np.searchsorted(offsets, p, side="right") - 1)
         W2 = np.abs(F.dequant_mxfp4(inp["w2"][l], inp["w2_scale"][l]))
         effect[p] = W2 @ d[q]
+    return effect
+
+
+def rounding_allowance(inp, spec, ref, mode):
+    """Per-output-element bound of how far a correct result may differ from
+    the oracle's because of the rounding point after FC1 alone (see
+    AMBIGUITY).  ref must come from oracle_out(..., keep=True).  Zero for
+    almost every element."""
+    effect = _pair_effects(inp, spec, ref, mode)
+    tokens = ref["tokens"]
+    A = np.zeros((tokens.shape[0], spec["H"]))
+    if not effect:
+        return A
+    ids, wts = M.topk_of(inp)
+    k = spec["k"]
+    inv = ref["inv"].reshape(-1, k)
     for i, t in enumerate(tokens):
         for s_ in range(k):
             p = int(inv[t, s_])
             if p in effect:
                 A[i] += abs(wts[t, s_]) * effect[p]
+    return A
+
+
+def y_rounding_allowance(inp, spec, ref, mode, n_pairs):
+    """The same bound for the per-pair FC2 outputs y (rows by pair index)."""
+    A = np.zeros((n_pairs, spec["H"]))
+    for p, e in _pair_effects(inp, spec, ref, mode).items():
+        A[p] = e
     return A
 
 

@@ -139,9 +139,15 @@ def test_plan_layout_and_tactics():
     assert B.situ_moe_plan(_prob()).route_blocks == 1
     big = B.situ_moe_plan(_prob(num_tokens=32768, local_num_experts=112, local_expert_offset=336))
     assert big.route_blocks == 128 and big.route_chunk == 4096
-    # decode shapes take 16-row m-tiles, prefill shapes 64-row ones
+    # decode shapes take 16-row m-tiles, prefill shapes 64-row ones, and
+    # w4a8 groups of more than 192 rows on average 128-row ones
     assert B.situ_moe_plan(_prob()).block_m == 16
-    assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a8")).block_m == 64
+    assert B.situ_moe_plan(_prob(num_tokens=4096, act_mode="w4a8")).block_m == 64
+    assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a16")).block_m == 64
+    assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a8")).block_m == 128
+    assert B.situ_moe_valid_tactics(_prob(num_tokens=16384, act_mode="w4a8"))[:2] == [(4, 20), (3, 19)]
+    # the 128-row kernel needs sizes that are multiples of 128
+    assert (4, 20) not in B.situ_moe_valid_tactics(_prob(num_tokens=16384, act_mode="w4a8", intermediate_size=416))
 
 
 def test_run_argument_errors_before_any_device_work():

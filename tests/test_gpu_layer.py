@@ -17,7 +17,8 @@ import synthetic as S
 from oracle import formats as F
 from oracle import moe as M
 
-from gpu_helpers import config_inputs, dev, oracle_out, parity, rounding_allowance, run_layer, ws_region
+from gpu_helpers import (config_inputs, dev, oracle_out, parity, rounding_allowance, run_layer, ws_region,
+                         y_rounding_allowance)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,13 @@ SMALL = {
     # K multiples of 128: the 64-row w4a8 tactic takes the LDS-tiled kernels
     "prefill_a": dict(T=600, H=512, I=256, E_g=8, E_l=6, off=1, k=4, seed=35, skew=True),
     "prefill_b": dict(T=300, H=384, I=128, E_g=5, E_l=5, off=0, k=3, seed=36, packed=True),
+    # several 128-row m-tiles per expert with ragged tails, K = 640 (an odd
+    # number of 128-wide K steps) and an output width that is not a multiple
+    # of the 256-row n-tile
+    "prefill_c": dict(T=700, H=640, I=384, E_g=6, E_l=4, off=1, k=3, seed=37, skew=True),
 }
+# shapes the 128-row w4a8 tactic accepts (hidden and intermediate sizes multiples of 128)
+WIDE_OK = [n for n, c in SMALL.items() if c["H"] % 128 == 0 and c["I"] % 128 == 0]
 
 
 # ------------------------------------------------------------------ routing
@@ -198,6 +205,18 @@ def test_layer_parity_small(name, mode, bm):
     assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
 
 
+@pytest.mark.parametrize("name", WIDE_OK)
+def test_layer_parity_small_w4a8_m128(name):
+    spec = S.spec_of(SMALL[name])
+    inp = S.generate(spec)
+    got, plan, ws, _ = run_layer(inp, spec, mode="w4a8", tactic=(4, 20))
+    assert plan.block_m == 128
+    ref = oracle_out(inp, spec, mode="w4a8", keep=True)
+    parity(got, ref["out"], f"{name} w4a8 m128", rounding_allowance(inp, spec, ref, "w4a8"))
+    none = np.all(ref["inv"].reshape(spec["T"], spec["k"]) < 0, axis=1)
+    assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged", "wide"])
 def test_w4a8_prequantized_equals_library_quantized(name):
     spec = S.spec_of(SMALL[name])
@@ -209,11 +228,12 @@ def test_w4a8_prequantized_equals_library_quantized(name):
     parity(a, ref["out"], f"{name} prequantized", rounding_allowance(inp, spec, ref, "w4a8"))
 
 
-@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
-def test_intermediate_h_matches_oracle(mode):
-    spec = S.spec_of(SMALL["wide"])
+@pytest.mark.parametrize("mode,name,tactic", [("w4a16", "wide", (-1, -1)), ("w4a8", "wide", (-1, -1)),
+                                               ("w4a8", "prefill_c", (3, 19)), ("w4a8", "prefill_c", (4, 20))])
+def test_intermediate_h_matches_oracle(mode, name, tactic):
+    spec = S.spec_of(SMALL[name])
     inp = S.generate(spec)
-    got, plan, ws, _ = run_layer(inp, spec, mode=mode)
+    got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tactic)
     ref = oracle_out(inp, spec, mode=mode, keep=True)
     P, I = int(ref["offsets"][-1]), spec["I"]
     if mode == "w4a16":
@@ -233,7 +253,7 @@ def test_intermediate_h_matches_oracle(mode):
     y = ws_region(plan, ws, "y", torch.float32, (P, spec["H"]))
     yr = np.zeros_like(y, dtype=np.float64)
     yr[ref["pairs"]] = ref["y"]
-    parity(y, yr, f"y {mode}")
+    parity(y, yr, f"y {mode}", y_rounding_allowance(inp, spec, ref, mode, P))
 
 
 def test_bf16_output_is_rne_of_fp32_output():
