@@ -59,8 +59,9 @@ class SituMoePlan(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64)] + \
                [(n, ctypes.c_uint64) for n in (
                    "off_counts", "off_offsets", "off_mtiles", "off_tile_expert", "off_perm", "off_inv",
-                   "off_xq", "off_xs", "off_h", "off_hs", "off_y", "off_route_hist", "off_tile_rows")] + \
-               [("reserved", ctypes.c_uint32 * 6)]
+                   "off_xq", "off_xs", "off_h", "off_hs", "off_y", "off_route_hist", "off_tile_rows",
+                   "off_y_exp")] + \
+               [("y_format", ctypes.c_int32), ("reserved", ctypes.c_uint32 * 3)]
 
 
 class SituMoeTensors(ctypes.Structure):
@@ -277,7 +278,7 @@ def new_workspace(plan, device=None):
 _REGIONS = {"counts": "off_counts", "offsets": "off_offsets", "mtiles": "off_mtiles",
             "tile_expert": "off_tile_expert", "perm": "off_perm", "inv": "off_inv", "xq": "off_xq",
             "xs": "off_xs", "h": "off_h", "hs": "off_hs", "y": "off_y", "route_hist": "off_route_hist",
-            "tile_rows": "off_tile_rows"}
+            "tile_rows": "off_tile_rows", "y_exp": "off_y_exp"}
 
 
 def workspace_view(plan, workspace, region, dtype, shape):

@@ -31,6 +31,7 @@
 // m-tiles and their experts come from the router's tile list on the device,
 // so no group size is ever read back to the host.
 #include "common.hpp"
+#include "dma.hpp"
 #include "internal.hpp"
 
 namespace situ {
@@ -39,23 +40,23 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_ca
 
 template <bool FP8, int TOKT>
 __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   const int I = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
   const int units = I / kFc1ColsPerWave;
   const int n_wgn = (units + 3) / 4;
-  const int total = a.mtiles[a.E_l] * n_wgn;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
   const int64_t xrow_bytes = FP8 ? (int64_t)K : (int64_t)K * 2;
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = w / n_wgn;
     const int unit = (w % n_wgn) * 4 + wave;
     if (unit >= units) continue;
-    const int l = a.tile_expert[mt];
-    const int p0 = a.offsets[l] + (mt - a.mtiles[l]) * (16 * TOKT);
-    const int p1 = min(a.offsets[l + 1], p0 + 16 * TOKT);
+    const int l = ((cptr)a.tile_expert)[mt];
+    const int p0 = ((cptr)a.offsets)[l] + (mt - ((cptr)a.mtiles)[l]) * (16 * TOKT);
+    const int p1 = min(((cptr)a.offsets)[l + 1], p0 + 16 * TOKT);
     const int n0 = unit * kFc1ColsPerWave;
 
     const uint8_t* xrow[TOKT];
@@ -197,23 +198,23 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
 
 template <bool FP8, int TOKT>
 __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   const int H = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
   const int wg_rows = 4 * kFc2RowsPerWave;
   const int n_wgn = (H + wg_rows - 1) / wg_rows;
-  const int total = a.mtiles[a.E_l] * n_wgn;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
   const int64_t hrow_bytes = FP8 ? (int64_t)K : (int64_t)K * 2;
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = w / n_wgn;
     const int n0 = (w % n_wgn) * wg_rows + wave * kFc2RowsPerWave;
     if (n0 >= H) continue;
-    const int l = a.tile_expert[mt];
-    const int p0 = a.offsets[l] + (mt - a.mtiles[l]) * (16 * TOKT);
-    const int p1 = min(a.offsets[l + 1], p0 + 16 * TOKT);
+    const int l = ((cptr)a.tile_expert)[mt];
+    const int p0 = ((cptr)a.offsets)[l] + (mt - ((cptr)a.mtiles)[l]) * (16 * TOKT);
+    const int p1 = min(((cptr)a.offsets)[l + 1], p0 + 16 * TOKT);
     const int ntiles = min(4, (H - n0) / 16);
 
     const uint8_t* hrow[TOKT];
@@ -358,7 +359,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // rows that exist, so the range check never depends on it.
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-  v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  // soff is wave-uniform by contract; readfirstlane keeps it in an SGPR (a
+  // value the compiler cannot prove uniform would make it loop over lanes)
+  v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, __builtin_amdgcn_readfirstlane((int)soff), 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -455,15 +458,18 @@ template <bool FP8, bool FC1, int KSPLIT>
 __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm_kernel(GemmArgs a) {
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
   extern __shared__ __align__(16) uint8_t lds[];
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform values are made visibly uniform (readfirstlane, scalar
+  // loads of the routing tables) so buffer resources stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
+  const cptr tile_expert = (cptr)a.tile_expert, offsets = (cptr)a.offsets, mtiles = (cptr)a.mtiles;
   const int r = lane & 15, g = lane >> 4;
   const int ks = wave % KSPLIT;
   const int uw = wave / KSPLIT;
   const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
   const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
   const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
-  const int total = a.mtiles[a.E_l] * n_wgn;
+  const int total = mtiles[a.E_l] * n_wgn;
   const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
   const int n_rows = FC1 ? 2 * a.N : a.N;          // weight rows per expert
   // contiguous K range of this wave
@@ -478,9 +484,9 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
     const int unit0 = (w % n_wgn) * UNITS_PER_WG;
     const int unit = unit0 + uw;
     const bool active = unit < units;  // uniform per wave; idle waves still meet the barriers
-    const int l = a.tile_expert[mt];
-    const int p0 = a.offsets[l] + (mt - a.mtiles[l]) * 16;
-    const int p1 = min(a.offsets[l + 1], p0 + 16);
+    const int l = tile_expert[mt];
+    const int p0 = offsets[l] + (mt - mtiles[l]) * 16;
+    const int p1 = min(offsets[l + 1], p0 + 16);
     const int p = p0 + r;
     const bool valid = p < p1;
 

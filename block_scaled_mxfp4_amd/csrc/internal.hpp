@@ -58,12 +58,15 @@ struct GemmArgs {
   const float* alpha_g;       // may be null
   const float* alpha_u;       // may be null
   // outputs
-  void* out;                  // FC1: h bf16 [P, I] or E4M3 [P, I]; FC2: y float [P, H]
-  uint8_t* out_scale;         // FC1 w4a8: E8M0 [P, I/32]
+  void* out;                  // FC1: h bf16 [P, I] or E4M3 [P, I]; FC2: y float [P, H] or fp16 [P, H]
+  uint8_t* out_scale;         // FC1 w4a8: E8M0 [P, I/32]; FC2: null (fp32 y) or y's exponents [ceil(H/64), out_rows]
+  int32_t out_rows;           // FC2 with fp16 y: rows of y (the exponent array's leading dimension)
 };
 
 struct CombineArgs {
-  const float* y;             // [P, H]
+  const float* y;             // [P, H] fp32, or null when y16 is given
+  const uint16_t* y16;        // [P, H] fp16 scaled per 64 columns by 2^(y_exp - 127), or null
+  const uint8_t* y_exp;       // [ceil(H/64), T*k]: column block major
   const int32_t* inv;         // [T*k]
   const uint16_t* weights;    // bf16 [T, k] or null
   const int32_t* packed;      // [T, k] or null

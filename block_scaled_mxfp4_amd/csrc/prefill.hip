@@ -248,6 +248,27 @@ __device__ __forceinline__ void st16(const v4i& r, uint32_t voff, f32x4 v) {
   asm volatile("s_nop 1\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
                : "memory");
 }
+// Max over each row of 16 lanes with DPP lane moves (no LDS round trips):
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float dpp_max(float m, int ctrl_id) {
+  const int b = __builtin_bit_cast(int, m);
+  int o;
+  switch (ctrl_id) {
+    case 0: o = __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false); break;    // quad_perm [1,0,3,2]
+    case 1: o = __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false); break;    // quad_perm [2,3,0,1]
+    case 2: o = __builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
+    default: o = __builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false); break;  // row_mirror
+  }
+  return fmaxf(m, __builtin_bit_cast(float, o));
+}
+__device__ __forceinline__ float row16_max(float m) {
+  return dpp_max(dpp_max(dpp_max(dpp_max(m, 0), 1), 2), 3);
+}
+__device__ __forceinline__ void st8(const v4i& r, uint32_t voff, uint32_t lo, uint32_t hi) {
+  const uint2 w = make_uint2(lo, hi);
+  asm volatile("s_nop 1\n\tbuffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
+               : "memory");
+}
 __device__ __forceinline__ void st4(const v4i& r, uint32_t voff, uint32_t v) {
   asm volatile("buffer_store_dword %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
 }
@@ -316,7 +337,16 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     // cache lines) instead of 16 tokens x 64 bytes.  scratch = 4352 bytes of
     // this wave's, in the stage the next item's first requests leave free.
     const int H = a.N;
-    const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
+    // fp16 y (out_scale = its exponents): each 64-column row segment, held
+    // by 16 lanes, takes the power-of-two scale that puts its largest
+    // magnitude in [2^14, 2^15); exponent byte E means a scale of 2^(E-127)
+    const bool y16 = a.out_scale != nullptr;
+    const int nb64 = (H + 63) / 64;
+    const v4i yr = y16 ? rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 2))
+                       : rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
+    // exponents column-block major: one block's bytes of consecutive rows are
+    // contiguous, so an item writes whole lines of them
+    const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
     constexpr int kRowPitch = 64 * 4 + 16;          // padded: the tile writes hit 16 distinct bank groups
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -333,7 +363,23 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
           const f32x4 v = *reinterpret_cast<const f32x4*>(scratch + t * kRowPitch + 16 * chunk);
           const int pr = 32 * wm + 16 * tt + t;
           const bool ok = x.p0 + pr < x.p1 && col < H;
-          st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
+          if (!y16) {
+            st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
+          } else {
+            // columns past H hold zeros (their weight rows read as zero)
+            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            m = row16_max(m);
+            const int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 127;   // floor(log2 m)
+            const int E = min(max(e + 113, 1), 254);
+            const float inv = __builtin_bit_cast(float, (uint32_t)(254 - E) << 23);     // 2^(127 - E)
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(v[0] * inv));
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(v[1] * inv));
+            const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(v[2] * inv));
+            const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(v[3] * inv));
+            st8(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, h0 | (h1 << 16), h2 | (h3 << 16));
+            st1(er, (ok && chunk == 0) ? (uint32_t)(col / 64) * (uint32_t)a.out_rows + (uint32_t)(x.p0 + pr) : kOobPf,
+                (uint32_t)E);
+          }
         }
       }
   }

@@ -278,7 +278,16 @@ situ_status situ_moe_plan(const situ_moe_problem* problem, situ_moe_plan_t* plan
   plan->off_xs = region(quant_here ? T * H / 32 : 0);
   plan->off_h = region(TK * I * (w4a8 ? 1 : 2));
   plan->off_hs = region(w4a8 ? TK * I / 32 : 0);
-  plan->off_y = region(TK * H * 4);
+  // y: fp32, or (the 128-row w4a8 tactic) fp16 with a power-of-two scale per
+  // 64 columns, which halves its write and read traffic
+  plan->y_format = plan->fc2_tactic == situ::FC2_W4A8_M128 ? 1 : 0;
+  if (plan->y_format == 1) {
+    plan->off_y = region(align_up(TK * H * 2) + TK * ((H + 63) / 64));
+    plan->off_y_exp = plan->off_y + align_up(TK * H * 2);
+  } else {
+    plan->off_y = region(TK * H * 4);
+    plan->off_y_exp = plan->off_y;
+  }
   // routing: one workgroup for small batches, else blocks of >= 4096 pairs (<= 1024 blocks)
   if (TK <= kRouteSingleMax) {
     plan->route_blocks = 1;
@@ -388,12 +397,16 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.K = (int32_t)I;
   g.N = (int32_t)H;
   g.out = at<void>(ws, plan->off_y);
-  g.out_scale = nullptr;
+  g.out_scale = plan->y_format == 1 ? at<uint8_t>(ws, plan->off_y_exp) : nullptr;
+  g.out_rows = (int32_t)((int64_t)T * p.top_k);
   if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, plan->max_mtiles, cus, s), "fc2")) != SITU_OK) return st;
   if ((st = mark(4)) != SITU_OK) return st;
 
   // combine
-  situ::CombineArgs c{at<float>(ws, plan->off_y), ra.inv, p.topk_packed ? nullptr : t->topk_weights,
+  const bool y16 = plan->y_format == 1;
+  situ::CombineArgs c{y16 ? nullptr : at<float>(ws, plan->off_y), y16 ? at<uint16_t>(ws, plan->off_y) : nullptr,
+                      y16 ? at<uint8_t>(ws, plan->off_y_exp) : nullptr, ra.inv,
+                      p.topk_packed ? nullptr : t->topk_weights,
                       p.topk_packed ? t->topk_packed : nullptr, t->out, T, (int32_t)H, p.top_k,
                       p.out_dtype == SITU_OUT_BF16 ? 1 : 0};
   if ((st = launch_status(situ::launch_combine(c, s), "combine")) != SITU_OK) return st;

@@ -105,10 +105,14 @@ typedef struct situ_moe_plan_t {
   uint64_t off_xs;              /* uint8 [T, H/32]  their E8M0 scales */
   uint64_t off_h;               /* FC1 output rows in perm order: bf16 [T*k, I] (w4a16) or E4M3 [T*k, I] (w4a8) */
   uint64_t off_hs;              /* uint8 [T*k, I/32] E8M0 scales of h (w4a8) */
-  uint64_t off_y;               /* float [T*k, H]   FC2 output rows in perm order */
+  uint64_t off_y;               /* FC2 output rows in perm order: float [T*k, H] (y_format 0), or
+                                   fp16 [T*k, H] scaled by 2^(y_exp - 127) per 64 columns (y_format 1) */
   uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms (route_blocks > 1) */
   uint64_t off_tile_rows;       /* int32 [max_mtiles, 2] first and one-past-last perm position of each m-tile */
-  uint32_t reserved[6];
+  uint64_t off_y_exp;           /* uint8 [ceil(H/64), T*k] block exponents of y (y_format 1), column block major,
+                                   inside the y region */
+  int32_t y_format;             /* 0: fp32 y; 1: fp16 y with an exponent per 64 columns (the 128-row w4a8 tactic) */
+  uint32_t reserved[3];
 } situ_moe_plan_t;
 
 /* Device tensors of one call.  Shapes use T, H, I, k, E_l of the problem. */

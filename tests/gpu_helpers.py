@@ -198,3 +198,17 @@ def parity(got, want, what="", allowance=None):
 
 def ws_region(plan, ws, name, dtype, shape):
     return B.workspace_view(plan, ws, name, dtype, shape).cpu().numpy()
+
+
+def read_y(plan, ws, P, H):
+    """The FC2 output rows y [P, H] as float64, decoded from the plan's y
+    format: fp32, or fp16 with exponent byte E (scale 2^(E-127)) per 64
+    columns."""
+    if plan.y_format == 0:
+        return ws_region(plan, ws, "y", torch.float32, (P, H)).astype(np.float64)
+    nb = (H + 63) // 64
+    y16 = ws_region(plan, ws, "y", torch.float16, (P, H)).astype(np.float64)
+    rows = plan.prob.num_tokens * plan.prob.top_k
+    e = ws_region(plan, ws, "y_exp", torch.uint8, (nb, rows))[:, :P].T.astype(np.int64)
+    assert np.all((e >= 1) & (e <= 254))
+    return y16 * np.ldexp(1.0, np.repeat(e, 64, axis=1)[:, :H] - 127)

@@ -126,7 +126,7 @@ def test_plan_layout_and_tactics():
                  "off_tile_expert": 4 * plan.max_mtiles, "off_perm": 4 * (T * k + 64), "off_inv": 4 * T * k,
                  "off_xq": T * H if w4a8 else 0, "off_xs": T * H // 32 if w4a8 else 0,
                  "off_h": T * k * I * (1 if w4a8 else 2), "off_hs": T * k * I // 32 if w4a8 else 0,
-                 "off_y": 4 * T * k * H,
+                 "off_y": (-(-2 * T * k * H // 256) * 256 + T * k * -(-H // 64)) if plan.y_format else 4 * T * k * H,
                  "off_route_hist": 4 * plan.route_blocks * E if plan.route_blocks > 1 else 0,
                  "off_tile_rows": 8 * plan.max_mtiles}
         spans = sorted((getattr(plan, n), getattr(plan, n) + s) for n, s in sizes.items())
@@ -135,6 +135,10 @@ def test_plan_layout_and_tactics():
         assert all(getattr(plan, n) % 256 == 0 for n in sizes)
         assert spans[-1][1] <= plan.workspace_bytes
         assert plan.max_mtiles >= (T * k + plan.block_m - 1) // plan.block_m
+        # compact y (fp16 + one exponent byte per 64 columns) only with the 128-row tactic
+        assert plan.y_format == (1 if plan.fc2_tactic == 20 else 0)
+        if plan.y_format:
+            assert plan.off_y_exp == plan.off_y + -(-2 * T * k * H // 256) * 256
     # decode batches are routed by one workgroup, prefill batches by blocks
     assert B.situ_moe_plan(_prob()).route_blocks == 1
     big = B.situ_moe_plan(_prob(num_tokens=32768, local_num_experts=112, local_expert_offset=336))

@@ -17,7 +17,7 @@ import synthetic as S
 from oracle import formats as F
 from oracle import moe as M
 
-from gpu_helpers import (config_inputs, dev, oracle_out, parity, rounding_allowance, run_layer, ws_region,
+from gpu_helpers import (config_inputs, dev, oracle_out, parity, read_y, rounding_allowance, run_layer, ws_region,
                          y_rounding_allowance)
 
 pytestmark = pytest.mark.gpu
@@ -250,7 +250,7 @@ def test_intermediate_h_matches_oracle(mode, name, tactic):
     rel = np.abs(hg - hr) / np.maximum(np.abs(hr), 1e-3 * np.sqrt(np.mean(hr ** 2)))
     assert np.mean(rel <= 1e-6) > 0.97, np.mean(rel <= 1e-6)
     assert np.max(rel) <= step * 1.01 + 1e-6
-    y = ws_region(plan, ws, "y", torch.float32, (P, spec["H"]))
+    y = read_y(plan, ws, P, spec["H"])
     yr = np.zeros_like(y, dtype=np.float64)
     yr[ref["pairs"]] = ref["y"]
     parity(y, yr, f"y {mode}", y_rounding_allowance(inp, spec, ref, mode, P))
