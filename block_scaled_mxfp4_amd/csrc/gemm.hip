@@ -454,6 +454,69 @@ __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb) {
   return decode_lds_scales(4 / ksplit, nkb) + (ksplit > 1 ? 4u * 4u * kWave * 16u : 0u);
 }
 
+// Decode epilogue of one wave's 16-row group: FC1 applies alpha and SiTU and
+// rounds h (bf16, or MXFP8 with one E8M0 scale per 32 columns); FC2 writes
+// fp32 y.  acc[q] holds weight tile q x the group's 16 tokens; this lane owns
+// token p (valid: inside the group) and rows 4g..4g+3 of each tile.
+// Per-expert parameters come through scalar loads.
+template <bool FP8, bool FC1>
+__device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 acc[4], int l, int p, bool valid,
+                                                int n0, int g, int ntiles) {
+  if constexpr (FC1) {
+    const int I = a.N;
+    const float ag = a.alpha_g ? __builtin_bit_cast(float, ((cptr)a.alpha_g)[l]) : 1.0f;
+    const float au = a.alpha_u ? __builtin_bit_cast(float, ((cptr)a.alpha_u)[l]) : 1.0f;
+    const float bb = __builtin_bit_cast(float, ((cptr)a.beta)[l]);
+    const float lb = __builtin_bit_cast(float, ((cptr)a.lbeta)[l]);
+    const float rb = 1.0f / bb, rlb = 1.0f / lb;
+    float hv[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, rb, rlb);
+    if constexpr (!FP8) {
+      if (valid) {
+        uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(hv[half][2]) | (f32_to_bf16_rne(hv[half][3]) << 16);
+          *reinterpret_cast<uint2*>(hrow + 16 * half) = make_uint2(lo, hi);
+        }
+      }
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(hv[half][i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      if (valid) {
+        const uint32_t code = e8m0_code_for_e4m3(amax);
+        const int sh = 127 - (int)code;
+        uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__builtin_ldexpf(hv[half][i], sh)) << (8 * i);
+          *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
+        }
+        if (g == 0) a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
+      }
+    }
+  } else {
+    if (valid) {
+      float* yrow = static_cast<float*>(a.out) + (int64_t)p * a.N + n0 + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < ntiles) *reinterpret_cast<f32x4*>(yrow + 16 * q) = acc[q];
+    }
+  }
+}
+
 template <bool FP8, bool FC1, int KSPLIT>
 __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm_kernel(GemmArgs a) {
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
@@ -593,60 +656,7 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
       }
     }
 
-    if (lead) {
-      if constexpr (FC1) {
-        const int I = a.N;
-        const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
-        const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
-        const float bb = a.beta[l], lb = a.lbeta[l];
-        const float rb = 1.0f / bb, rlb = 1.0f / lb;
-        float hv[2][4];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, rb, rlb);
-        if constexpr (!FP8) {
-          if (valid) {
-            uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
-              const uint32_t hi = f32_to_bf16_rne(hv[half][2]) | (f32_to_bf16_rne(hv[half][3]) << 16);
-              *reinterpret_cast<uint2*>(hrow + 16 * half) = make_uint2(lo, hi);
-            }
-          }
-        } else {
-          float amax = 0.0f;
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(hv[half][i]));
-          amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-          amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-          if (valid) {
-            const uint32_t code = e8m0_code_for_e4m3(amax);
-            const int sh = 127 - (int)code;
-            uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              uint32_t packed = 0;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__builtin_ldexpf(hv[half][i], sh)) << (8 * i);
-              *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
-            }
-            if (g == 0) a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
-          }
-        }
-      } else {
-        if (valid) {
-          float* yrow = static_cast<float*>(a.out) + (int64_t)p * a.N + n0 + 4 * g;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (q < ntiles) *reinterpret_cast<f32x4*>(yrow + 16 * q) = acc[q];
-        }
-      }
-    }
+    if (lead) decode_epilogue<FP8, FC1>(a, acc, l, p, valid, n0, g, ntiles);
     __syncthreads();   // staged scales and partial sums are reused by the next work item
   }
 }

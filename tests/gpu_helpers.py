@@ -78,42 +78,96 @@ def oracle_out(inp, spec, mode=None, tokens=None, prequantized=False, keep=False
 
 
 # Relative distance to a rounding midpoint below which either rounding of an
-# element of h is a correct result: the GPU computes h in fp32 within a few
-# ulp (~1e-7) of the oracle's correctly rounded value, so 2^-16 leaves a wide
-# margin while excusing only elements that sit on a rounding boundary.
+# element of h is a correct result, for the SiTU evaluation alone: the GPU
+# evaluates SiTU in fp32 within a few ulp (~1e-7), so 2^-16 leaves a wide
+# margin.
 AMBIGUITY = 2.0 ** -16
 
 
-def _bf16_ambiguity(v):
-    """Size of the other bf16 rounding choice of v where v is within
-    AMBIGUITY of a bf16 rounding midpoint, else 0."""
+def acc_error_ulps(K):
+    """Bound, in fp32 ulps of sum_k |x_k w_k|, of how far an FC1 output the
+    GPU accumulates (exact block products summed in fp32, in an order other
+    than the oracle's float64 sum) may lie from the oracle's: a fixed part
+    for the sums inside the matrix-core instructions plus one ulp per 64
+    products.  Measured on the device at K = 640: flips that needed up to
+    10 ulp on elements whose flip matters (one tiny element of a block
+    needed 23)."""
+    return 8 + K / 64
+
+
+def h_uncertainty(inp, spec, ref, mode):
+    """Per element of ref["h_pre"], a bound of |GPU h - oracle h| before the
+    rounding point: the FC1 accumulation bound (acc_error_ulps times
+    sum_k |x_k w_k| on the gate and up sums, propagated through alpha and
+    SiTU by evaluating SiTU at the perturbed inputs) plus the SiTU
+    evaluation error (AMBIGUITY relative)."""
+    I, H = spec["I"], spec["H"]
+    eps = acc_error_ulps(H) * 2.0 ** -24
+    xf = M.activations(inp, mode, False)[0]
+    pairs, offsets, perm = ref["pairs"], ref["offsets"], ref["perm"]
+    k = spec["k"]
+    acc = ref["acc"]
+    hpre = ref["h_pre"]
+    out = np.zeros_like(hpre)
+    E_l = spec["E_l"]
+    ones = np.ones(E_l, np.float32)
+    a_g = ones if inp.get("alpha_gate") is None else np.asarray(inp["alpha_gate"], np.float64)
+    a_u = ones if inp.get("alpha_up") is None else np.asarray(inp["alpha_up"], np.float64)
+    beta = np.asarray(inp["situ_beta"], np.float64)
+    lbeta = np.asarray(inp["situ_linear_beta"], np.float64)
+    for l in range(E_l):
+        q = np.nonzero((pairs >= offsets[l]) & (pairs < offsets[l + 1]))[0]
+        if q.size == 0:
+            continue
+        W = np.abs(F.dequant_mxfp4(inp["w1"][l], inp["w1_scale"][l]))
+        S = np.abs(xf[perm[pairs[q]] // k]) @ W.T               # [n, 2I] sums of |x w|
+        g = a_g[l] * acc[q, :I]
+        u = a_u[l] * acc[q, I:]
+        dg = a_g[l] * eps * S[:, :I]
+        du = a_u[l] * eps * S[:, I:]
+        h0 = M.situ(g, u, beta[l], lbeta[l])
+        d = np.zeros_like(h0)
+        for sg, su in ((1, 0), (-1, 0), (0, 1), (0, -1)):
+            d = np.maximum(d, np.abs(M.situ(g + sg * dg, u + su * du, beta[l], lbeta[l]) - h0))
+        out[q] = 1.5 * d + AMBIGUITY * np.abs(hpre[q])
+    return out
+
+
+def _bf16_ambiguity(v, tol=None):
+    """Size of the other bf16 rounding choice of v where v lies within tol
+    (default AMBIGUITY * |v|) of a bf16 rounding midpoint, else 0."""
     v = np.asarray(v, np.float64)
     q = F.bf16_to_f64(F.f32_to_bf16_rne(v.astype(np.float32)))
     a = np.abs(v)
+    tol = AMBIGUITY * a if tol is None else tol
     ulp = np.ldexp(1.0, F.floor_log2(np.where(a > 0, a, 1.0)) - 7)
-    amb = (a > 0) & (ulp / 2 - np.abs(v - q) <= AMBIGUITY * a)
+    amb = (a > 0) & (ulp / 2 - np.abs(v - q) <= tol)
     return np.where(amb, ulp, 0.0)
 
 
-def _mxfp8_ambiguity(v):
+def _mxfp8_ambiguity(v, tol=None):
     """The same for MXFP8 rows (32-element blocks along the last axis): an
-    element near an E4M3 rounding midpoint under its block scale, or a whole
-    block whose max is within AMBIGUITY of a power of two (two candidate
-    E8M0 scales), may round either way."""
+    element within tol of an E4M3 rounding midpoint under its block scale, or
+    a whole block whose max lies within its tol of a power of two (two
+    candidate E8M0 scales), may round either way."""
     v = np.asarray(v, np.float64)
     n, I = v.shape
+    tol = AMBIGUITY * np.abs(v) if tol is None else np.asarray(tol, np.float64)
     codes, sc = F.mx_quantize(v, "e4m3")
     q = F.mx_dequantize(codes, sc, "e4m3")
     scale = np.repeat(F.decode_e8m0(sc), 32, axis=-1)
     s = v / scale
     a = np.abs(s)
     spacing = np.where(a < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, F.floor_log2(np.where(a > 0, a, 1.0)) - 3))
-    amb = (a > 0) & (a < 448.0) & (spacing / 2 - np.abs(s - q / scale) <= AMBIGUITY * a)
+    amb = (a > 0) & (a < 448.0) & (spacing / 2 - np.abs(s - q / scale) <= tol / scale)
     d = np.where(amb, spacing * scale, 0.0)
-    # block scale ambiguity
-    blocks = np.abs(v).reshape(n, I // 32, 32).max(-1)
-    m = blocks / np.ldexp(1.0, F.floor_log2(np.where(blocks > 0, blocks, 1.0)))
-    near = (blocks > 0) & ((m - 1.0 <= AMBIGUITY) | (2.0 - m <= 2 * AMBIGUITY))
+    # block scale ambiguity: the block max within its element's tol of a power of two
+    av = np.abs(v).reshape(n, I // 32, 32)
+    arg = av.argmax(-1)
+    blocks = np.take_along_axis(av, arg[..., None], -1)[..., 0]
+    btol = np.take_along_axis(tol.reshape(n, I // 32, 32), arg[..., None], -1)[..., 0]
+    p2 = np.ldexp(1.0, F.floor_log2(np.where(blocks > 0, blocks, 1.0)))
+    near = (blocks > 0) & ((blocks - p2 <= btol) | (2 * p2 - blocks <= btol))
     if near.any():
         for sgn in (-1, 1):
             alt_sc = np.clip(sc.astype(np.int64) + sgn, 0, 254).astype(np.uint8)
@@ -128,7 +182,8 @@ def _pair_effects(inp, spec, ref, mode):
     """{pair index: bound of the change of that pair's FC2 output y} for the
     pairs whose h holds an element on a rounding boundary (see AMBIGUITY)."""
     hpre = ref["h_pre"]
-    d = _bf16_ambiguity(hpre) if mode == "w4a16" else _mxfp8_ambiguity(hpre)
+    tol = h_uncertainty(inp, spec, ref, mode)
+    d = _bf16_ambiguity(hpre, tol) if mode == "w4a16" else _mxfp8_ambiguity(hpre, tol)
     rows = np.nonzero(d.any(axis=1))[0]
     pairs = ref["pairs"]
     offsets = ref["offsets"]

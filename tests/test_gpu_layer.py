@@ -42,6 +42,12 @@ SMALL = {
     # number of 128-wide K steps) and an output width that is not a multiple
     # of the 256-row n-tile
     "prefill_c": dict(T=700, H=640, I=384, E_g=6, E_l=4, off=1, k=3, seed=37, skew=True),
+    # an output width of 160: FC2's last 64-row unit holds 2 of 4 tiles
+    "decode_tail": dict(T=40, H=160, I=256, E_g=10, E_l=7, off=2, k=4, seed=38),
+    # many 16-row m-tiles per expert (skewed) with K = 640 and 512: more work
+    # items than workgroups, and FC1 outputs where the gate or up sum
+    # cancels, so the FC1 accumulation order decides some rounding points
+    "decode_many": dict(T=600, H=640, I=512, E_g=8, E_l=8, off=0, k=4, seed=39, skew=True),
 }
 # shapes the 128-row w4a8 tactic accepts (hidden and intermediate sizes multiples of 128)
 WIDE_OK = [n for n, c in SMALL.items() if c["H"] % 128 == 0 and c["I"] % 128 == 0]
