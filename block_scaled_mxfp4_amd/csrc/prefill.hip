@@ -317,12 +317,18 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
         const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
         const uint32_t code = e8m0_code_for_e4m3(amax);
         const int sh = 127 - (int)code;
+        // E4M3 codes by the hardware conversion (round to nearest even) of
+        // the scaled values clamped to +-448, which gives the MX rule's
+        // saturating codes; a negative value that rounds to zero keeps its
+        // sign (code 0x80, the value zero)
         uint32_t packed[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          packed[h2] = 0;
+          float sv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) packed[h2] |= e4m3_encode(__builtin_ldexpf(hv[h2][e], sh)) << (8 * e);
+          for (int e = 0; e < 4; ++e) sv[e] = fminf(fmaxf(__builtin_ldexpf(hv[h2][e], sh), -448.0f), 448.0f);
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sv[0], sv[1], 0, false);
+          packed[h2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv[2], sv[3], lo, true);
         }
         const uint32_t ho = valid ? (uint32_t)(pr * I + col0 + 4 * g) : kOobPf;
         st4(hr, ho, packed[0]);
