@@ -6,11 +6,12 @@
 // test_kimi_k3_situ_moe.py, pull request 17865).  A token with no local slot
 // gets an exact zero row ("TokenSpeed SiTU", "Supported contract": the
 // output is a partial sum the caller all-reduces, so nothing is
-// renormalized).  A workgroup covers 512 columns of one token, four per lane;
-// slot rows are fetched eight at a time and summed in slot order.  y is fp32,
-// or fp16 with a power-of-two scale 2^(E-127) per 64 columns (decoded
-// exactly to fp32 here).
+// renormalized).  A workgroup covers 512 columns of one token (fp32 y: four
+// per lane of two waves; fp16 y: eight per lane of one wave); slot rows are
+// fetched eight at a time and summed in slot order.  fp16 y carries a
+// power-of-two scale 2^(E-127) per 64 columns, decoded exactly to fp32 here.
 #include "common.hpp"
+#include "dma.hpp"
 #include "internal.hpp"
 
 namespace situ {
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     const int64_t t = it / nblk;
     const int c = (int)(it % nblk) * kCombineCols + threadIdx.x * 4;
     if (c >= a.H) continue;
-    const int32_t* inv = a.inv + t * a.k;
+    const cptr inv = (cptr)(a.inv + t * a.k);          // the token's slots: scalar loads
+    const cptr pk = (cptr)(a.packed ? a.packed + t * a.k : a.inv);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < a.k; s0 += kSlotBatch) {
       int pos[kSlotBatch];
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
       for (int u = 0; u < kSlotBatch; ++u) {
         const int s = s0 + u;
         pos[u] = s < a.k ? inv[s] : -1;
-        const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)a.packed[t * a.k + s] >> 16) : a.weights[t * a.k + s]) : 0u;
+        const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
         wgt[u] = bf16_to_f32(wb);
       }
       if constexpr (Y16) {
@@ -83,12 +85,77 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   }
 }
 
+// fp16 y: one wave per 512 columns of a token, eight columns (16 bytes of y)
+// per lane; the token's slot positions and weights come through scalar loads.
+constexpr int kY16Cols = 512;
+
+__global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
+  const int nblk = (a.H + kY16Cols - 1) / kY16Cols;
+  const int64_t items = a.T * nblk;
+  const int64_t rows = a.T * a.k;
+  const int lane = threadIdx.x;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t t = it / nblk;
+    const int c = (int)(it % nblk) * kY16Cols + lane * 8;
+    const cptr inv = (cptr)(a.inv + t * a.k);
+    const cptr pk = (cptr)(a.packed ? a.packed + t * a.k : a.inv);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.k; s0 += kSlotBatch) {
+      int pos[kSlotBatch];
+      float wgt[kSlotBatch];
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u) {
+        const int s = s0 + u;
+        pos[u] = s < a.k ? inv[s] : -1;
+        const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
+        wgt[u] = bf16_to_f32(wb);
+      }
+      uint4 hv[kSlotBatch];
+      uint32_t ev[kSlotBatch];
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u)
+        if (pos[u] >= 0 && c < a.H) {
+          hv[u] = *reinterpret_cast<const uint4*>(a.y16 + (int64_t)pos[u] * a.H + c);
+          ev[u] = a.y_exp[(int64_t)(c / 64) * rows + pos[u]];
+        }
+#pragma unroll
+      for (int u = 0; u < kSlotBatch; ++u)    // accumulate in slot order
+        if (pos[u] >= 0 && c < a.H) {
+          const float sc = __builtin_bit_cast(float, ev[u] << 23);   // 2^(E - 127), E in [1, 254]
+          const uint32_t w4[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t b = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+            acc[e] = __builtin_fmaf(wgt[u], (float)__builtin_bit_cast(_Float16, b) * sc, acc[e]);
+          }
+        }
+    }
+    if (c < a.H) {
+      if (a.out_bf16) {
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_rne(acc[2 * e]) | (f32_to_bf16_rne(acc[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + t * a.H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        float* orow = static_cast<float*>(a.out) + t * a.H + c;
+        *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4*>(orow + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      }
+    }
+  }
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t nblk = (a.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = a.T * nblk;
   const int64_t grid = items < (1 << 20) ? items : (1 << 20);
-  if (a.y16)
+  if (a.y16 && a.H % 8 == 0) {
+    const int64_t nb16 = (a.H + kY16Cols - 1) / kY16Cols;
+    const int64_t it16 = a.T * nb16;
+    const int64_t g16 = it16 < (1 << 20) ? it16 : (1 << 20);
+    hipLaunchKernelGGL(combine_y16_kernel, dim3((unsigned)g16), dim3(kWave), 0, s, a);
+  } else if (a.y16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);

@@ -262,11 +262,12 @@ def test_intermediate_h_matches_oracle(mode, name, tactic):
     parity(y, yr, f"y {mode}", y_rounding_allowance(inp, spec, ref, mode, P))
 
 
-def test_bf16_output_is_rne_of_fp32_output():
-    spec = S.spec_of(SMALL["wide"])
+@pytest.mark.parametrize("name,mode,tactic", [("wide", "w4a16", (-1, -1)), ("prefill_c", "w4a8", (4, 20))])
+def test_bf16_output_is_rne_of_fp32_output(name, mode, tactic):
+    spec = S.spec_of(SMALL[name])
     inp = S.generate(spec)
-    f, *_ = run_layer(inp, spec, out_dtype="f32")
-    b, *_ = run_layer(inp, spec, out_dtype="bf16")
+    f, *_ = run_layer(inp, spec, mode=mode, out_dtype="f32", tactic=tactic)
+    b, *_ = run_layer(inp, spec, mode=mode, out_dtype="bf16", tactic=tactic)
     assert np.array_equal(b, F.f32_to_bf16_rne(f))
 
 
