@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 # Sources whose change invalidates stored HBM-traffic counters of the GEMM kernels.
 GEMM_SOURCES = ("block_scaled_mxfp4_amd/csrc/gemm.hip", "block_scaled_mxfp4_amd/csrc/prefill.hip",
+                "block_scaled_mxfp4_amd/csrc/dma.hpp",
                 "block_scaled_mxfp4_amd/csrc/common.hpp", "block_scaled_mxfp4_amd/csrc/internal.hpp",
                 "block_scaled_mxfp4_amd/build.py")
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
