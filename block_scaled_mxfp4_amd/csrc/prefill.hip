@@ -248,10 +248,12 @@ __device__ __forceinline__ void st16(const v4i& r, uint32_t voff, f32x4 v) {
   asm volatile("s_nop 1\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
                : "memory");
 }
-// Max over each row of 16 lanes with DPP lane moves (no LDS round trips):
-// swap neighbours, swap pairs, mirror within 8, mirror within 16.
-__device__ __forceinline__ float dpp_max(float m, int ctrl_id) {
-  const int b = __builtin_bit_cast(int, m);
+// Max over each row of 16 lanes of a non-negative float, on its bit
+// pattern (ordered like the value for non-negative floats), with DPP lane
+// moves (no LDS round trips): swap neighbours, swap pairs, mirror within 8,
+// mirror within 16.
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t m, int ctrl_id) {
+  const int b = (int)m;
   int o;
   switch (ctrl_id) {
     case 0: o = __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false); break;    // quad_perm [1,0,3,2]
@@ -259,10 +261,10 @@ __device__ __forceinline__ float dpp_max(float m, int ctrl_id) {
     case 2: o = __builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
     default: o = __builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false); break;  // row_mirror
   }
-  return fmaxf(m, __builtin_bit_cast(float, o));
+  return max(m, (uint32_t)o);
 }
 __device__ __forceinline__ float row16_max(float m) {
-  return dpp_max(dpp_max(dpp_max(dpp_max(m, 0), 1), 2), 3);
+  return __builtin_bit_cast(float, dpp_umax(dpp_umax(dpp_umax(dpp_umax(__builtin_bit_cast(uint32_t, m), 0), 1), 2), 3));
 }
 __device__ __forceinline__ void st8(const v4i& r, uint32_t voff, uint32_t lo, uint32_t hi) {
   const uint2 w = make_uint2(lo, hi);
@@ -281,7 +283,7 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
-template <bool FC1, int TOK = kPfTok>
+template <bool FC1, int TOK = kPfTok, bool Y16 = false>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
                                             int wave, int lane, uint8_t* scratch) {
   const int r = lane & 15, g = lane >> 4;
@@ -343,12 +345,11 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     // cache lines) instead of 16 tokens x 64 bytes.  scratch = 4352 bytes of
     // this wave's, in the stage the next item's first requests leave free.
     const int H = a.N;
-    // fp16 y (out_scale = its exponents): each 64-column row segment, held
+    // fp16 y (Y16; out_scale = its exponents): each 64-column row segment, held
     // by 16 lanes, takes the power-of-two scale that puts its largest
     // magnitude in [2^14, 2^15); exponent byte E means a scale of 2^(E-127)
-    const bool y16 = a.out_scale != nullptr;
     const int nb64 = (H + 63) / 64;
-    const v4i yr = y16 ? rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 2))
+    const v4i yr = Y16 ? rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 2))
                        : rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
     // exponents column-block major: one block's bytes of consecutive rows are
     // contiguous, so an item writes whole lines of them
@@ -363,13 +364,18 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
           *reinterpret_cast<f32x4*>(scratch + r * kRowPitch + (16 * i + 4 * g) * 4) = acc[4 * half + i][tt];
         const int tok = lane >> 4, chunk = lane & 15;
         const int col = n0 + 16 * 8 * wn + 64 * half + 4 * chunk;
+        // all four reads first: the stores below are ordered memory operations
+        // the compiler does not move reads across
+        f32x4 vk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vk[k] = *reinterpret_cast<const f32x4*>(scratch + (4 * k + tok) * kRowPitch + 16 * chunk);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int t = 4 * k + tok;                  // token within the 16-token tile
-          const f32x4 v = *reinterpret_cast<const f32x4*>(scratch + t * kRowPitch + 16 * chunk);
+          const f32x4 v = vk[k];
           const int pr = 32 * wm + 16 * tt + t;
           const bool ok = x.p0 + pr < x.p1 && col < H;
-          if (!y16) {
+          if constexpr (!Y16) {
             st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
           } else {
             // columns past H hold zeros (their weight rows read as zero)
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
       pw_issue(lds_addr_of(st0), d, 0);
     }
     // the second stage is free for FC2's output transpose
-    pf_epilogue<FC1, kWTok>(a, cur, acc, wn, wm, wave, lane, st1 + wave * 4352);
+    pf_epilogue<FC1, kWTok, !FC1>(a, cur, acc, wn, wm, wave, lane, st1 + wave * 4352);
     cur = nxt;
   }
 }
