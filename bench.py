@@ -2,11 +2,19 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
 
-A step is one call of the whole layer (routing, [MXFP8 quantization],
-FC1 + SiTU, FC2, combine) over one batch of synthetic tokens already
-resident in HBM.  The default workload is the TP8-shard decode batch the
-metric is quoted on (config 1: 64 tokens, hidden 3584, 896 local experts,
-intermediate 384, top-16, w4a16); --config selects another shard shape.
+A step is one call of the whole layer (routing, FC1 + SiTU, FC2, combine)
+over one batch of synthetic tokens already resident in HBM.  The default
+workload is the TP8-shard decode batch the metric is quoted on (config 1:
+64 tokens, hidden 3584, 896 local experts, intermediate 384, top-16,
+w4a16); --config selects another shard shape.  The w4a8 prefill shards take
+their activations MXFP8-quantized per token, as the workload defines them
+(quantized once by the library before timing); the step with bf16 input and
+the library's own quantization is reported beside it.
+
+value comes from plain (eager) calls.  The step is also captured once into a
+HIP graph and replayed (the layer runs no host synchronization and records
+no memset node); the replay time and whether its output equals the eager
+one bit for bit are reported beside it.
 
 Prints one JSON line: tokens/s, ms per step, the roofline of the dominant
 kernel (algorithmic bytes or flops per launch over its average duration
@@ -58,7 +66,9 @@ def algorithmic_work(spec, counts, tokens_used, y_format=0):
         "fc2_bytes": A * fc2_w + P * h_row + (P * (2 * H + (H + 63) // 64) if y_format else P * H * 4),
         "fc1_flops": 2.0 * P * H * 2 * I,
         "fc2_flops": 2.0 * P * I * H,
-        "layer_bytes": A * (fc1_w + fc2_w) + T * 2 * H + T * k * 6 + T * H * 4,
+        # the layer's own inputs and output: weights of the active experts, the
+        # activations as the workload gives them (w4a8: MXFP8 per token), routing, fp32 out
+        "layer_bytes": A * (fc1_w + fc2_w) + T * x_row + T * k * 6 + T * H * 4,
         "quantize_bytes": T * 2 * H + T * (H + H // 32) if w4a8 else 0,
     }
     return work
@@ -171,14 +181,28 @@ def main(argv=None):
 
     packed = inp.get("topk_packed") is not None
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
-    prob = B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
-                          local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
-                          act_mode=spec["mode"], topk_packed=packed, out_dtype="f32")
+    w4a8 = spec["mode"] == "w4a8"
+
+    def problem(prequantized):
+        return B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
+                              local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
+                              act_mode=spec["mode"], act_prequantized=prequantized, topk_packed=packed,
+                              out_dtype="f32")
+
+    x_bf16 = d(inp["hidden_states"])
+    prob = problem(w4a8)
     plan = B.situ_moe_plan(prob)
-    tens = dict(hidden_states=d(inp["hidden_states"]), w1=d(inp["w1"]), w1_scale=d(inp["w1_scale"]),
+    if w4a8:   # the workload's activations arrive MXFP8-quantized per token
+        x_codes = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        x_scales = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        B.situ_moe_quantize_mxfp8(x_bf16, x_codes, x_scales)
+        torch.cuda.synchronize()
+    tens = dict(hidden_states=x_codes if w4a8 else x_bf16, w1=d(inp["w1"]), w1_scale=d(inp["w1_scale"]),
                 w2=d(inp["w2"]), w2_scale=d(inp["w2_scale"]), situ_beta=d(inp["situ_beta"]),
                 situ_linear_beta=d(inp["situ_linear_beta"]), alpha_gate=d(inp["alpha_gate"]),
                 alpha_up=d(inp["alpha_up"]), out=torch.empty((T, H), dtype=torch.float32, device=dev))
+    if w4a8:
+        tens["hidden_states_scale"] = x_scales
     if packed:
         tens["topk_packed"] = d(inp["topk_packed"])
     else:
@@ -205,7 +229,58 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / K
+    eager_ms = start.elapsed_time(end) / K
+    eager_out = tens["out"].clone()
+
+    # The same step captured once into a HIP graph, replayed K times.
+    graph_ms = None
+    graph_same = None
+    graph_error = None
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            B.situ_moe_run(plan, ts, ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            B.situ_moe_run(plan, ts, ws)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record(stream)
+        for _ in range(K):
+            graph.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        graph_same = bool(torch.equal(tens["out"].view(torch.int32), eager_out.view(torch.int32)))
+        graph_ms = gs.elapsed_time(ge) / K
+        del graph
+    except Exception as e:   # capture unavailable: reported, the eager number stands regardless
+        graph_error = f"{type(e).__name__}: {e}"
+    ms_per_step = eager_ms
+
+    bf16_input_ms = None
+    if w4a8:   # bf16 activations, quantized by the library inside the step
+        prob16 = problem(False)
+        plan16 = B.situ_moe_plan(prob16)
+        t16 = dict(tens, hidden_states=x_bf16)
+        t16.pop("hidden_states_scale")
+        ts16 = B.make_tensors(prob16, **t16)
+        ws16 = B.new_workspace(plan16, dev)
+        for _ in range(3):
+            B.situ_moe_run(plan16, ts16, ws16)
+        torch.cuda.synchronize()
+        bs, be = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bs.record(stream)
+        for _ in range(K):
+            B.situ_moe_run(plan16, ts16, ws16)
+        be.record(stream)
+        torch.cuda.synchronize()
+        bf16_input_ms = bs.elapsed_time(be) / K
+        del ws16
 
     # Kernel durations: K more calls, each recording six HIP events on the
     # library's stream at the stage boundaries (the events themselves add a
@@ -223,7 +298,6 @@ def main(argv=None):
     tokens_used = int(np.count_nonzero((inv >= 0).any(axis=1)))
     work = algorithmic_work(spec, counts, tokens_used, plan.y_format)
 
-    w4a8 = spec["mode"] == "w4a8"
     dom = "fc1" if stage_ms["fc1"] >= stage_ms["fc2"] else "fc2"
     workload = f"{spec['name']}_{spec['mode']}"
     traffic = stored_traffic(workload, dom)
@@ -270,7 +344,14 @@ def main(argv=None):
         "layer_hbm_gbs": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
         "wall_s_timed_region": round(wall, 4),
+        "graph_replay": {"ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
+                         "bitwise_equal_to_eager": graph_same, "error": graph_error},
+        "activations": "MXFP8 per token (prequantized)" if w4a8 else "bf16",
     }
+    if bf16_input_ms is not None:
+        res["bf16_input"] = {"ms_per_step": round(bf16_input_ms, 5),
+                             "tokens_per_s": round(T / (bf16_input_ms * 1e-3), 1),
+                             "note": "the same step with bf16 activations quantized by the library (eager)"}
     if not args.no_cpu_baseline:
         _log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(inp, spec)
