@@ -43,14 +43,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         wgt[u] = bf16_to_f32(wb);
       }
       if constexpr (Y16) {
-        const int64_t rows = a.T * a.k;
+        const int64_t nb64 = (a.H + 63) / 64;
         uint2 hv[kSlotBatch];
         uint32_t ev[kSlotBatch];
 #pragma unroll
         for (int u = 0; u < kSlotBatch; ++u)
           if (pos[u] >= 0) {
             hv[u] = *reinterpret_cast<const uint2*>(a.y16 + (int64_t)pos[u] * a.H + c);
-            ev[u] = a.y_exp[(int64_t)(c / 64) * rows + pos[u]];
+            ev[u] = a.y_exp[(int64_t)pos[u] * nb64 + c / 64];
           }
 #pragma unroll
         for (int u = 0; u < kSlotBatch; ++u)
@@ -92,7 +92,7 @@ constexpr int kY16Cols = 512;
 __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
   const int nblk = (a.H + kY16Cols - 1) / kY16Cols;
   const int64_t items = a.T * nblk;
-  const int64_t rows = a.T * a.k;
+  const int64_t nb64 = (a.H + 63) / 64;
   const int lane = threadIdx.x;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int64_t t = it / nblk;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
       for (int u = 0; u < kSlotBatch; ++u)
         if (pos[u] >= 0 && c < a.H) {
           hv[u] = *reinterpret_cast<const uint4*>(a.y16 + (int64_t)pos[u] * a.H + c);
-          ev[u] = a.y_exp[(int64_t)(c / 64) * rows + pos[u]];
+          ev[u] = a.y_exp[(int64_t)pos[u] * nb64 + c / 64];
         }
 #pragma unroll
       for (int u = 0; u < kSlotBatch; ++u)    // accumulate in slot order

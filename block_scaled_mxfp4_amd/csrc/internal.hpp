@@ -66,7 +66,7 @@ struct GemmArgs {
 struct CombineArgs {
   const float* y;             // [P, H] fp32, or null when y16 is given
   const uint16_t* y16;        // [P, H] fp16 scaled per 64 columns by 2^(y_exp - 127), or null
-  const uint8_t* y_exp;       // [ceil(H/64), T*k]: column block major
+  const uint8_t* y_exp;       // [T*k, ceil(H/64)]: row-major
   const int32_t* inv;         // [T*k]
   const uint16_t* weights;    // bf16 [T, k] or null
   const int32_t* packed;      // [T, k] or null

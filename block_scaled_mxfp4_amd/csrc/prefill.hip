@@ -351,8 +351,10 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     const int nb64 = (H + 63) / 64;
     const v4i yr = Y16 ? rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 2))
                        : rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
-    // exponents column-block major: one block's bytes of consecutive rows are
-    // contiguous, so an item writes whole lines of them
+    // exponents row-major [row][nb64]: a row's bytes are contiguous for the
+    // combine, which gathers whole rows; the n-tiles of one m-tile run back to
+    // back on one XCD, so their bytes of a line meet in its L2 before the
+    // line is written back
     const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
     constexpr int kRowPitch = 64 * 4 + 16;          // padded: the tile writes hit 16 distinct bank groups
 #pragma unroll
@@ -389,7 +391,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
             const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(v[2] * inv));
             const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(v[3] * inv));
             st8(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, h0 | (h1 << 16), h2 | (h3 << 16));
-            st1(er, (ok && chunk == 0) ? (uint32_t)(col / 64) * (uint32_t)a.out_rows + (uint32_t)(x.p0 + pr) : kOobPf,
+            st1(er, (ok && chunk == 0) ? (uint32_t)(x.p0 + pr) * (uint32_t)nb64 + (uint32_t)(col / 64) : kOobPf,
                 (uint32_t)E);
           }
         }

@@ -109,7 +109,7 @@ typedef struct situ_moe_plan_t {
                                    fp16 [T*k, H] scaled by 2^(y_exp - 127) per 64 columns (y_format 1) */
   uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms (route_blocks > 1) */
   uint64_t off_tile_rows;       /* int32 [max_mtiles, 2] first and one-past-last perm position of each m-tile */
-  uint64_t off_y_exp;           /* uint8 [ceil(H/64), T*k] block exponents of y (y_format 1), column block major,
+  uint64_t off_y_exp;           /* uint8 [T*k, ceil(H/64)] block exponents of y (y_format 1), row-major,
                                    inside the y region */
   int32_t y_format;             /* 0: fp32 y; 1: fp16 y with an exponent per 64 columns (the 128-row w4a8 tactic) */
   uint32_t reserved[3];

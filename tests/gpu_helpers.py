@@ -264,6 +264,6 @@ def read_y(plan, ws, P, H):
     nb = (H + 63) // 64
     y16 = ws_region(plan, ws, "y", torch.float16, (P, H)).astype(np.float64)
     rows = plan.prob.num_tokens * plan.prob.top_k
-    e = ws_region(plan, ws, "y_exp", torch.uint8, (nb, rows))[:, :P].T.astype(np.int64)
+    e = ws_region(plan, ws, "y_exp", torch.uint8, (rows, nb))[:P].astype(np.int64)
     assert np.all((e >= 1) & (e <= 254))
     return y16 * np.ldexp(1.0, np.repeat(e, 64, axis=1)[:, :H] - 127)
