@@ -248,29 +248,6 @@ __device__ __forceinline__ void st16(const v4i& r, uint32_t voff, f32x4 v) {
   asm volatile("s_nop 1\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
                : "memory");
 }
-// Max over each row of 16 lanes of a non-negative float, on its bit
-// pattern (ordered like the value for non-negative floats), with DPP lane
-// moves (no LDS round trips): swap neighbours, swap pairs, mirror within 8,
-// mirror within 16.
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t m, int ctrl_id) {
-  const int b = (int)m;
-  int o;
-  switch (ctrl_id) {
-    case 0: o = __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false); break;    // quad_perm [1,0,3,2]
-    case 1: o = __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false); break;    // quad_perm [2,3,0,1]
-    case 2: o = __builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
-    default: o = __builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false); break;  // row_mirror
-  }
-  return max(m, (uint32_t)o);
-}
-__device__ __forceinline__ float row16_max(float m) {
-  return __builtin_bit_cast(float, dpp_umax(dpp_umax(dpp_umax(dpp_umax(__builtin_bit_cast(uint32_t, m), 0), 1), 2), 3));
-}
-__device__ __forceinline__ void st8(const v4i& r, uint32_t voff, uint32_t lo, uint32_t hi) {
-  const uint2 w = make_uint2(lo, hi);
-  asm volatile("s_nop 1\n\tbuffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(w), "v"(voff), "s"(r)
-               : "memory");
-}
 __device__ __forceinline__ void st4(const v4i& r, uint32_t voff, uint32_t v) {
   asm volatile("buffer_store_dword %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
 }
@@ -283,7 +260,7 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
-template <bool FC1, int TOK = kPfTok, bool Y16 = false>
+template <bool FC1, int TOK = kPfTok>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
                                             int wave, int lane, uint8_t* scratch) {
   const int r = lane & 15, g = lane >> 4;
@@ -345,17 +322,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     // cache lines) instead of 16 tokens x 64 bytes.  scratch = 4352 bytes of
     // this wave's, in the stage the next item's first requests leave free.
     const int H = a.N;
-    // fp16 y (Y16; out_scale = its exponents): each 64-column row segment, held
-    // by 16 lanes, takes the power-of-two scale that puts its largest
-    // magnitude in [2^14, 2^15); exponent byte E means a scale of 2^(E-127)
-    const int nb64 = (H + 63) / 64;
-    const v4i yr = Y16 ? rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 2))
-                       : rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
-    // exponents row-major [row][nb64]: a row's bytes are contiguous for the
-    // combine, which gathers whole rows; the n-tiles of one m-tile run back to
-    // back on one XCD, so their bytes of a line meet in its L2 before the
-    // line is written back
-    const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
+    const v4i yr = rsrc4(static_cast<float*>(a.out) + (size_t)x.p0 * H, (uint32_t)(TOK * H * 4));
     constexpr int kRowPitch = 64 * 4 + 16;          // padded: the tile writes hit 16 distinct bank groups
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -377,23 +344,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
           const f32x4 v = vk[k];
           const int pr = 32 * wm + 16 * tt + t;
           const bool ok = x.p0 + pr < x.p1 && col < H;
-          if constexpr (!Y16) {
-            st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
-          } else {
-            // columns past H hold zeros (their weight rows read as zero)
-            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-            m = row16_max(m);
-            const int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 127;   // floor(log2 m)
-            const int E = min(max(e + 113, 1), 254);
-            const float inv = __builtin_bit_cast(float, (uint32_t)(254 - E) << 23);     // 2^(127 - E)
-            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(v[0] * inv));
-            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(v[1] * inv));
-            const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(v[2] * inv));
-            const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(v[3] * inv));
-            st8(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, h0 | (h1 << 16), h2 | (h3 << 16));
-            st1(er, (ok && chunk == 0) ? (uint32_t)(x.p0 + pr) * (uint32_t)nb64 + (uint32_t)(col / 64) : kOobPf,
-                (uint32_t)E);
-          }
+          st16(yr, ok ? (uint32_t)(pr * H + col) * 4u : kOobPf, v);
         }
       }
   }
@@ -512,6 +463,7 @@ constexpr int kWStSB = kWStSA + 2 * kWRows * 4;             // [8 token tiles][2
 constexpr int kWStage = kWStSB + kWTok * 2 * 4;             // 74752 bytes
 constexpr int kWDmas = 10;                                  // DMAs per wave per stage
 
+
 struct PwGeo {
   v4i wr, sr, xr, xsr;
   uint32_t a_row[2][2];  // [tile][block]: row offset of this lane's row (kOobPf: none)
@@ -624,8 +576,83 @@ __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, i
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 22, 0);   // the step's LDS reads first
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then its MFMAs
+  // the token fragments and the first two weight tiles' reads, then each
+  // weight tile's MFMA pair followed by the reads of the tile two ahead, so
+  // only the first reads' latency precedes the MFMAs (all 22 reads first
+  // measured 7 % slower on FC1)
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// A store whose data comes from LDS reads (not from an MFMA), so no VALU
+// pass is needed before it; wait states after it cover its late read of
+// the data registers.
+__device__ __forceinline__ void st16u(const v4i& r, uint32_t voff, u32x4 v) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
+}
+
+// FC2 epilogue of the wide kernel's 128 x 32 wave tile: fp16 y with one
+// exponent per 64 columns of a row.  For each 16-token x 64-column block
+// the row maximum (over the 4 lanes that share a token), the exponent and
+// the fp16 codes are made in the MFMA layout; the codes then go through the
+// wave's LDS scratch (16 rows of 144 bytes) so that a row store covers 8
+// tokens x 128 contiguous bytes, and the block's 16 exponent bytes leave in
+// one store.  3 stores per block.
+constexpr int kWYPitch = 128 + 16;
+constexpr int kWYScratch = 16 * kWYPitch;
+__device__ __forceinline__ void pw_epilogue_y16(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
+                                                int lane, uint8_t* scratch) {
+  const int r = lane & 15, g = lane >> 4;
+  const int H = a.N, n0 = x.nt * kWRows;
+  const int nb64 = (H + 63) / 64;
+  const v4i yr = rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kWTok * H * 2));
+  const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
+  const int t8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int col0 = n0 + 128 * wn + 64 * half;   // first column of the block
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[4 * half + i][tt][e]));
+      m = fmaxf(m, __shfl_xor(m, 16, kWave));       // columns past H hold zeros
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 127;   // floor(log2 m)
+      const int E = min(max(ex + 113, 1), 254);
+      const float inv = __builtin_bit_cast(float, (uint32_t)(254 - E) << 23);        // 2^(127 - E)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = acc[4 * half + i][tt];
+        const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(v[0] * inv));
+        const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(v[1] * inv));
+        const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(v[2] * inv));
+        const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(v[3] * inv));
+        // token r, columns 16i + 4g .. +3 of the block
+        *reinterpret_cast<uint2*>(scratch + r * kWYPitch + 32 * i + 8 * g) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+      u32x4 rows[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) rows[k] = *reinterpret_cast<const u32x4*>(scratch + (8 * k + t8) * kWYPitch + 16 * c8);
+      const int col = col0 + 8 * c8;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pr = 32 * wm + 16 * tt + 8 * k + t8;   // row within the item
+        const bool ok = x.p0 + pr < x.p1 && col < H;
+        st16u(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, rows[k]);
+      }
+      const int pe = 32 * wm + 16 * tt + r;
+      const bool oke = g == 0 && x.p0 + pe < x.p1 && col0 < H;
+      st1(er, oke ? (uint32_t)(x.p0 + pe) * (uint32_t)nb64 + (uint32_t)(col0 / 64) : kOobPf, (uint32_t)E);
+    }
 }
 
 // Item -> expert, n-tile and pair range (128-row routing tiles, exact ranges
@@ -707,7 +734,8 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
       pw_issue(lds_addr_of(st0), d, 0);
     }
     // the second stage is free for FC2's output transpose
-    pf_epilogue<FC1, kWTok, !FC1>(a, cur, acc, wn, wm, wave, lane, st1 + wave * 4352);
+    if constexpr (FC1) pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr);
+    else pw_epilogue_y16(a, cur, acc, wn, wm, lane, st1 + wave * kWYScratch);
     cur = nxt;
   }
 }
