@@ -113,37 +113,40 @@ __device__ __forceinline__ float exp_fast(float x) {
   return __builtin_amdgcn_exp2f(x * kL2e);
 }
 
-// tanh in fp32 within ~1e-6 relative.  |x| < 0.7: the odd polynomial
-// x + x^3 * Q(x^2), Q of degree 4 fitted (iteratively reweighted least
-// squares on [0, 0.7], uniform relative error ~1.5 ulp); above: the identity
-// tanh(a) = 1 - 2 / (e^(2a) + 1), where tanh > 0.6 so the subtraction loses
-// no accuracy.
-__device__ __forceinline__ float tanh_fast(float x) {
-  const float a = fabsf(x);
-  const float x2 = a * a;
-  float q = -0.005230488255620003f;
-  q = fmaf(q, x2, 0.020192988216876984f);
-  q = fmaf(q, x2, -0.05359668657183647f);
-  q = fmaf(q, x2, 0.13329659402370453f);
-  q = fmaf(q, x2, -0.3333321511745453f);
-  const float small = fmaf(a * x2, q, a);
-  const float big = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp_fast(2.0f * a) + 1.0f);
-  return copysignf(a < 0.7f ? small : big, x);
+// tanh(x) as a quotient n / d of fp32 values: x clamped to [-9, 9] (tanh(9)
+// is 1 in fp32), n = x P(x^2), d = Q(x^2) with P, Q of degree 4, fitted on
+// [0, 9] for the smallest largest relative error (reweighted least squares
+// on the linearized residual x P - tanh(x) Q): 3.5e-7 relative when evaluated
+// in fp32 by Horner's rule.  All coefficients are positive, so d >= 1.
+__device__ __forceinline__ void tanh_nd(float x, float& n, float& d) {
+  const float c = __builtin_amdgcn_fmed3f(x, -9.0f, 9.0f);
+  const float s = c * c;
+  float p = 1.3419761e-08f, q = 7.80470088e-07f;
+  p = fmaf(p, s, 2.06612074e-05f); q = fmaf(q, s, 0.000329103255f);
+  p = fmaf(p, s, 0.00349899239f);  q = fmaf(q, s, 0.0258901921f);
+  p = fmaf(p, s, 0.133839771f);    q = fmaf(q, s, 0.467172986f);
+  p = fmaf(p, s, 1.0f);            q = fmaf(q, s, 1.0f);
+  n = c * p;
+  d = q;
 }
 
 // SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)] in fp32, rb = 1/b
-// and rlb = 1/lb precomputed per expert.  Relative error below ~4e-6 over
-// every input range (host emulation of the fp32 steps: 9 ulp for inputs of
-// unit scale, 61 ulp at scale 30): h feeds a rounding point (bf16, or MXFP8
-// whose E4M3 steps are 6-12 % apart), and an h this close to the exact
-// value flips a rounding decision only for elements within ~2^-18 of a
-// rounding boundary.  (The tanh-free form 2c*sigmoid(2x/c) - c of the
-// MegaMoE commit cancels near x = 0 and loses that accuracy.)
+// and rlb = 1/lb precomputed per expert, as one quotient: the two tanh
+// quotients and sigmoid = 1 / (1 + e^-g) share a single reciprocal (one
+// exponential and one reciprocal per element).  Relative error below ~4e-6
+// over every input range (host emulation of these fp32 steps against
+// float64: 6e-7 for inputs of unit scale, 3.8e-6 at scale 30-100, where the
+// rounding of -g*log2(e) dominates): h feeds a rounding point (bf16, or MXFP8
+// whose E4M3 steps are 6-12 % apart), and an h this close to the exact value
+// flips a rounding decision only for elements within ~2^-18 of a rounding
+// boundary.  For g below about -76 the denominator overflows and h is 0 (the
+// exact value is below 1e-33).
 __device__ __forceinline__ float situ_act(float g, float u, float b, float lb, float rb, float rlb) {
-  const float tg = b * tanh_fast(g * rb);
-  const float sg = __builtin_amdgcn_rcpf(1.0f + exp_fast(-g));
-  const float tu = lb * tanh_fast(u * rlb);
-  return tg * sg * tu;
+  float n1, d1, n3, d3;
+  tanh_nd(g * rb, n1, d1);
+  tanh_nd(u * rlb, n3, d3);
+  const float den = (d1 * d3) * (1.0f + exp_fast(-g));
+  return ((b * n1) * (lb * n3)) * __builtin_amdgcn_rcpf(den);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
 // With two K steps a weight row contributes 128 contiguous bytes per stage,
 // so the weight DMAs also move whole cache lines (8 rows x 128 B per
 // instruction, swizzled like the activations); the larger token tile halves
-// the weight bytes staged per MFMA.  Two stages of 73 KB: one workgroup per
+// the weight bytes staged per MFMA.  Two stages of 75 KB: one workgroup per
 // CU.  Routed with 128-row m-tiles.
 namespace {
 
@@ -460,7 +460,7 @@ constexpr int kWStA = 0;                                    // 16 weight tiles
 constexpr int kWStB = kWStA + 16 * kWTileSw;                // [2 steps][8 token tiles]
 constexpr int kWStSA = kWStB + 16 * kWTileSw;               // [2 steps][256 rows] scale dwords
 constexpr int kWStSB = kWStSA + 2 * kWRows * 4;             // [8 token tiles][2 steps][16 tokens]
-constexpr int kWStage = kWStSB + kWTok * 2 * 4;             // 74752 bytes
+constexpr int kWStage = kWStSB + kWTok * 2 * 4;             // 76800 bytes
 constexpr int kWDmas = 10;                                  // DMAs per wave per stage
 
 
