@@ -598,27 +598,28 @@ __device__ __forceinline__ void st16u(const v4i& r, uint32_t voff, u32x4 v) {
 }
 
 // FC2 epilogue of the wide kernel's 128 x 32 wave tile: fp16 y with one
-// exponent per 64 columns of a row.  For each 16-token x 64-column block
-// the row maximum (over the 4 lanes that share a token), the exponent and
-// the fp16 codes are made in the MFMA layout; the codes then go through the
+// exponent per 64 columns of a row.  For each 16-token x 64-column block the
+// row maximum (over the 4 lanes that share a token), the exponent and the
+// fp16 codes are made in the MFMA layout; the codes then go through the
 // wave's LDS scratch (16 rows of 144 bytes) so that a row store covers 8
 // tokens x 128 contiguous bytes, and the block's 16 exponent bytes leave in
-// one store.  3 stores per block.
+// one store: 12 stores per wave and item.  The rows and exponents are made
+// at the item's end (pw_y16_prepare) but their stores leave four at a time
+// during the next item's first K steps (pw_y16_store), so that they drain
+// while the matrix cores run instead of stalling all eight waves at once.
 constexpr int kWYPitch = 128 + 16;
 constexpr int kWYScratch = 16 * kWYPitch;
-__device__ __forceinline__ void pw_epilogue_y16(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
-                                                int lane, uint8_t* scratch) {
+struct YPend {
+  u32x4 rows[8];     // [2 * block + k]
+  uint32_t e[4];     // exponent of token r's row segment, per block
+};
+__device__ __forceinline__ void pw_y16_prepare(f32x4 acc[8][2], int lane, uint8_t* scratch, YPend& yp) {
   const int r = lane & 15, g = lane >> 4;
-  const int H = a.N, n0 = x.nt * kWRows;
-  const int nb64 = (H + 63) / 64;
-  const v4i yr = rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kWTok * H * 2));
-  const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
   const int t8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int col0 = n0 + 128 * wn + 64 * half;   // first column of the block
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -639,20 +640,37 @@ __device__ __forceinline__ void pw_epilogue_y16(const GemmArgs& a, const PfItem&
         // token r, columns 16i + 4g .. +3 of the block
         *reinterpret_cast<uint2*>(scratch + r * kWYPitch + 32 * i + 8 * g) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
       }
-      u32x4 rows[2];
+      const int blk = 2 * tt + half;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) rows[k] = *reinterpret_cast<const u32x4*>(scratch + (8 * k + t8) * kWYPitch + 16 * c8);
+      for (int k = 0; k < 2; ++k) yp.rows[2 * blk + k] = *reinterpret_cast<const u32x4*>(scratch + (8 * k + t8) * kWYPitch + 16 * c8);
+      yp.e[blk] = (uint32_t)E;
+    }
+}
+// Stores 4 PART .. 4 PART + 3 of the 12: per block, two row stores (8 tokens
+// each) and the exponent store.
+template <int PART>
+__device__ __forceinline__ void pw_y16_store(const GemmArgs& a, const PfItem& x, const YPend& yp, int wn, int wm, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int t8 = lane >> 3, c8 = lane & 7;
+  const int H = a.N, n0 = x.nt * kWRows;
+  const int nb64 = (H + 63) / 64;
+  const v4i yr = rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kWTok * H * 2));
+  const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
+#pragma unroll
+  for (int j = 4 * PART; j < 4 * PART + 4; ++j) {
+    const int blk = j / 3, kind = j % 3, tt = blk >> 1, half = blk & 1;
+    const int col0 = n0 + 128 * wn + 64 * half;
+    if (kind < 2) {
+      const int pr = 32 * wm + 16 * tt + 8 * kind + t8;
       const int col = col0 + 8 * c8;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int pr = 32 * wm + 16 * tt + 8 * k + t8;   // row within the item
-        const bool ok = x.p0 + pr < x.p1 && col < H;
-        st16u(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, rows[k]);
-      }
+      const bool ok = x.p0 + pr < x.p1 && col < H;
+      st16u(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, yp.rows[2 * blk + kind]);
+    } else {
       const int pe = 32 * wm + 16 * tt + r;
       const bool oke = g == 0 && x.p0 + pe < x.p1 && col0 < H;
-      st1(er, oke ? (uint32_t)(x.p0 + pe) * (uint32_t)nb64 + (uint32_t)(col0 / 64) : kOobPf, (uint32_t)E);
+      st1(er, oke ? (uint32_t)(x.p0 + pe) * (uint32_t)nb64 + (uint32_t)(col0 / 64) : kOobPf, yp.e[blk]);
     }
+  }
 }
 
 // Item -> expert, n-tile and pair range (128-row routing tiles, exact ranges
@@ -700,6 +718,11 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
     lds_barrier();
     pw_issue(lds_addr_of(st0), d, 0);
   }
+  // FC2: the previous item's y stores leave during this item's first K steps
+  // (before the stage requests when an item has three or more stages)
+  bool pend = false;
+  PfItem px{0, 0, 0, 0};
+  YPend yp;
   for (; it < i_end; it += per_xcd_wgs) {
     const int it_next = it + per_xcd_wgs;
     PfItem nxt{0, 0, 0, 0};
@@ -719,12 +742,28 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
         const int J = J0 + u;
         if (J < n_st) {
           dma_barrier<0>();                                  // stage J has landed everywhere
+          if constexpr (!FC1) {
+            if (pend) {
+              if (J == 0) pw_y16_store<0>(a, px, yp, wn, wm, lane);
+              else if (J == 1) {
+                if (n_st >= 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
+                else pw_y16_store<2>(a, px, yp, wn, wm, lane);
+              }
+              else if (J == 2) pw_y16_store<2>(a, px, yp, wn, wm, lane);
+            }
+          }
           if (J + 1 < n_st) pw_issue(lds_addr_of(u ? st0 : st1), d, J + 1);
           const uint8_t* stc = u ? st1 : st0;
           pw_compute(stc, 0, FC1, wn, wm, lane, acc);
+          if constexpr (!FC1) {
+            if (pend && J == 0 && n_st < 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
+          }
           if (2 * J + 1 < steps) pw_compute(stc, 1, FC1, wn, wm, lane, acc);
         }
       }
+    }
+    if constexpr (!FC1) {
+      if (pend && n_st < 2) pw_y16_store<2>(a, px, yp, wn, wm, lane);
     }
 
     // every wave is done with the stages: request the next item's first one
@@ -734,8 +773,18 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
       pw_issue(lds_addr_of(st0), d, 0);
     }
     // the second stage is free for FC2's output transpose
-    if constexpr (FC1) pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr);
-    else pw_epilogue_y16(a, cur, acc, wn, wm, lane, st1 + wave * kWYScratch);
+    if constexpr (FC1) {
+      pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr);
+    } else {
+      pw_y16_prepare(acc, lane, st1 + wave * kWYScratch, yp);
+      px = cur;
+      pend = true;
+      if (it_next >= i_end) {        // the last item: nothing to hide the stores behind
+        pw_y16_store<0>(a, px, yp, wn, wm, lane);
+        pw_y16_store<1>(a, px, yp, wn, wm, lane);
+        pw_y16_store<2>(a, px, yp, wn, wm, lane);
+      }
+    }
     cur = nxt;
   }
 }
