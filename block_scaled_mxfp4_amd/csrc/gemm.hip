@@ -390,9 +390,25 @@ struct Step {
   uint32_t xs;
 };
 
-// XL: the activation pieces may come from LDS (d.x_lds), read by compute_step.
+// w4a16 with the activation rows staged in LDS (XL and d.x_lds set): this
+// lane's piece of step j from there, zero past the group or past K.
+__device__ __forceinline__ void load_x_lds(uint4 x[4], const DecodeGeo& d, int j) {
+  const int kb = 4 * j + d.g;
+  const bool ok = kb < d.nkb && d.x_row != kOob;
+  const uint8_t* src = d.x_lds + (ok ? d.x_lds_off + (uint32_t)kb * 64u : 0u);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * c);
+    x[c] = ok ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// XL: the activation rows may be staged in LDS (d.x_lds); their pieces then
+// travel in the same register ring, read from LDS when x_now (once the
+// staging barrier has passed) and by load_x_lds for the steps requested
+// before it.
 template <bool FP8, bool XL = false>
-__device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int j) {
+__device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int j, bool x_now = true) {
   const int kb = 4 * j + d.g;
   const bool kin = kb < d.nkb;
   const uint32_t wo = kin ? d.w_row + (uint32_t)kb * 16u : kOob;
@@ -400,10 +416,12 @@ __device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int 
   for (int q = 0; q < 4; ++q)
     b.w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
   if constexpr (!FP8) {
-    if (!XL || d.x_lds == nullptr) {   // otherwise compute_step reads them from LDS
+    if (!XL || d.x_lds == nullptr) {
       const uint32_t xo = (kin && d.x_row != kOob) ? d.x_row + (uint32_t)kb * 64u : kOob;
 #pragma unroll
       for (int c = 0; c < 4; ++c) b.x[c] = bload16(d.xr, xo + 16u * c);
+    } else if (x_now) {
+      load_x_lds(b.x, d, j);
     }
     b.xs = 127u;
   } else {
@@ -418,7 +436,7 @@ __device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int 
   }
 }
 
-template <bool FP8, bool XL = false>
+template <bool FP8>
 __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo& d, int j, f32x4 acc[4]) {
   const int kb = 4 * j + d.g;
   const bool kin = kb < d.nkb;
@@ -426,19 +444,6 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 #pragma unroll
   for (int q = 0; q < 4; ++q) sv[q] = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
   if constexpr (!FP8) {
-    uint4 xv[4];
-    if (XL && d.x_lds != nullptr) {
-      const bool ok = kin && d.x_row != kOob;
-      const uint8_t* src = d.x_lds + (ok ? d.x_lds_off + (uint32_t)kb * 64u : 0u);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * c);
-        xv[c] = ok ? v : make_uint4(0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) xv[c] = b.x[c];
-    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float sc = e8m0_to_f32(sv[q]);
@@ -449,7 +454,7 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
       fp4x8_to_bf16x8(b.w[q].w, sc, wb + 12);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const uint32_t xb[4] = {xv[qq].x, xv[qq].y, xv[qq].z, xv[qq].w};
+        const uint32_t xb[4] = {b.x[qq].x, b.x[qq].y, b.x[qq].z, b.x[qq].w};
         acc[q] = mfma_bf16_16x16x32(wb + 4 * qq, xb, acc[q]);
       }
     }
@@ -469,23 +474,22 @@ __host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int n
   return (uint32_t)(units_per_wg * 64 * nkb + 15) / 16u * 16u;
 }
 __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return ksplit > 1 ? 4u * 4u * kWave * 16u : 0u; }
-// FC2 in w4a16: an m-tile of at most decode_x_rows() tokens has its h rows
-// staged in LDS once per work item; the K loop then reads them there instead
-// of every wave loading its lanes' pieces (mostly past the group: decode
-// m-tiles hold one or two tokens) beside the weights each step (TP8 decode
-// FC2 -6 %; FC1, whose rows are 7 KB, gained nothing and lost occupancy
-// when they took more than a few rows).  The rows get what is left of a third
-// of the LDS (kDecodeWavesPerSimd workgroups per CU) after the scales and
-// partial sums, 16 at most.
+// w4a16: an m-tile of at most decode_x_rows() tokens has its activation rows
+// staged in LDS once per work item; its pieces then travel in the register
+// ring from LDS instead of every wave loading its lanes' pieces (mostly past
+// the group: decode m-tiles hold one or two tokens) from memory beside the
+// weights each step (TP8 decode FC1 -2..5 %, FC2 -6 %).  The rows get what is
+// left of a third of the LDS (kDecodeWavesPerSimd workgroups per CU) after
+// the scales and partial sums, 16 at most (FC1 at H = 3584: 3 rows).
 __host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8, bool fc1) {
   const uint32_t budget = 160u * 1024u / (uint32_t)kDecodeWavesPerSimd - 512u;
   const uint32_t used = decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit);
   const uint32_t left = budget > used ? budget - used : 0u;
   const int rows = (int)(left / ((uint32_t)K * 2u));
-  return (fp8 || fc1) ? 0 : (rows < 16 ? rows : 16);
+  return fp8 ? 0 : (rows < 16 ? rows : 16);
 }
-__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, bool fc1, int ksplit, int K) {
-  return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8, fc1) * (uint32_t)K * 2u;
+__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, int ksplit, int K) {
+  return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8) * (uint32_t)K * 2u;
 }
 __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb, uint32_t x_bytes) {
   return decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit) + x_bytes;
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
   const int my_steps = j_end - j_begin;
   f32x4* red = reinterpret_cast<f32x4*>(lds + decode_lds_scales(UNITS_PER_WG, nkb));   // [4 waves][4][64]
   uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, nkb) + decode_lds_red(KSPLIT);
-  constexpr bool XL = !FP8 && !FC1;            // FC2 in w4a16 may stage its h rows
+  constexpr bool XL = !FP8;                    // w4a16 may stage its activation rows
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = w / n_wgn;
@@ -610,16 +614,19 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
         *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * nkb + 16 * cc) = bload16(sr, src);
       }
     }
-    // FC2 in w4a16 with few tokens: stage the m-tile's h rows (16-byte loads)
-    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, nkb, K, FP8, FC1);   // uniform
-    if constexpr (!FP8 && !FC1) {
+    // w4a16 with few tokens: stage the m-tile's activation rows (16-byte loads)
+    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, nkb, K, FP8);   // uniform
+    if constexpr (XL) {
       if (x_in_lds) {
         const int row_chunks = K / 8;               // K bf16 values / 16 bytes
+        // FC1 rows x[perm[p] / k]; FC2 rows h[p], addressed from the m-tile's first
         const __amdgpu_buffer_rsrc_t xr =
-            make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
+            FC1 ? make_rsrc(a.act, 0x7fffffff)
+                : make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
         for (int c = threadIdx.x; c < (p1 - p0) * row_chunks; c += kGemmThreads) {
           const int i = c / row_chunks, cc = c % row_chunks;
-          *reinterpret_cast<uint4*>(x_stage + (size_t)i * K * 2 + 16 * cc) = bload16(xr, (uint32_t)i * arow_bytes + 16u * cc);
+          const uint32_t row = FC1 ? (uint32_t)(a.perm[p0 + i] / a.top_k) : (uint32_t)i;
+          *reinterpret_cast<uint4*>(x_stage + (size_t)i * K * 2 + 16 * cc) = bload16(xr, row * arow_bytes + 16u * cc);
         }
       }
     }
@@ -669,9 +676,16 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
       // first kDecodeDepth steps of weights go out before the scale barrier
 #pragma unroll
       for (int u = 0; u < kDecodeDepth; ++u)
-        if (u < my_steps) load_step<FP8, XL>(buf[u], d, j_begin + u);
+        if (u < my_steps) load_step<FP8, XL>(buf[u], d, j_begin + u, false);
     }
-    __syncthreads();   // staged scales visible
+    __syncthreads();   // staged scales (and activation rows) visible
+    if constexpr (XL) {
+      if (active && d.x_lds != nullptr) {
+#pragma unroll
+        for (int u = 0; u < kDecodeDepth; ++u)
+          if (u < my_steps) load_x_lds(buf[u].x, d, j_begin + u);
+      }
+    }
 
     if (active) {
       // K loop over this wave's range: the weights of the next kDecodeDepth
@@ -686,7 +700,7 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
             if (i + u + kDecodeDepth < my_steps)
               load_step<FP8, XL>(buf[(u + kDecodeDepth) % NB], d, j_begin + i + u + kDecodeDepth);
             __builtin_amdgcn_sched_barrier(0);
-            compute_step<FP8, XL>(buf[u], d, j_begin + i + u, acc);
+            compute_step<FP8>(buf[u], d, j_begin + i + u, acc);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -750,9 +764,9 @@ static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hi
 template <bool FP8, bool FC1>
 hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
   switch (decode_ksplit(a.K)) {
-    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32, decode_lds_x(FP8, FC1, 4, a.K)));
-    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32, decode_lds_x(FP8, FC1, 2, a.K)));
-    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32, decode_lds_x(FP8, FC1, 1, a.K)));
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32, decode_lds_x(FP8, 4, a.K)));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32, decode_lds_x(FP8, 2, a.K)));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32, decode_lds_x(FP8, 1, a.K)));
   }
 }
 
