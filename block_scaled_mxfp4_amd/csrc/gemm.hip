@@ -481,7 +481,7 @@ __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return kspli
 // weights each step (TP8 decode FC1 -2..5 %, FC2 -6 %).  The rows get what is
 // left of a third of the LDS (kDecodeWavesPerSimd workgroups per CU) after
 // the scales and partial sums, 16 at most (FC1 at H = 3584: 3 rows).
-__host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8, bool fc1) {
+__host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8) {
   const uint32_t budget = 160u * 1024u / (uint32_t)kDecodeWavesPerSimd - 512u;
   const uint32_t used = decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit);
   const uint32_t left = budget > used ? budget - used : 0u;
