@@ -170,27 +170,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a)
   for (int l = tid; l < a.E_l; l += kRouteThreads) a.hist[(int64_t)blockIdx.x * a.E_l + l] = h[l];
 }
 
-// 2. one workgroup: per expert, exclusive prefix over blocks; expert scans;
-//    hist[b][l] becomes the first position of block b's pairs of expert l.
+// 2. one workgroup: per expert, exclusive prefix over blocks (hist[b][l]
+//    becomes the first position of block b's pairs of expert l within the
+//    expert's group), then the expert scans.  The blocks' counts are read 16
+//    at a time so their loads overlap (one dependent round trip per block
+//    cost ~0.35 us each).
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) {
   __shared__ int wave_sums[2][kRouteWaves];
   const int tid = threadIdx.x;
   int total = 0;
   if (tid < a.E_l) {
     int run = 0;
-    for (int b = 0; b < a.nblocks; ++b) {
-      const int c = a.hist[(int64_t)b * a.E_l + tid];
-      a.hist[(int64_t)b * a.E_l + tid] = run;
-      run += c;
+    for (int b0 = 0; b0 < a.nblocks; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        c[u] = b0 + u < a.nblocks ? a.hist[(int64_t)(b0 + u) * a.E_l + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < a.nblocks) a.hist[(int64_t)(b0 + u) * a.E_l + tid] = run;
+        run += c[u];
+      }
     }
     total = run;
   }
-  const int excl = scan_experts(a, total, wave_sums);
-  if (tid < a.E_l)
-    for (int b = 0; b < a.nblocks; ++b) a.hist[(int64_t)b * a.E_l + tid] += excl;
+  scan_experts(a, total, wave_sums);
 }
 
-// 3. per block: per-wave counts again, bases from hist[b][l], scatter.
+// 3. per block: per-wave counts again, bases from offsets[l] + hist[b][l],
+//    scatter.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a) {
   __shared__ int cnt[kRouteWaves][kMaxLocalExperts];
   const int tid = threadIdx.x;
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
   const int64_t j1 = j0 + a.chunk < a.TK ? j0 + a.chunk : a.TK;
   count_waves(a, j0, j1, cnt);
   for (int l = tid; l < a.E_l; l += kRouteThreads) {
-    int run = a.hist[(int64_t)blockIdx.x * a.E_l + l];
+    int run = a.offsets[l] + a.hist[(int64_t)blockIdx.x * a.E_l + l];
     for (int w = 0; w < kRouteWaves; ++w) {
       const int c = cnt[w][l];
       cnt[w][l] = run;

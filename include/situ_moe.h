@@ -107,7 +107,8 @@ typedef struct situ_moe_plan_t {
   uint64_t off_hs;              /* uint8 [T*k, I/32] E8M0 scales of h (w4a8) */
   uint64_t off_y;               /* FC2 output rows in perm order: float [T*k, H] (y_format 0), or
                                    fp16 [T*k, H] scaled by 2^(y_exp - 127) per 64 columns (y_format 1) */
-  uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms (route_blocks > 1) */
+  uint64_t off_route_hist;      /* int32 [route_blocks, E_l] per-block histograms, then each block's first position
+                                   within its expert's group (route_blocks > 1) */
   uint64_t off_tile_rows;       /* int32 [max_mtiles, 2] first and one-past-last perm position of each m-tile */
   uint64_t off_y_exp;           /* uint8 [T*k, ceil(H/64)] block exponents of y (y_format 1), row-major,
                                    inside the y region */
