@@ -328,8 +328,11 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
 //    are staged in LDS once per work item with 16-byte loads; one byte per
 //    lane per tile per step straight from memory costs a request each and
 //    measured ~30 % of the achievable stream rate;
-//  - the activation pieces travel in the same ring as the weights: they come
-//    from L2, but loading them just in time stalled every step on its latency;
+//  - the activation pieces are requested ahead of their use (loading them
+//    just in time stalled every step on its latency): w4a8 carries them in
+//    the weights' ring, w4a16 one step ahead in a ring of their own, from
+//    LDS when its m-tile is small enough to be staged there, else from L2,
+//    so that its weights can run further ahead;
 //  - partial sums meet in LDS in a fixed order (bitwise reproducible).
 // FC1 units are 32 gate + 32 up rows; FC2 units are 64 output rows.
 //
@@ -340,15 +343,33 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
 constexpr uint32_t kOob = 0x80000000u;   // an offset past every resource: reads 0
 
 // K steps in flight per wave, and the occupancy the register budget
-// targets (waves per SIMD).
+// targets (waves per SIMD): four for the w4a16 FC1 kernel with K split in
+// two or not at all, whose ring fits 128 registers (TP8 decode FC1 -1 %, EP8
+// -1.5 %), three elsewhere (FC2's deeper weight ring needs a few more, and a
+// four-way split's partial sums would spill).
 #ifndef SITU_DECODE_DEPTH
 #define SITU_DECODE_DEPTH 1
 #endif
 #ifndef SITU_DECODE_WAVES
 #define SITU_DECODE_WAVES 3
 #endif
+#ifndef SITU_DECODE_WAVES_FC1
+#define SITU_DECODE_WAVES_FC1 4
+#endif
 constexpr int kDecodeDepth = SITU_DECODE_DEPTH;
-constexpr int kDecodeWavesPerSimd = SITU_DECODE_WAVES;
+__host__ __device__ constexpr int decode_waves(bool fp8, bool fc1, int ksplit) {
+  return (!fp8 && fc1 && ksplit <= 2) ? SITU_DECODE_WAVES_FC1 : SITU_DECODE_WAVES;
+}
+// w4a16 weight steps in flight (the activation pieces stay one step ahead):
+// two for FC2 with its K split (EP8 decode FC2 -3 %), one elsewhere (the
+// unsplit three-step FC2 of TP8 decode measured 2 % slower with two, FC1 no
+// faster).
+#ifndef SITU_DECODE_WDEPTH_FC1
+#define SITU_DECODE_WDEPTH_FC1 1
+#endif
+#ifndef SITU_DECODE_WDEPTH_FC2
+#define SITU_DECODE_WDEPTH_FC2 2
+#endif
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -390,8 +411,8 @@ struct Step {
   uint32_t xs;
 };
 
-// w4a16 with the activation rows staged in LDS (XL and d.x_lds set): this
-// lane's piece of step j from there, zero past the group or past K.
+// w4a16 with the activation rows staged in LDS (d.x_lds set): this lane's
+// piece of step j from there, zero past the group or past K.
 __device__ __forceinline__ void load_x_lds(uint4 x[4], const DecodeGeo& d, int j) {
   const int kb = 4 * j + d.g;
   const bool ok = kb < d.nkb && d.x_row != kOob;
@@ -403,26 +424,32 @@ __device__ __forceinline__ void load_x_lds(uint4 x[4], const DecodeGeo& d, int j
   }
 }
 
-// XL: the activation rows may be staged in LDS (d.x_lds); their pieces then
-// travel in the same register ring, read from LDS when x_now (once the
-// staging barrier has passed) and by load_x_lds for the steps requested
-// before it.
-template <bool FP8, bool XL = false>
-__device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int j, bool x_now = true) {
+// The four weight tiles' pieces of step j (zero past K).
+__device__ __forceinline__ void load_w(uint4 w[4], const DecodeGeo& d, int j) {
   const int kb = 4 * j + d.g;
-  const bool kin = kb < d.nkb;
-  const uint32_t wo = kin ? d.w_row + (uint32_t)kb * 16u : kOob;
+  const uint32_t wo = kb < d.nkb ? d.w_row + (uint32_t)kb * 16u : kOob;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    b.w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
-  if constexpr (!FP8) {
-    if (!XL || d.x_lds == nullptr) {
-      const uint32_t xo = (kin && d.x_row != kOob) ? d.x_row + (uint32_t)kb * 64u : kOob;
+    w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
+}
+
+// w4a16: this lane's activation piece of step j from memory (zero past the
+// group or past K).
+__device__ __forceinline__ void load_x_mem(uint4 x[4], const DecodeGeo& d, int j) {
+  const int kb = 4 * j + d.g;
+  const uint32_t xo = (kb < d.nkb && d.x_row != kOob) ? d.x_row + (uint32_t)kb * 64u : kOob;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) b.x[c] = bload16(d.xr, xo + 16u * c);
-    } else if (x_now) {
-      load_x_lds(b.x, d, j);
-    }
+  for (int c = 0; c < 4; ++c) x[c] = bload16(d.xr, xo + 16u * c);
+}
+
+// Step j's weights and this lane's activation piece, both from memory.
+template <bool FP8>
+__device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int j) {
+  const int kb = 4 * j + d.g;
+  const bool kin = kb < d.nkb;
+  load_w(b.w, d, j);
+  if constexpr (!FP8) {
+    load_x_mem(b.x, d, j);
     b.xs = 127u;
   } else {
     // E4M3 operand: bytes 0..15 are K 128j + 16g .. +15 (block 4j + g/2), bytes
@@ -436,34 +463,41 @@ __device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int 
   }
 }
 
-template <bool FP8>
-__device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo& d, int j, f32x4 acc[4]) {
+// w4a16 step j: the weight pieces dequantized to bf16 by their E8M0 scales
+// (staged in LDS), times the activation piece.
+__device__ __forceinline__ void compute_w4a16(const uint4 w[4], const uint4 x[4], const DecodeGeo& d, int j,
+                                              f32x4 acc[4]) {
   const int kb = 4 * j + d.g;
   const bool kin = kb < d.nkb;
-  uint32_t sv[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sv[q] = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
-  if constexpr (!FP8) {
+  for (int q = 0; q < 4; ++q) {
+    const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u);
+    uint32_t wb[16];
+    fp4x8_to_bf16x8(w[q].x, sc, wb + 0);
+    fp4x8_to_bf16x8(w[q].y, sc, wb + 4);
+    fp4x8_to_bf16x8(w[q].z, sc, wb + 8);
+    fp4x8_to_bf16x8(w[q].w, sc, wb + 12);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float sc = e8m0_to_f32(sv[q]);
-      uint32_t wb[16];
-      fp4x8_to_bf16x8(b.w[q].x, sc, wb + 0);
-      fp4x8_to_bf16x8(b.w[q].y, sc, wb + 4);
-      fp4x8_to_bf16x8(b.w[q].z, sc, wb + 8);
-      fp4x8_to_bf16x8(b.w[q].w, sc, wb + 12);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const uint32_t xb[4] = {b.x[qq].x, b.x[qq].y, b.x[qq].z, b.x[qq].w};
-        acc[q] = mfma_bf16_16x16x32(wb + 4 * qq, xb, acc[q]);
-      }
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint32_t xb[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
+      acc[q] = mfma_bf16_16x16x32(wb + 4 * qq, xb, acc[q]);
     }
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo& d, int j, f32x4 acc[4]) {
+  if constexpr (!FP8) {
+    compute_w4a16(b.w, b.x, d, j, acc);
   } else {
+    const int kb = 4 * j + d.g;
+    const bool kin = kb < d.nkb;
     const uint32_t xb[8] = {b.x[0].x, b.x[0].y, b.x[0].z, b.x[0].w, b.x[1].x, b.x[1].y, b.x[1].z, b.x[1].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t av[4] = {b.w[q].x, b.w[q].y, b.w[q].z, b.w[q].w};
-      acc[q] = mfma_scale_fp4_fp8(av, xb, sv[q], b.xs, acc[q]);
+      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
+      acc[q] = mfma_scale_fp4_fp8(av, xb, sv, b.xs, acc[q]);
     }
   }
 }
@@ -479,17 +513,18 @@ __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return kspli
 // ring from LDS instead of every wave loading its lanes' pieces (mostly past
 // the group: decode m-tiles hold one or two tokens) from memory beside the
 // weights each step (TP8 decode FC1 -2..5 %, FC2 -6 %).  The rows get what is
-// left of a third of the LDS (kDecodeWavesPerSimd workgroups per CU) after
-// the scales and partial sums, 16 at most (FC1 at H = 3584: 3 rows).
-__host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8) {
-  const uint32_t budget = 160u * 1024u / (uint32_t)kDecodeWavesPerSimd - 512u;
+// left of the LDS share of one of the decode_waves() workgroups of a CU after
+// the scales and partial sums, 16 at most (FC1 at H = 3584: one row, FC2 at
+// I = 384: 16).
+__host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8, bool fc1) {
+  const uint32_t budget = 160u * 1024u / (uint32_t)decode_waves(fp8, fc1, ksplit) - 512u;
   const uint32_t used = decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit);
   const uint32_t left = budget > used ? budget - used : 0u;
   const int rows = (int)(left / ((uint32_t)K * 2u));
   return fp8 ? 0 : (rows < 16 ? rows : 16);
 }
-__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, int ksplit, int K) {
-  return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8) * (uint32_t)K * 2u;
+__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, bool fc1, int ksplit, int K) {
+  return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8, fc1) * (uint32_t)K * 2u;
 }
 __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb, uint32_t x_bytes) {
   return decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit) + x_bytes;
@@ -559,7 +594,7 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
 }
 
 template <bool FP8, bool FC1, int KSPLIT>
-__global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
   extern __shared__ __align__(16) uint8_t lds[];
   // wave-uniform values are made visibly uniform (readfirstlane, scalar
@@ -584,6 +619,7 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
   f32x4* red = reinterpret_cast<f32x4*>(lds + decode_lds_scales(UNITS_PER_WG, nkb));   // [4 waves][4][64]
   uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, nkb) + decode_lds_red(KSPLIT);
   constexpr bool XL = !FP8;                    // w4a16 may stage its activation rows
+  constexpr int DW = FC1 ? SITU_DECODE_WDEPTH_FC1 : (KSPLIT > 1 ? SITU_DECODE_WDEPTH_FC2 : 1);
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = w / n_wgn;
@@ -615,7 +651,7 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
       }
     }
     // w4a16 with few tokens: stage the m-tile's activation rows (16-byte loads)
-    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, nkb, K, FP8);   // uniform
+    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, nkb, K, FP8, FC1);   // uniform
     if constexpr (XL) {
       if (x_in_lds) {
         const int row_chunks = K / 8;               // K bf16 values / 16 bytes
@@ -637,7 +673,6 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
 
     DecodeGeo d;
     int n0 = 0, ntiles = 4;
-    Step<FP8> buf[kDecodeDepth + 1];
     if (active) {
       const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
       d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
@@ -673,35 +708,68 @@ __global__ __launch_bounds__(kGemmThreads, kDecodeWavesPerSimd) void decode_gemm
                           16u * (uint32_t)nkb);
         d.xs_row = (uint32_t)r * (uint32_t)nkb;
       }
-      // first kDecodeDepth steps of weights go out before the scale barrier
-#pragma unroll
-      for (int u = 0; u < kDecodeDepth; ++u)
-        if (u < my_steps) load_step<FP8, XL>(buf[u], d, j_begin + u, false);
     }
-    __syncthreads();   // staged scales (and activation rows) visible
     if constexpr (XL) {
-      if (active && d.x_lds != nullptr) {
+      // w4a16: weights DW steps ahead in a ring of DW + 1 register sets (the
+      // first DW requested before the staging barrier), the activation piece
+      // of the next step in a ring of two, read during the current step from
+      // LDS (staged m-tile) or from memory; NU steps per pass keep both ring
+      // indices compile-time constants
+      constexpr int NW = DW + 1, NU = NW % 2 == 0 ? NW : 2 * NW;
+      Step<FP8> wr[NW], xr[2];           // .w of the one ring, .x of the other
+      if (active) {
+#pragma unroll
+        for (int u = 0; u < DW; ++u)
+          if (u < my_steps) load_w(wr[u].w, d, j_begin + u);
+        if (!x_in_lds && my_steps > 0) load_x_mem(xr[0].x, d, j_begin);
+      }
+      __syncthreads();   // staged scales and activation rows visible
+      if (active) {
+        if (x_in_lds && my_steps > 0) load_x_lds(xr[0].x, d, j_begin);
+#pragma unroll 1
+        for (int i = 0; i < my_steps; i += NU) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int s = i + u;
+            if (s < my_steps) {
+              if (s + DW < my_steps) load_w(wr[(u + DW) % NW].w, d, j_begin + s + DW);
+              if (s + 1 < my_steps) {
+                if (x_in_lds) load_x_lds(xr[(u + 1) % 2].x, d, j_begin + s + 1);
+                else load_x_mem(xr[(u + 1) % 2].x, d, j_begin + s + 1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+              compute_w4a16(wr[u % NW].w, xr[u % 2].x, d, j_begin + s, acc);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+    } else {
+      // w4a8: the weights and activation pieces of the next kDecodeDepth
+      // steps are in flight while the current one is computed (the first
+      // ones requested before the staging barrier); a ring of kDecodeDepth + 1
+      // register buffers rotated by unrolling (compile-time indices);
+      // sched_barrier(0) keeps each prefetch ahead of its compute
+      constexpr int NB = kDecodeDepth + 1;
+      Step<FP8> buf[NB];
+      if (active) {
 #pragma unroll
         for (int u = 0; u < kDecodeDepth; ++u)
-          if (u < my_steps) load_x_lds(buf[u].x, d, j_begin + u);
+          if (u < my_steps) load_step<FP8>(buf[u], d, j_begin + u);
       }
-    }
-
-    if (active) {
-      // K loop over this wave's range: the weights of the next kDecodeDepth
-      // steps are in flight while the current one is computed; a ring of
-      // kDecodeDepth + 1 register buffers rotated by unrolling (compile-time
-      // indices); sched_barrier(0) keeps each prefetch ahead of its compute.
-      constexpr int NB = kDecodeDepth + 1;
-      for (int i = 0; i < my_steps; i += NB) {
+      __syncthreads();   // staged scales visible
+      if (active) {
+#pragma unroll 1
+        for (int i = 0; i < my_steps; i += NB) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          if (i + u < my_steps) {
-            if (i + u + kDecodeDepth < my_steps)
-              load_step<FP8, XL>(buf[(u + kDecodeDepth) % NB], d, j_begin + i + u + kDecodeDepth);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_step<FP8>(buf[u], d, j_begin + i + u, acc);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int u = 0; u < NB; ++u) {
+            if (i + u < my_steps) {
+              if (i + u + kDecodeDepth < my_steps)
+                load_step<FP8>(buf[(u + kDecodeDepth) % NB], d, j_begin + i + u + kDecodeDepth);
+              __builtin_amdgcn_sched_barrier(0);
+              compute_step<FP8>(buf[u], d, j_begin + i + u, acc);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
@@ -764,9 +832,9 @@ static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hi
 template <bool FP8, bool FC1>
 hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
   switch (decode_ksplit(a.K)) {
-    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32, decode_lds_x(FP8, 4, a.K)));
-    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32, decode_lds_x(FP8, 2, a.K)));
-    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32, decode_lds_x(FP8, 1, a.K)));
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32, decode_lds_x(FP8, FC1, 4, a.K)));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32, decode_lds_x(FP8, FC1, 2, a.K)));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32, decode_lds_x(FP8, FC1, 1, a.K)));
   }
 }
 

@@ -38,8 +38,11 @@ namespace {
 constexpr int kPfRows = 256;      // weight rows per work item
 constexpr int kPfTok = 64;        // token rows per work item (the m-tile)
 constexpr int kStageA = 16 * 1024;
-// activation tile: 2 DMA blocks of 8 tokens x 128 B (full cache lines),
-// 128 B apart so that the fragment reads of 16 tokens hit distinct banks
+// activation tile: 2 DMA blocks of 8 tokens x 128 B (full cache lines) with
+// 128 B between them.  On gfx950 that gap makes each 16-token fragment read a
+// two-way bank conflict (back to back they are conflict-free); the wide
+// kernel with the blocks back to back measured no faster (FC2 slower), so the
+// layout stays.
 constexpr int kTileB = 2 * (1024 + 128);
 constexpr int kStageB = 4 * kTileB;
 constexpr int kStageSA = kPfRows * 4;
