@@ -223,6 +223,27 @@ def test_layer_parity_small_w4a8_m128(name):
     assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
 
 
+# The 16-row decode kernels with K split in two on both GEMMs and both
+# activation sources of w4a16: m-tiles small enough to be staged in LDS (at
+# most 3 rows of FC1's 2048-wide input, 7 of FC2's) and larger ones read from
+# memory, with the weights two steps ahead in FC2.  Routing counts 26, 15, 21
+# and 34 give m-tiles of 16, 10, 15, 16, 5, 16, 16 and 2 rows.
+DECODE_SPLIT = dict(T=48, H=2048, I=2048, E_g=4, E_l=4, off=0, k=2, seed=40, skew=True)
+
+
+@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
+def test_layer_parity_decode_split_k(mode):
+    spec = S.spec_of(DECODE_SPLIT)
+    inp = S.generate(spec)
+    counts = M.route(M.topk_of(inp)[0], spec["off"], spec["E_l"])[0]
+    assert counts.tolist() == [26, 15, 21, 34]
+    tac = (0, 16) if mode == "w4a16" else (2, 18)
+    got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tac)
+    assert plan.block_m == 16
+    ref = oracle_out(inp, spec, mode=mode, keep=True)
+    parity(got, ref["out"], f"decode split-K {mode}", rounding_allowance(inp, spec, ref, mode))
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged", "wide"])
 def test_w4a8_prequantized_equals_library_quantized(name):
     spec = S.spec_of(SMALL[name])
