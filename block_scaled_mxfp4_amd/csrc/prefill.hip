@@ -792,8 +792,222 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// FC2 at short K (at most three 128-wide K steps, as at I = 384): a work item
+// is one 128-row m-tile x two 256-row n-tiles.  The m-tile's activations for
+// the whole of K are requested once per item and stay in LDS, and the second
+// n-tile's weights (256 rows x K) are requested while the first one is
+// multiplied, into the other of two buffers; one wait per item then covers
+// all of K instead of one per two-step stage.  TP8 prefill FC2 -8 % against
+// the two-stage kernel (one n-tile per item -5 %, three -7 %: with more the
+// work items are too few for an even spread over the CUs).  Waves, MFMA
+// tiles and the fp16 y epilogue are those of the wide kernel.
+namespace {
+
+constexpr int kSMaxSteps = 3;
+#ifndef SITU_FC2S_NT_PER_ITEM
+#define SITU_FC2S_NT_PER_ITEM 2
+#endif
+constexpr int kSNtPerItem = SITU_FC2S_NT_PER_ITEM;            // n-tiles per work item
+constexpr int kSH = 0;                                        // activations: [step][8 token tiles]
+constexpr int kSHS = kSH + kSMaxSteps * 8 * kWTileSw;         // [8 token tiles][step][16 tokens] scale dwords
+constexpr int kSW = kSHS + 8 * kSMaxSteps * 16 * 4;           // two weight buffers
+constexpr int kSWScales = kSMaxSteps * 16 * 1024;             // in a buffer: [step][16 tiles] of 16 rows x 64 B, then
+constexpr int kSWBuf = kSWScales + kSMaxSteps * kWRows * 4;   // [step][256 rows] scale dwords
+constexpr int kSLds = kSW + 2 * kSWBuf;                       // 161280 bytes
+static_assert(kSLds <= 160 * 1024, "short-K FC2 LDS");
+static_assert(8 * kWYScratch <= kSWBuf, "the y transpose fits a weight buffer");
+
+struct PsGeo {
+  v4i wr, sr, xr, xsr;
+  uint32_t b_row[2];   // activation rows of tokens 16*wave + l/8 (+8)
+  uint32_t sb_row;     // scale row of token 16*wave + l%16
+  int K, steps, nkb;
+};
+
+__device__ __forceinline__ PsGeo ps_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr) {
+  PsGeo d;
+  d.K = a.K;
+  d.steps = a.K / 128;
+  d.nkb = a.K / 32;
+  const size_t wexp = (size_t)a.N * (size_t)(a.K / 2);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * a.N * d.nkb, (uint32_t)(a.N * d.nkb));
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)a.K : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)a.K : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)d.nkb : kOobPf;
+  return d;
+}
+
+// This wave's token tile of the m-tile for every K step (the wide kernel's
+// swizzled layout), and its scale dwords.
+__device__ __forceinline__ void ps_issue_act(uint8_t* lds, const PsGeo& d, int w, int l) {
+  const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
+#pragma unroll
+  for (int s = 0; s < kSMaxSteps; ++s)
+    if (s < d.steps) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dma16(d.xr, lds_addr_of(lds + kSH + (8 * s + w) * kWTileSw + h * (1024 + 128)),
+              d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * s + chunk);
+    }
+  if (l < 16 * d.steps)   // lane l: step l / 16, token l % 16
+    dma4(d.xsr, lds_addr_of(lds + kSHS + w * (kSMaxSteps * 64)),
+         d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * (uint32_t)(l >> 4));
+}
+
+// This wave's two 16-row weight tiles of n-tile rows n0.. for every K step
+// (16 rows x 64 B per request, stored in lane order), and a share of the
+// n-tile's scale dwords.
+__device__ __forceinline__ void ps_issue_w(uint8_t* wb, const PsGeo& d, int N, int n0, int w, int l) {
+  const int r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = n0 + 16 * (2 * w + i) + r;
+    const uint32_t ar = row < N ? (uint32_t)row * (uint32_t)(d.K / 2) : kOobPf;
+#pragma unroll
+    for (int s = 0; s < kSMaxSteps; ++s)
+      if (s < d.steps)
+        dma16(d.wr, lds_addr_of(wb + (16 * s + 2 * w + i) * 1024),
+              ar == kOobPf ? kOobPf : ar + (uint32_t)(4 * s + g) * 16u);
+  }
+#pragma unroll
+  for (int q = w; q < 4 * kSMaxSteps; q += 8) {   // per step four blocks of 64 rows
+    const int s = q >> 2, blk = q & 3;
+    if (s < d.steps) {
+      const int row = n0 + 64 * blk + l;
+      dma4(d.sr, lds_addr_of(wb + kSWScales + s * 1024 + blk * 256),
+           row < N ? (uint32_t)row * (uint32_t)d.nkb + 4u * (uint32_t)s : kOobPf);
+    }
+  }
+}
+
+// K step s for one wave: 8 weight tiles x 2 token tiles of MFMAs, the reads
+// and MFMAs interleaved as in the wide kernel.
+__device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb, int s, int wn, int wm, int lane,
+                                           f32x4 acc[8][2]) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
+  uint4 blo[2], bhi[2];
+  uint32_t sb[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tile = 2 * wm + tt;
+    const uint8_t* row = lds + kSH + (8 * s + tile) * kWTileSw + rowoff;
+    blo[tt] = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
+    bhi[tt] = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ rr));
+    sb[tt] = lds[kSHS + tile * (kSMaxSteps * 64) + s * 64 + r * 4 + g];
+  }
+  uint4 av[8];
+  uint32_t sa[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tile = 8 * wn + i;
+    av[i] = *reinterpret_cast<const uint4*>(wb + (16 * s + tile) * 1024 + lane * 16);
+    sa[i] = wb[kSWScales + s * 1024 + (16 * tile + r) * 4 + g];
+  }
+  uint32_t bf[2][8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
+    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t lds[kSLds];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int steps = a.K / 128;
+  const int n_tiles = (a.N + kWRows - 1) / kWRows;
+  const int groups = (n_tiles + kSNtPerItem - 1) / kSNtPerItem;   // work items per m-tile
+  const cptr te = (cptr)a.tile_expert, tr = (cptr)a.tile_rows;
+  const int total = ((cptr)a.mtiles)[a.E_l] * groups;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
+  const int chunk = (total + 7) / 8;
+  const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+
+  // the y rows of the previous n-tile leave during the next one's K steps
+  bool pend = false;
+  PfItem px{0, 0, 0, 0};
+  YPend yp;
+  for (int it = i_begin + slot; it < i_end; it += per_xcd_wgs) {
+    const int m = it / groups, grp = it % groups;
+    PfItem x;
+    x.l = te[m];
+    x.nt = 0;
+    x.p0 = tr[2 * m];
+    x.p1 = tr[2 * m + 1];
+    const int nt0 = grp * kSNtPerItem, nt1 = min(n_tiles, nt0 + kSNtPerItem);
+    const PsGeo d = ps_geo(a, x, pf_act_rows<false>(a, x, wave_u, lane));
+    lds_barrier();                      // every wave is done with the previous item's LDS
+    ps_issue_act(lds, d, wave, lane);
+    ps_issue_w(lds + kSW, d, a.N, nt0 * kWRows, wave, lane);
+    for (int nt = nt0; nt < nt1; ++nt) {
+      const int b = (nt - nt0) & 1;
+      uint8_t* wb = lds + kSW + b * kSWBuf;
+      dma_barrier<0>();                 // activations and this n-tile's weights have landed everywhere
+      if (nt + 1 < nt1) ps_issue_w(lds + kSW + (b ^ 1) * kSWBuf, d, a.N, (nt + 1) * kWRows, wave, lane);
+      f32x4 acc[8][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kSMaxSteps; ++s) {
+        if (s < steps) {
+          if (pend) {                   // parts 0, 1, 2 at steps 0, 1, 2 (the last step takes the rest)
+            if (s == 0) pw_y16_store<0>(a, px, yp, wn, wm, lane);
+            if (s == min(1, steps - 1)) pw_y16_store<1>(a, px, yp, wn, wm, lane);
+            if (s == min(2, steps - 1)) pw_y16_store<2>(a, px, yp, wn, wm, lane);
+          }
+          ps_compute(lds, wb, s, wn, wm, lane, acc);
+        }
+      }
+      lds_barrier();                    // every wave is done reading wb: it holds the y transpose now
+      pw_y16_prepare(acc, lane, wb + wave * kWYScratch, yp);
+      px = x;
+      px.nt = nt;
+      pend = true;
+    }
+  }
+  if (pend) {
+    pw_y16_store<0>(a, px, yp, wn, wm, lane);
+    pw_y16_store<1>(a, px, yp, wn, wm, lane);
+    pw_y16_store<2>(a, px, yp, wn, wm, lane);
+  }
+}
+
 template <bool FC1>
 hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
+  if constexpr (!FC1) {
+    if (a.K % 128 == 0 && a.K <= 128 * kSMaxSteps) {     // the m-tile's activations fit beside two n-tiles
+      const int64_t work = (int64_t)max_mtiles * ((a.N + kWRows - 1) / kWRows + kSNtPerItem - 1) / kSNtPerItem;
+      int64_t grid = cus;                                    // one workgroup per CU
+      if (grid > work) grid = (work + 7) / 8 * 8;
+      if (grid <= 0) return hipSuccess;
+      hipLaunchKernelGGL(prefill_fc2_short_kernel, dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int n_tiles = FC1 ? a.N / 128 : (a.N + kWRows - 1) / kWRows;
   const int64_t work = (int64_t)max_mtiles * n_tiles;
   int64_t grid = cus;                                        // one workgroup per CU
