@@ -104,15 +104,6 @@ __device__ __forceinline__ f32x4 mfma_scale_fp4_fp8(const uint32_t a[4], const u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
 }
 
-// e^x in fp32 by the hardware 2^y of y = x*log2(e): relative error about
-// |y| * 2^-24 from the rounding of the product (below 4e-6 for |x| < 87,
-// where the result is a normal float) plus the hardware's own ~1 ulp.
-// Overflow gives +inf, underflow 0.
-__device__ __forceinline__ float exp_fast(float x) {
-  constexpr float kL2e = 1.44269502162933349609375f;     // log2(e) rounded to fp32
-  return __builtin_amdgcn_exp2f(x * kL2e);
-}
-
 // tanh(x) as a quotient n / d of fp32 values: x clamped to [-9, 9] (tanh(9)
 // is 1 in fp32), n = x P(x^2), d = Q(x^2) with P, Q of degree 4, fitted on
 // [0, 9] for the smallest largest relative error (reweighted least squares
@@ -130,23 +121,36 @@ __device__ __forceinline__ void tanh_nd(float x, float& n, float& d) {
   d = q;
 }
 
-// SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)] in fp32, rb = 1/b
-// and rlb = 1/lb precomputed per expert, as one quotient: the two tanh
-// quotients and sigmoid = 1 / (1 + e^-g) share a single reciprocal (one
-// exponential and one reciprocal per element).  Relative error below ~4e-6
-// over every input range (host emulation of these fp32 steps against
-// float64: 6e-7 for inputs of unit scale, 3.8e-6 at scale 30-100, where the
-// rounding of -g*log2(e) dominates): h feeds a rounding point (bf16, or MXFP8
-// whose E4M3 steps are 6-12 % apart), and an h this close to the exact value
-// flips a rounding decision only for elements within ~2^-18 of a rounding
-// boundary.  For g below about -76 the denominator overflows and h is 0 (the
-// exact value is below 1e-33).
-__device__ __forceinline__ float situ_act(float g, float u, float b, float lb, float rb, float rlb) {
+// SiTU(g, u) = [b*tanh(g/b)*sigmoid(g)] * [lb*tanh(u/lb)] of the alpha-scaled
+// accumulators g = ag*acc_g, u = au*acc_u, in fp32.  The per-expert constants
+// fold alpha, 1/beta and log2(e) into one multiplier per use, and the two
+// tanh quotients and sigmoid = 1 / (1 + e^-g) share a single reciprocal (one
+// exponential and one reciprocal per element).  situ_q leaves out the factor
+// b*lb (applied by situ_h, or folded into the MXFP8 block scale).  Relative
+// error below ~4e-6 over every input range (host emulation of these fp32
+// steps against float64: under 1e-6 for inputs of unit scale, 3.8e-6 at scale
+// 30-100, where the rounding of the exponent's argument dominates): h feeds a
+// rounding point (bf16, or MXFP8 whose E4M3 steps are 6-12 % apart), and an h
+// this close to the exact value flips a rounding decision only for elements
+// within ~2^-18 of a rounding boundary.  For g below about -76 the
+// denominator overflows and h is 0 (the exact value is below 1e-33).
+struct SituK {
+  float kg, ke, ku, blb;   // ag/b, -ag*log2(e), au/lb, b*lb
+};
+__device__ __forceinline__ SituK situ_consts(float ag, float au, float b, float lb) {
+  constexpr float kL2e = 1.44269502162933349609375f;     // log2(e) rounded to fp32
+  return SituK{ag * (1.0f / b), -(ag * kL2e), au * (1.0f / lb), b * lb};
+}
+__device__ __forceinline__ float situ_q(float acc_g, float acc_u, const SituK& k) {
   float n1, d1, n3, d3;
-  tanh_nd(g * rb, n1, d1);
-  tanh_nd(u * rlb, n3, d3);
-  const float den = (d1 * d3) * (1.0f + exp_fast(-g));
-  return ((b * n1) * (lb * n3)) * __builtin_amdgcn_rcpf(den);
+  tanh_nd(acc_g * k.kg, n1, d1);
+  tanh_nd(acc_u * k.ku, n3, d3);
+  const float e = __builtin_amdgcn_exp2f(acc_g * k.ke);   // e^-g (hardware 2^y, ~1 ulp)
+  const float t = d1 * d3;
+  return (n1 * n3) * __builtin_amdgcn_rcpf(__builtin_fmaf(t, e, t));
+}
+__device__ __forceinline__ float situ_h(float acc_g, float acc_u, const SituK& k) {
+  return situ_q(acc_g, acc_u, k) * k.blb;
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

@@ -149,8 +149,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
     // epilogue: alpha, SiTU, rounding point R1, store h in perm order
     const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
     const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
-    const float b = a.beta[l], lb = a.lbeta[l];
-    const float rb = 1.0f / b, rlb = 1.0f / lb;
+    const SituK sk = situ_consts(ag, au, a.beta[l], a.lbeta[l]);
 #pragma unroll
     for (int tt = 0; tt < TOKT; ++tt) {
       const int64_t p = p0 + 16 * tt + r;
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          hv[half][i] = situ_act(ag * acc[half][tt][i], au * acc[2 + half][tt][i], b, lb, rb, rlb);
+          hv[half][i] = situ_h(acc[half][tt][i], acc[2 + half][tt][i], sk);
       if constexpr (!FP8) {
         if (valid[tt]) {
           uint16_t* hrow = static_cast<uint16_t*>(a.out) + p * I + n0 + 4 * g;
@@ -542,15 +541,14 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
     const int I = a.N;
     const float ag = a.alpha_g ? __builtin_bit_cast(float, ((cptr)a.alpha_g)[l]) : 1.0f;
     const float au = a.alpha_u ? __builtin_bit_cast(float, ((cptr)a.alpha_u)[l]) : 1.0f;
-    const float bb = __builtin_bit_cast(float, ((cptr)a.beta)[l]);
-    const float lb = __builtin_bit_cast(float, ((cptr)a.lbeta)[l]);
-    const float rb = 1.0f / bb, rlb = 1.0f / lb;
+    const SituK sk = situ_consts(ag, au, __builtin_bit_cast(float, ((cptr)a.beta)[l]),
+                                 __builtin_bit_cast(float, ((cptr)a.lbeta)[l]));
     float hv[2][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        hv[half][i] = situ_act(ag * acc[half][i], au * acc[2 + half][i], bb, lb, rb, rlb);
+        hv[half][i] = situ_h(acc[half][i], acc[2 + half][i], sk);
     if constexpr (!FP8) {
       if (valid) {
         uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;

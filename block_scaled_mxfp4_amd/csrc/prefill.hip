@@ -273,9 +273,8 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     const cptr ag_p = (cptr)a.alpha_g, au_p = (cptr)a.alpha_u;
     const float ag = a.alpha_g ? __builtin_bit_cast(float, ag_p[x.l]) : 1.0f;
     const float au = a.alpha_u ? __builtin_bit_cast(float, au_p[x.l]) : 1.0f;
-    const float bb = __builtin_bit_cast(float, ((cptr)a.beta)[x.l]);
-    const float lb = __builtin_bit_cast(float, ((cptr)a.lbeta)[x.l]);
-    const float rb = 1.0f / bb, rlb = 1.0f / lb;
+    const SituK sk = situ_consts(ag, au, __builtin_bit_cast(float, ((cptr)a.beta)[x.l]),
+                                 __builtin_bit_cast(float, ((cptr)a.lbeta)[x.l]));
     const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(TOK * I));
     const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
 #pragma unroll
@@ -284,33 +283,52 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
       const bool valid = x.p0 + pr < x.p1;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {          // two 32-column MXFP8 blocks per wave
-        float hv[2][4];
+        // h = q * b*lb with q = situ_q: the block maximum of |h| is b*lb times
+        // that of |q| (rounding is monotone), and h * 2^sh is q * (b*lb * 2^sh)
+        // in one product, exact whenever the block's scale leaves the elements
+        // that get a nonzero E4M3 code in fp32's normal range (sh <= 108);
+        // other blocks (all zero, or below 2^-100) take h and then 2^sh
+        float qv[2][4];
         float amax = 0.0f;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 2 * blk + h2;
-            hv[h2][e] = situ_act(ag * acc[i][tt][e], au * acc[4 + i][tt][e], bb, lb, rb, rlb);
-            amax = fmaxf(amax, fabsf(hv[h2][e]));
+            qv[h2][e] = situ_q(acc[i][tt][e], acc[4 + i][tt][e], sk);
+            amax = fmaxf(amax, fabsf(qv[h2][e]));
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
         const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
-        const uint32_t code = e8m0_code_for_e4m3(amax);
+        const uint32_t code = e8m0_code_for_e4m3(amax * sk.blb);
         const int sh = 127 - (int)code;
+        // rows past the group are not stored: their blocks do not matter
+        const bool direct = __builtin_amdgcn_ballot_w64(valid && sh > 108) == 0;   // uniform
         // E4M3 codes by the hardware conversion (round to nearest even) of
         // the scaled values clamped to +-448, which gives the MX rule's
         // saturating codes; a negative value that rounds to zero keeps its
         // sign (code 0x80, the value zero)
+        float sv[2][4];
+        if (direct) {
+          const float scl = __builtin_ldexpf(sk.blb, sh);
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[h2][e] = qv[h2][e] * scl;
+        } else {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[h2][e] = __builtin_ldexpf(qv[h2][e] * sk.blb, sh);
+        }
         uint32_t packed[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          float sv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[e] = fminf(fmaxf(__builtin_ldexpf(hv[h2][e], sh), -448.0f), 448.0f);
-          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sv[0], sv[1], 0, false);
-          packed[h2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv[2], sv[3], lo, true);
+          for (int e = 0; e < 4; ++e) sv[h2][e] = fminf(fmaxf(sv[h2][e], -448.0f), 448.0f);
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sv[h2][0], sv[h2][1], 0, false);
+          packed[h2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv[h2][2], sv[h2][3], lo, true);
         }
         const uint32_t ho = valid ? (uint32_t)(pr * I + col0 + 4 * g) : kOobPf;
         st4(hr, ho, packed[0]);
