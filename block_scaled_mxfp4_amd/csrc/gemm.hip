@@ -502,7 +502,8 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 }
 
 // Dynamic LDS of a decode launch: staged scales of the workgroup's units,
-// then the split-K partial sums.
+// then one region that holds the staged activation rows during the K loop
+// and the split-K partial sums after it.
 __host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int nkb) {
   return (uint32_t)(units_per_wg * 64 * nkb + 15) / 16u * 16u;
 }
@@ -513,11 +514,10 @@ __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return kspli
 // the group: decode m-tiles hold one or two tokens) from memory beside the
 // weights each step (TP8 decode FC1 -2..5 %, FC2 -6 %).  The rows get what is
 // left of the LDS share of one of the decode_waves() workgroups of a CU after
-// the scales and partial sums, 16 at most (FC1 at H = 3584: one row, FC2 at
-// I = 384: 16).
+// the scales, 16 at most (FC1 at H = 3584: three rows, FC2 at I = 384: 16).
 __host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8, bool fc1) {
   const uint32_t budget = 160u * 1024u / (uint32_t)decode_waves(fp8, fc1, ksplit) - 512u;
-  const uint32_t used = decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit);
+  const uint32_t used = decode_lds_scales(4 / ksplit, nkb);
   const uint32_t left = budget > used ? budget - used : 0u;
   const int rows = (int)(left / ((uint32_t)K * 2u));
   return fp8 ? 0 : (rows < 16 ? rows : 16);
@@ -526,7 +526,7 @@ __host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, bool fc1, int kspl
   return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8, fc1) * (uint32_t)K * 2u;
 }
 __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb, uint32_t x_bytes) {
-  return decode_lds_scales(4 / ksplit, nkb) + decode_lds_red(ksplit) + x_bytes;
+  return decode_lds_scales(4 / ksplit, nkb) + (x_bytes > decode_lds_red(ksplit) ? x_bytes : decode_lds_red(ksplit));
 }
 
 // Decode epilogue of one wave's 16-row group: FC1 applies alpha and SiTU and
@@ -614,8 +614,9 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
   const int j_begin = min(steps, ks * per);
   const int j_end = min(steps, j_begin + per);
   const int my_steps = j_end - j_begin;
-  f32x4* red = reinterpret_cast<f32x4*>(lds + decode_lds_scales(UNITS_PER_WG, nkb));   // [4 waves][4][64]
-  uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, nkb) + decode_lds_red(KSPLIT);
+  // the activation rows during the K loop, then the partial sums [4 waves][4][64]
+  uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, nkb);
+  f32x4* red = reinterpret_cast<f32x4*>(x_stage);
   constexpr bool XL = !FP8;                    // w4a16 may stage its activation rows
   constexpr int DW = FC1 ? SITU_DECODE_WDEPTH_FC1 : (KSPLIT > 1 ? SITU_DECODE_WDEPTH_FC2 : 1);
 
@@ -776,6 +777,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
     // split-K reduction in a fixed order
     bool lead = active;
     if constexpr (KSPLIT > 1) {
+      if (XL && x_in_lds) __syncthreads();   // uniform: every wave is done with the staged rows
       if (active && ks != 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) red[(wave * 4 + q) * kWave + lane] = acc[q];

@@ -225,7 +225,7 @@ def test_layer_parity_small_w4a8_m128(name):
 
 # The 16-row decode kernels with K split in two on both GEMMs and both
 # activation sources of w4a16: m-tiles small enough to be staged in LDS (at
-# most 3 rows of FC1's 2048-wide input, 7 of FC2's) and larger ones read from
+# most 7 rows of FC1's 2048-wide input, 11 of FC2's) and larger ones read from
 # memory, with the weights two steps ahead in FC2.  Routing counts 26, 15, 21
 # and 34 give m-tiles of 16, 10, 15, 16, 5, 16, 16 and 2 rows.
 DECODE_SPLIT = dict(T=48, H=2048, I=2048, E_g=4, E_l=4, off=0, k=2, seed=40, skew=True)
