@@ -49,8 +49,11 @@ def _log(msg):
 
 
 def algorithmic_work(spec, counts, tokens_used, y_format=0):
-    """Bytes and flops the layer must move / compute, per stage.
-    y_format 1: y is fp16 with one exponent byte per 64 columns."""
+    """Bytes and flops the layer must move / compute, per stage: every active
+    expert's packed E2M1 weights with their E8M0 scales, each used token's
+    input row as the kernel reads it, h and y once each, and 2 flops per
+    multiply-add of the two contractions.  y_format 1: y is fp16 with one
+    exponent byte per 64 columns."""
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
     counts = np.asarray(counts, np.int64)
     A = int(np.count_nonzero(counts))
