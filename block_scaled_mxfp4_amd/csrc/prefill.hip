@@ -265,7 +265,7 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
 template <bool FC1, int TOK = kPfTok>
 __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
-                                            int wave, int lane, uint8_t* scratch) {
+                                            int wave, int lane, uint8_t* scratch, int ntt = 2) {
   const int r = lane & 15, g = lane >> 4;
   const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
   if constexpr (FC1) {
@@ -279,6 +279,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      if (tt >= ntt) break;                          // uniform: a tile of padding rows only
       const int pr = 32 * wm + 16 * tt + r;          // row within the m-tile
       const bool valid = x.p0 + pr < x.p1;
 #pragma unroll
@@ -562,7 +563,54 @@ __device__ __forceinline__ void pw_issue(uint32_t st, const PwGeo& d, int J) {
   }
 }
 
-// K step s of a stage for one wave: 8 weight tiles x 2 token tiles of MFMAs.
+// The MFMAs of one K step (8 weight tiles x NTT token tiles) and their
+// interleave with the step's LDS reads: the token fragments and the first
+// weight tiles' reads, then each pair of MFMAs followed by more reads, so
+// only the first reads' latency precedes the MFMAs (all reads first measured
+// 7 % slower on FC1).  NTT = 2: 22 reads, 16 MFMAs; NTT = 1: 19 and 8.
+template <int NTT>
+__device__ __forceinline__ void pw_mfmas(const uint4 blo[2], const uint4 bhi[2], const uint32_t sb[2],
+                                         const uint4 av[8], const uint32_t sa[8], f32x4 acc[8][2]) {
+  uint32_t bf[2][8];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
+    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
+  }
+  if constexpr (NTT == 2) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  } else {   // one MFMA per weight tile: the reads run four tiles ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+}
+
+// Token tiles of a wave's 32 rows that hold any row of the group (0, 1 or 2):
+// the others are padding of the group's last m-tile, whose MFMAs, and FC1
+// epilogue, are skipped (their rows are never stored).
+__device__ __forceinline__ int pw_active_tiles(const PfItem& x, int wm) {
+  const int left = x.p1 - (x.p0 + 32 * wm);
+  return left <= 0 ? 0 : (left <= 16 ? 1 : 2);
+}
+
+// K step s of a stage for one wave: 8 weight tiles x NTT token tiles of MFMAs.
+template <int NTT>
 __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, int wn, int wm, int lane,
                                            f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4, rr = r & 7;
@@ -570,7 +618,7 @@ __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, i
   uint4 blo[2], bhi[2];
   uint32_t sb[2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < NTT; ++tt) {
     const int tile = 2 * wm + tt;
     const uint8_t* row = st + kWStB + (8 * s + tile) * kWTileSw + rowoff;
     blo[tt] = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
@@ -585,29 +633,7 @@ __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, i
     av[i] = *reinterpret_cast<const uint4*>(st + kWStA + tile * kWTileSw + rowoff + 16 * ((4 * s + g) ^ rr));
     sa[i] = st[kWStSA + s * 1024 + (16 * tile + r) * 4 + g];
   }
-  uint32_t bf[2][8];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
-    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
-  }
-  // the token fragments and the first two weight tiles' reads, then each
-  // weight tile's MFMA pair followed by the reads of the tile two ahead, so
-  // only the first reads' latency precedes the MFMAs (all 22 reads first
-  // measured 7 % slower on FC1)
-  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  pw_mfmas<NTT>(blo, bhi, sb, av, sa, acc);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -757,6 +783,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
     f32x4 acc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ntt = pw_active_tiles(cur, wm);   // uniform per wave
     for (int J0 = 0; J0 < n_st; J0 += 2) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -775,11 +802,15 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
           }
           if (J + 1 < n_st) pw_issue(lds_addr_of(u ? st0 : st1), d, J + 1);
           const uint8_t* stc = u ? st1 : st0;
-          pw_compute(stc, 0, FC1, wn, wm, lane, acc);
+          if (ntt == 2) pw_compute<2>(stc, 0, FC1, wn, wm, lane, acc);
+          else if (ntt == 1) pw_compute<1>(stc, 0, FC1, wn, wm, lane, acc);
           if constexpr (!FC1) {
             if (pend && J == 0 && n_st < 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
           }
-          if (2 * J + 1 < steps) pw_compute(stc, 1, FC1, wn, wm, lane, acc);
+          if (2 * J + 1 < steps) {
+            if (ntt == 2) pw_compute<2>(stc, 1, FC1, wn, wm, lane, acc);
+            else if (ntt == 1) pw_compute<1>(stc, 1, FC1, wn, wm, lane, acc);
+          }
         }
       }
     }
@@ -795,7 +826,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
     }
     // the second stage is free for FC2's output transpose
     if constexpr (FC1) {
-      pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr);
+      pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr, ntt);
     } else {
       pw_y16_prepare(acc, lane, st1 + wave * kWYScratch, yp);
       px = cur;
@@ -902,8 +933,9 @@ __device__ __forceinline__ void ps_issue_w(uint8_t* wb, const PsGeo& d, int N, i
   }
 }
 
-// K step s for one wave: 8 weight tiles x 2 token tiles of MFMAs, the reads
+// K step s for one wave: 8 weight tiles x NTT token tiles of MFMAs, the reads
 // and MFMAs interleaved as in the wide kernel.
+template <int NTT>
 __device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb, int s, int wn, int wm, int lane,
                                            f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4, rr = r & 7;
@@ -911,7 +943,7 @@ __device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb
   uint4 blo[2], bhi[2];
   uint32_t sb[2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < NTT; ++tt) {
     const int tile = 2 * wm + tt;
     const uint8_t* row = lds + kSH + (8 * s + tile) * kWTileSw + rowoff;
     blo[tt] = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
@@ -926,25 +958,7 @@ __device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb
     av[i] = *reinterpret_cast<const uint4*>(wb + (16 * s + tile) * 1024 + lane * 16);
     sa[i] = wb[kSWScales + s * 1024 + (16 * tile + r) * 4 + g];
   }
-  uint32_t bf[2][8];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    bf[tt][0] = blo[tt].x; bf[tt][1] = blo[tt].y; bf[tt][2] = blo[tt].z; bf[tt][3] = blo[tt].w;
-    bf[tt][4] = bhi[tt].x; bf[tt][5] = bhi[tt].y; bf[tt][6] = bhi[tt].z; bf[tt][7] = bhi[tt].w;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i], sb[tt], acc[i][tt]);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  pw_mfmas<NTT>(blo, bhi, sb, av, sa, acc);
 }
 
 }  // namespace
@@ -977,6 +991,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
     x.p0 = tr[2 * m];
     x.p1 = tr[2 * m + 1];
     const int nt0 = grp * kSNtPerItem, nt1 = min(n_tiles, nt0 + kSNtPerItem);
+    const int ntt = pw_active_tiles(x, wm);   // uniform per wave
     const PsGeo d = ps_geo(a, x, pf_act_rows<false>(a, x, wave_u, lane));
     lds_barrier();                      // every wave is done with the previous item's LDS
     ps_issue_act(lds, d, wave, lane);
@@ -997,7 +1012,8 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
             if (s == min(1, steps - 1)) pw_y16_store<1>(a, px, yp, wn, wm, lane);
             if (s == min(2, steps - 1)) pw_y16_store<2>(a, px, yp, wn, wm, lane);
           }
-          ps_compute(lds, wb, s, wn, wm, lane, acc);
+          if (ntt == 2) ps_compute<2>(lds, wb, s, wn, wm, lane, acc);
+          else if (ntt == 1) ps_compute<1>(lds, wb, s, wn, wm, lane, acc);
         }
       }
       lds_barrier();                    // every wave is done reading wb: it holds the y transpose now
