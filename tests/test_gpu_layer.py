@@ -244,6 +244,44 @@ def test_layer_parity_decode_split_k(mode):
     parity(got, ref["out"], f"decode split-K {mode}", rounding_allowance(inp, spec, ref, mode))
 
 
+# Groups whose sizes sit on and around the m-tile boundaries (16, 17, 32, 33,
+# 48, 64, 65 and 125 rows): the 128-row kernels skip the 16-token tiles of a
+# wave that hold no row of the group, so their last m-tiles end in every
+# position relative to the waves' 32-row and the MFMAs' 16-row tiles.  I = 256
+# takes the short-K FC2 kernel in the 128-row tactic, I = 512 the two-stage one.
+BOUNDARY_COUNTS = [16, 17, 32, 33, 48, 64, 65, 125]
+
+
+def boundary_routing(inp, seed):
+    """Top-2 ids giving expert e exactly BOUNDARY_COUNTS[e] pairs, the two
+    slots of a token distinct, tokens in a seeded random order."""
+    ids = np.repeat(np.arange(len(BOUNDARY_COUNTS)), BOUNDARY_COUNTS)
+    T = len(ids) // 2
+    pair = np.stack([ids[:T], ids[T:][::-1]], axis=1)
+    for i in np.nonzero(pair[:, 0] == pair[:, 1])[0]:   # swap a clash with a row that takes it
+        for j in range(T):
+            if pair[j, 1] != pair[i, 0] and pair[i, 1] != pair[j, 0] and pair[j, 0] != pair[j, 1]:
+                pair[[i, j], 1] = pair[[j, i], 1]
+                break
+    rng = np.random.default_rng(seed)
+    out = dict(inp)
+    out["topk_ids"] = pair[rng.permutation(T)].astype(np.int32)
+    return out
+
+
+@pytest.mark.parametrize("I,mode,tactic", [(256, "w4a8", (4, 20)), (512, "w4a8", (4, 20)), (256, "w4a8", (3, 19)),
+                                           (256, "w4a16", (0, 16)), (256, "w4a8", (2, 18))])
+def test_layer_parity_group_boundaries(I, mode, tactic):
+    spec = S.spec_of(dict(T=200, H=256, I=I, E_g=8, E_l=8, off=0, k=2, seed=45))
+    inp = boundary_routing(S.generate(spec), 46)
+    counts = M.route(inp["topk_ids"], 0, 8)[0]
+    assert counts.tolist() == BOUNDARY_COUNTS
+    assert np.all(inp["topk_ids"][:, 0] != inp["topk_ids"][:, 1])
+    got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tactic)
+    ref = oracle_out(inp, spec, mode=mode, keep=True)
+    parity(got, ref["out"], f"group boundaries I={I} {mode} {tactic}", rounding_allowance(inp, spec, ref, mode))
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged", "wide"])
 def test_w4a8_prequantized_equals_library_quantized(name):
     spec = S.spec_of(SMALL[name])
