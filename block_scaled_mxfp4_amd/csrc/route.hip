@@ -36,15 +36,25 @@ __device__ __forceinline__ int local_expert_of(const RouteArgs& a, int64_t j) {
 }
 
 // Pairs [j0, j1) are split into kRouteWaves contiguous sub-chunks, one per
-// wave, in order.  Each wave counts its sub-chunk into cnt[wave][l].
-__device__ void count_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts]) {
+// wave, in order.  Each wave counts its sub-chunk into cnt[wave][l]; the
+// local experts of a lane's first kRouteKept pairs stay in lv[] for the
+// scatter (a sub-chunk of blocks of up to 4096 pairs needs no reload).
+constexpr int kRouteKept = 4;
+__device__ void count_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts],
+                            int lv[kRouteKept]) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   for (int i = tid; i < kRouteWaves * kMaxLocalExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const int64_t chunk = (j1 - j0 + kRouteWaves - 1) / kRouteWaves;
   const int64_t w0 = j0 + (int64_t)wave * chunk;
   const int64_t w1 = w0 + chunk < j1 ? w0 + chunk : j1;
-  for (int64_t base = w0; base < w1; base += kWave) {
+#pragma unroll
+  for (int it = 0; it < kRouteKept; ++it) {
+    const int64_t j = w0 + (int64_t)it * kWave + lane;
+    lv[it] = j < w1 ? local_expert_of(a, j) : -1;
+    if (lv[it] >= 0) atomicAdd(&cnt[wave][lv[it]], 1);
+  }
+  for (int64_t base = w0 + (int64_t)kRouteKept * kWave; base < w1; base += kWave) {
     const int64_t j = base + lane;
     if (j < w1) {
       const int l = local_expert_of(a, j);
@@ -57,7 +67,8 @@ __device__ void count_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cn
 // cnt[w][l] holds the first position of wave w's pairs of expert l; walk the
 // sub-chunks again 64 pairs at a time and place each pair at base + its rank
 // among the lanes holding the same expert (ballots over the key bits).
-__device__ void scatter_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts]) {
+__device__ void scatter_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*cnt)[kMaxLocalExperts],
+                              const int lv[kRouteKept]) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t chunk = (j1 - j0 + kRouteWaves - 1) / kRouteWaves;
   const int64_t w0 = j0 + (int64_t)wave * chunk;
@@ -65,10 +76,17 @@ __device__ void scatter_waves(const RouteArgs& a, int64_t j0, int64_t j1, int (*
   int nbits = 0;
   while ((1 << nbits) < a.E_l) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int64_t base = w0; base < w1; base += kWave) {
+  int it = 0;
+  for (int64_t base = w0; base < w1; base += kWave, ++it) {
     const int64_t j = base + lane;
     const bool in = j < w1;
-    const int l = in ? local_expert_of(a, j) : -1;
+    int l = -1;
+    if (it < kRouteKept) {             // uniform; the register copy, selected without indexing
+#pragma unroll
+      for (int q = 0; q < kRouteKept; ++q) l = it == q ? lv[q] : l;
+    } else {
+      l = in ? local_expert_of(a, j) : -1;
+    }
     const bool loc = l >= 0;
     uint64_t eq = __ballot(loc);
     for (int b = 0; b < nbits; ++b) {
@@ -132,7 +150,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int offs[kMaxLocalExperts];
   __shared__ int wave_sums[2][kRouteWaves];
   const int tid = threadIdx.x;
-  count_waves(a, 0, a.TK, cnt);
+  int lv[kRouteKept];
+  count_waves(a, 0, a.TK, cnt, lv);
   // per expert: exclusive scan over waves, total
   int total = 0;
   for (int l = tid; l < a.E_l; l += kRouteThreads) {
@@ -150,7 +169,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __syncthreads();
   for (int i = tid; i < kRouteWaves * a.E_l; i += kRouteThreads) cnt[i / a.E_l][i % a.E_l] += offs[i % a.E_l];
   __syncthreads();
-  scatter_waves(a, 0, a.TK, cnt);
+  scatter_waves(a, 0, a.TK, cnt, lv);
 }
 
 // Large batches, three launches.  Block b owns the pairs [b*C, (b+1)*C).
@@ -205,7 +224,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
   const int tid = threadIdx.x;
   const int64_t j0 = (int64_t)blockIdx.x * a.chunk;
   const int64_t j1 = j0 + a.chunk < a.TK ? j0 + a.chunk : a.TK;
-  count_waves(a, j0, j1, cnt);
+  int lv[kRouteKept];
+  count_waves(a, j0, j1, cnt, lv);
   for (int l = tid; l < a.E_l; l += kRouteThreads) {
     int run = a.offsets[l] + a.hist[(int64_t)blockIdx.x * a.E_l + l];
     for (int w = 0; w < kRouteWaves; ++w) {
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     }
   }
   __syncthreads();
-  scatter_waves(a, j0, j1, cnt);
+  scatter_waves(a, j0, j1, cnt, lv);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
