@@ -27,6 +27,9 @@ __all__ = [
 
 ACT_W4A16, ACT_W4A8 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
+ACTIVATIONS = {"situ": 0, "swiglu": 1, "swiglu_bias": 2}
+WEIGHT_FORMATS = {"mxfp4": 0, "nvfp4": 1}
+ABI_VERSION = 2
 STATUS_NAMES = {0: "SITU_OK", 1: "SITU_E_NULL_ARG", 2: "SITU_E_BAD_SHAPE", 3: "SITU_E_UNSUPPORTED",
                 4: "SITU_E_MISSING_SCALE", 5: "SITU_E_DEVICE", 6: "SITU_E_WORKSPACE", 7: "SITU_E_LAUNCH"}
 
@@ -48,7 +51,7 @@ class SituMoeProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden_size", "intermediate_size", "num_experts", "local_expert_offset",
         "local_num_experts", "top_k", "act_mode", "act_prequantized", "topk_packed", "out_dtype",
-        "tactic_fc1", "tactic_fc2")]
+        "tactic_fc1", "tactic_fc2", "activation", "weight_format")]
 
 
 class SituMoePlan(ctypes.Structure):
@@ -68,7 +71,8 @@ class SituMoeTensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "hidden_states", "hidden_states_scale", "topk_ids", "topk_weights", "topk_packed",
         "w1", "w1_scale", "w2", "w2_scale", "situ_beta", "situ_linear_beta", "alpha_gate",
-        "alpha_up", "out")]
+        "alpha_up", "out", "swiglu_alpha", "swiglu_beta", "alpha_down", "gate_up_lora_delta",
+        "activation_lora_input")]
 
 
 _LIB = None
@@ -85,6 +89,9 @@ def load():
     if not os.path.exists(path):
         raise SituMoeError(5, f"{path} is not built; run `python -m block_scaled_mxfp4_amd.build`")
     lib = ctypes.CDLL(path)
+    lib.situ_moe_abi_version.restype = ctypes.c_int32
+    if lib.situ_moe_abi_version() != ABI_VERSION:
+        raise SituMoeError(5, f"{path} has ABI {lib.situ_moe_abi_version()}, this binding needs {ABI_VERSION}; rebuild it")
     P = ctypes.POINTER
     c_int, c_i64, c_u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
     sig = {
@@ -114,10 +121,13 @@ def _check(status):
 
 
 def _stream(stream):
-    if stream is not None:
-        return ctypes.c_void_p(int(stream))
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    """A hipStream_t from a torch.cuda.Stream, a raw handle (int), or None
+    (torch's current stream)."""
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    handle = getattr(stream, "cuda_stream", stream)
+    return ctypes.c_void_p(int(handle))
 
 
 # ------------------------------------------------------------------ C names
@@ -220,18 +230,21 @@ def _need(t, dtype, shape, name):
 
 def make_problem(*, num_tokens, hidden_size, intermediate_size, num_experts, local_expert_offset,
                  local_num_experts, top_k, act_mode="w4a16", act_prequantized=False, topk_packed=False,
-                 out_dtype="f32", tactic=(-1, -1)):
+                 out_dtype="f32", tactic=(-1, -1), activation="situ", weight_format="mxfp4"):
     act = {"w4a16": ACT_W4A16, "w4a8": ACT_W4A8}[act_mode] if isinstance(act_mode, str) else int(act_mode)
     od = {"f32": OUT_F32, "float32": OUT_F32, "bf16": OUT_BF16, "bfloat16": OUT_BF16}[out_dtype] \
         if isinstance(out_dtype, str) else int(out_dtype)
+    ak = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    wf = WEIGHT_FORMATS[weight_format] if isinstance(weight_format, str) else int(weight_format)
     return SituMoeProblem(num_tokens, hidden_size, intermediate_size, num_experts, local_expert_offset,
                           local_num_experts, top_k, act, int(bool(act_prequantized)), int(bool(topk_packed)),
-                          od, int(tactic[0]), int(tactic[1]))
+                          od, int(tactic[0]), int(tactic[1]), ak, wf)
 
 
 def make_tensors(problem, *, hidden_states, hidden_states_scale=None, topk_ids=None, topk_weights=None,
-                 topk_packed=None, w1, w1_scale, w2, w2_scale, situ_beta, situ_linear_beta,
-                 alpha_gate=None, alpha_up=None, out):
+                 topk_packed=None, w1, w1_scale, w2, w2_scale, situ_beta=None, situ_linear_beta=None,
+                 alpha_gate=None, alpha_up=None, out, swiglu_alpha=None, swiglu_beta=None, alpha_down=None,
+                 gate_up_lora_delta=None, activation_lora_input=None):
     """Check dtypes/shapes/devices of torch tensors against the problem and
     return the C struct of their device pointers."""
     import torch
@@ -249,22 +262,28 @@ def make_tensors(problem, *, hidden_states, hidden_states_scale=None, topk_ids=N
     else:
         _need(topk_ids, torch.int32, (T, k), "topk_ids")
         _need(topk_weights, torch.bfloat16, (T, k), "topk_weights")
+    sblk = 16 if p.weight_format == WEIGHT_FORMATS["nvfp4"] else 32   # K elements per weight scale
     _need(w1, torch.uint8, (E, 2 * I, H // 2), "w1")
-    _need(w1_scale, torch.uint8, (E, 2 * I, H // 32), "w1_scale")
+    _need(w1_scale, torch.uint8, (E, 2 * I, H // sblk), "w1_scale")
     _need(w2, torch.uint8, (E, H, I // 2), "w2")
-    _need(w2_scale, torch.uint8, (E, H, I // 32), "w2_scale")
-    for name, t in (("situ_beta", situ_beta), ("situ_linear_beta", situ_linear_beta)):
-        _need(t, torch.float32, (E,), name)
-    for name, t in (("alpha_gate", alpha_gate), ("alpha_up", alpha_up)):
-        if t is not None:
+    _need(w2_scale, torch.uint8, (E, H, I // sblk), "w2_scale")
+    required = {0: ("situ_beta", "situ_linear_beta"), 1: (), 2: ("swiglu_alpha", "swiglu_beta")}[p.activation]
+    params = {"situ_beta": situ_beta, "situ_linear_beta": situ_linear_beta, "swiglu_alpha": swiglu_alpha,
+              "swiglu_beta": swiglu_beta, "alpha_gate": alpha_gate, "alpha_up": alpha_up, "alpha_down": alpha_down}
+    for name, t in params.items():
+        if name in required or t is not None:
             _need(t, torch.float32, (E,), name)
+    if gate_up_lora_delta is not None:
+        _need(gate_up_lora_delta, torch.bfloat16, (T * k, 2 * I), "gate_up_lora_delta")
+    if activation_lora_input is not None:
+        _need(activation_lora_input, torch.bfloat16, (T * k, I), "activation_lora_input")
     _need(out, torch.bfloat16 if p.out_dtype == OUT_BF16 else torch.float32, (T, H), "out")
     ts = SituMoeTensors()
     for name, t in (("hidden_states", hidden_states), ("hidden_states_scale", hidden_states_scale),
                     ("topk_ids", topk_ids), ("topk_weights", topk_weights), ("topk_packed", topk_packed),
                     ("w1", w1), ("w1_scale", w1_scale), ("w2", w2), ("w2_scale", w2_scale),
-                    ("situ_beta", situ_beta), ("situ_linear_beta", situ_linear_beta),
-                    ("alpha_gate", alpha_gate), ("alpha_up", alpha_up), ("out", out)):
+                    ("out", out), ("gate_up_lora_delta", gate_up_lora_delta),
+                    ("activation_lora_input", activation_lora_input)) + tuple(params.items()):
         setattr(ts, name, None if t is None else t.data_ptr())
     return ts
 
@@ -291,12 +310,18 @@ def workspace_view(plan, workspace, region, dtype, shape):
 
 
 def situ_moe(*, hidden_states, hidden_states_scale=None, topk_ids=None, topk_weights=None,
-             topk_packed=None, w1, w1_scale, w2, w2_scale, situ_beta, situ_linear_beta,
+             topk_packed=None, w1, w1_scale, w2, w2_scale, situ_beta=None, situ_linear_beta=None,
              alpha_gate=None, alpha_up=None, num_experts, local_expert_offset, local_num_experts,
              intermediate_size, act_mode="w4a16", out_dtype=None, tactic=(-1, -1), out=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, activation="situ", weight_format="mxfp4", swiglu_alpha=None,
+             swiglu_beta=None, alpha_down=None, gate_up_lora_delta=None, activation_lora_input=None):
     """One call of the layer on torch device tensors (keyword-only, like the
-    pages' mxfp4_situ_routed_moe): returns the [T, H] partial output."""
+    pages' mxfp4_situ_routed_moe): returns the [T, H] partial output.
+
+    stream: a torch.cuda.Stream, a raw hipStream_t handle, or None for the
+    current stream.  `out` and the workspace, when this function allocates
+    them, come from torch's caching allocator on that stream, so they are not
+    handed to another allocation while the layer's kernels still use them."""
     import torch
     T, H = hidden_states.shape
     k = (topk_packed if topk_packed is not None else topk_ids).shape[1]
@@ -307,15 +332,26 @@ def situ_moe(*, hidden_states, hidden_states_scale=None, topk_ids=None, topk_wei
                         num_experts=num_experts, local_expert_offset=local_expert_offset,
                         local_num_experts=local_num_experts, top_k=k, act_mode=act_mode,
                         act_prequantized=hidden_states.dtype == torch.uint8,
-                        topk_packed=topk_packed is not None, out_dtype=od, tactic=tactic)
+                        topk_packed=topk_packed is not None, out_dtype=od, tactic=tactic,
+                        activation=activation, weight_format=weight_format)
     plan = situ_moe_plan(prob)
-    if out is None:
-        out = torch.empty((T, H), dtype=out_dtype, device=hidden_states.device)
+    dev = hidden_states.device
+    if stream is None:
+        stream_obj = torch.cuda.current_stream(dev)
+    elif isinstance(stream, torch.cuda.Stream):
+        stream_obj = stream
+    else:
+        stream_obj = torch.cuda.ExternalStream(int(stream), device=dev)
+    with torch.cuda.stream(stream_obj):
+        if out is None:
+            out = torch.empty((T, H), dtype=out_dtype, device=dev)
+        if workspace is None:
+            workspace = new_workspace(plan, dev)
     ts = make_tensors(prob, hidden_states=hidden_states, hidden_states_scale=hidden_states_scale,
                       topk_ids=topk_ids, topk_weights=topk_weights, topk_packed=topk_packed, w1=w1,
                       w1_scale=w1_scale, w2=w2, w2_scale=w2_scale, situ_beta=situ_beta,
-                      situ_linear_beta=situ_linear_beta, alpha_gate=alpha_gate, alpha_up=alpha_up, out=out)
-    if workspace is None:
-        workspace = new_workspace(plan, hidden_states.device)
-    situ_moe_run(plan, ts, workspace, stream)
+                      situ_linear_beta=situ_linear_beta, alpha_gate=alpha_gate, alpha_up=alpha_up, out=out,
+                      swiglu_alpha=swiglu_alpha, swiglu_beta=swiglu_beta, alpha_down=alpha_down,
+                      gate_up_lora_delta=gate_up_lora_delta, activation_lora_input=activation_lora_input)
+    situ_moe_run(plan, ts, workspace, stream_obj)
     return out

@@ -16,6 +16,18 @@
 
 namespace situ {
 
+// The routing weight of slot s (bf16 bits wb) as fp32, times the FC2 output
+// scale alpha_down of the slot's expert where one is given (one fp32
+// product; the expert comes from the slot's global id).
+__device__ __forceinline__ float slot_weight(const CombineArgs& a, int64_t t, int s, int pos, uint32_t wb, cptr pk) {
+  float w = bf16_to_f32(wb);
+  if (a.alpha_down && pos >= 0) {
+    const int id = a.packed ? (int)((uint32_t)pk[s] & 0xffffu) : a.ids[t * a.k + s];
+    w = w * a.alpha_down[id - a.off];
+  }
+  return w;
+}
+
 constexpr int kCombineThreads = 128;
 constexpr int kCombineCols = kCombineThreads * 4;   // columns per workgroup
 constexpr int kSlotBatch = 8;                       // slot loads kept in flight together
@@ -40,7 +52,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         const int s = s0 + u;
         pos[u] = s < a.k ? inv[s] : -1;
         const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
-        wgt[u] = bf16_to_f32(wb);
+        wgt[u] = slot_weight(a, t, s, pos[u], wb, pk);
       }
       if constexpr (Y16) {
         const int64_t nb64 = (a.H + 63) / 64;
@@ -108,7 +120,7 @@ __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
         const int s = s0 + u;
         pos[u] = s < a.k ? inv[s] : -1;
         const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
-        wgt[u] = bf16_to_f32(wb);
+        wgt[u] = slot_weight(a, t, s, pos[u], wb, pk);
       }
       uint4 hv[kSlotBatch];
       uint32_t ev[kSlotBatch];
@@ -143,6 +155,23 @@ __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
       }
     }
   }
+}
+
+// Zero rows of pairs outside the shard: one wave per row, 16 bytes per lane.
+__global__ __launch_bounds__(256) void zero_nonlocal_rows_kernel(const int32_t* inv, uint16_t* rows, int64_t TK,
+                                                                  int32_t I) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (row >= TK || inv[row] >= 0) return;
+  uint16_t* r = rows + row * I;
+  for (int c = (threadIdx.x % kWave) * 8; c < I; c += kWave * 8)
+    *reinterpret_cast<uint4*>(r + c) = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_nonlocal_rows(const int32_t* inv, uint16_t* rows, int64_t TK, int32_t I, hipStream_t s) {
+  if (TK == 0) return hipSuccess;
+  const int64_t grid = (TK + 3) / 4;
+  hipLaunchKernelGGL(zero_nonlocal_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, inv, rows, TK, I);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {

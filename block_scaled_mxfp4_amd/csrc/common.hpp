@@ -79,6 +79,50 @@ __device__ __forceinline__ void fp4x8_to_bf16x8(uint32_t w, float scale, uint32_
   out[3] = __builtin_bit_cast(uint32_t, r3);
 }
 
+// Eight E2M1 values (one dword, low nibble first) times an arbitrary fp32
+// scale s as eight bf16 in four dwords.  The scaled convert applies only the
+// exponent of its scale operand (measured on gfx950: a scale of 0.7 acts as
+// 0.5), so an NVFP4 block's E4M3 scale is applied by a multiply: E2M1 values
+// have at most two significant bits and E4M3 values four, so every product
+// is exact in fp32 and in bf16, whose upper halves are kept.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp4x8_to_bf16x8_mul(uint32_t w, float s, uint32_t out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x2 v;
+    switch (i) {
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    out[i] = __builtin_amdgcn_perm(__float_as_uint(v.y * s), __float_as_uint(v.x * s), 0x07060302u);
+  }
+}
+
+// Value of an E4M3 code (OCP FN variant: bias 7, 0x7F / 0xFF NaN) by the hardware decode.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
+
+// One lane's 32 E2M1 weights of a K block (16 bytes) as 16 dwords of bf16:
+// MXFP4 with the block's E8M0 code in s, or (NV) NVFP4 with the two E4M3
+// scales of its 16-element halves in the two low bytes of s.
+template <bool NV>
+__device__ __forceinline__ void dequant_w4a16(const uint4& w, uint32_t s, uint32_t wb[16]) {
+  if constexpr (NV) {
+    const float s0 = e4m3_to_f32(s & 0xffu), s1 = e4m3_to_f32((s >> 8) & 0xffu);
+    fp4x8_to_bf16x8_mul(w.x, s0, wb + 0);
+    fp4x8_to_bf16x8_mul(w.y, s0, wb + 4);
+    fp4x8_to_bf16x8_mul(w.z, s1, wb + 8);
+    fp4x8_to_bf16x8_mul(w.w, s1, wb + 12);
+  } else {
+    const float sc = e8m0_to_f32(s);
+    fp4x8_to_bf16x8(w.x, sc, wb + 0);
+    fp4x8_to_bf16x8(w.y, sc, wb + 4);
+    fp4x8_to_bf16x8(w.z, sc, wb + 8);
+    fp4x8_to_bf16x8(w.w, sc, wb + 12);
+  }
+}
+
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
 // Lane l holds A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16];
 // the result D[4*(l/16) + i][l%16] sits in element i of lane l.
@@ -152,6 +196,57 @@ __device__ __forceinline__ float situ_q(float acc_g, float acc_u, const SituK& k
 __device__ __forceinline__ float situ_h(float acc_g, float acc_u, const SituK& k) {
   return situ_q(acc_g, acc_u, k) * k.blb;
 }
+
+// The gated activation of the FC1 epilogues, h = q * blb with q = act_q:
+//  kind 0, SiTU: as situ_q above (blb = b*lb);
+//  kind 1, SwiGLU, g * sigmoid(g) * u, the fused SwiGLU the pages compare SiTU
+//          against (pull request 17865, review of test_kimi_k3_situ_moe.py);
+//  kind 2, SwigluBias, g * sigmoid(g * sa) * (u + sb) with per-expert sa, sb
+//          (CUTLASS SwigluBias, the same review's _swiglu_bias_act);
+// for kinds 1 and 2, q = (kg*x_g) * (ku*x_u + kb) / (1 + 2^(ke*x_g)) with one
+// exponential and one reciprocal, blb = 1.  The inputs x_g, x_u are the
+// accumulators (alpha folded into the constants), or -- with a LoRA delta,
+// which is added after alpha -- g and u themselves (constants built with
+// unit alphas).
+enum : int { kActSitu = 0, kActSwiglu = 1, kActSwigluBias = 2 };
+struct ActK {
+  int kind;
+  SituK s;       // SiTU
+  float kg, ke, ku, kb;
+};
+__device__ __forceinline__ ActK act_consts(int kind, float ag, float au, float p0, float p1) {
+  constexpr float kL2e = 1.44269502162933349609375f;
+  ActK k;
+  k.kind = kind;
+  if (kind == kActSitu) {
+    k.s = situ_consts(ag, au, p0, p1);
+    k.kg = k.ke = k.ku = k.kb = 0.0f;
+  } else {
+    const float sa = kind == kActSwigluBias ? p0 : 1.0f;
+    k.s = SituK{0.0f, 0.0f, 0.0f, 1.0f};
+    k.kg = ag;
+    k.ke = -(sa * ag * kL2e);
+    k.ku = au;
+    k.kb = kind == kActSwigluBias ? p1 : 0.0f;
+  }
+  return k;
+}
+__device__ __forceinline__ float act_blb(const ActK& k) { return k.s.blb; }
+__device__ __forceinline__ float act_q(float xg, float xu, const ActK& k) {
+  if (k.kind == kActSitu) return situ_q(xg, xu, k.s);
+  const float e = __builtin_amdgcn_exp2f(xg * k.ke);
+  return (xg * k.kg) * __builtin_fmaf(xu, k.ku, k.kb) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ float act_h(float xg, float xu, const ActK& k) { return act_q(xg, xu, k) * k.s.blb; }
+
+// Per-expert activation constants of one FC1 work item and its LoRA mode:
+// `lora` set when a delta is added (then the constants take unit alphas and
+// the inputs are g = fma(ag, acc_g, d_g), u = fma(au, acc_u, d_u)).
+struct ActItem {
+  ActK k;
+  float ag, au;
+  bool lora;
+};
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 

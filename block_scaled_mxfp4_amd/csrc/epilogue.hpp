@@ -1,0 +1,86 @@
+// FC1 epilogue pieces shared by the grouped-GEMM kernels: the per-expert
+// activation constants of a work item, the LoRA delta of one lane's columns
+// and the bf16 rows handed to the down LoRA.
+//
+// The LoRA bridges follow the decomposed MoE-LoRA op of the xorl-wheels
+// release notes ("Changes since 875b7d7"): a gate_up LoRA delta is added to
+// the FC1 output before the activation, the activation's output is handed
+// back as the down LoRA's input, and with no bridges the op is the plain
+// pipeline.  The delta is in the layer's real-valued domain, so it is added
+// after the alpha scaling: g = alpha_g * acc_g + d_g, u = alpha_u * acc_u + d_u.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace situ {
+
+// Activation constants of expert l (scalar loads of the per-expert arrays).
+__device__ __forceinline__ ActItem act_item(const GemmArgs& a, int l) {
+  typedef const int32_t __attribute__((address_space(4)))* cp;
+  ActItem it;
+  it.ag = a.alpha_g ? __builtin_bit_cast(float, ((cp)a.alpha_g)[l]) : 1.0f;
+  it.au = a.alpha_u ? __builtin_bit_cast(float, ((cp)a.alpha_u)[l]) : 1.0f;
+  const float p0 = a.beta ? __builtin_bit_cast(float, ((cp)a.beta)[l]) : 0.0f;
+  const float p1 = a.lbeta ? __builtin_bit_cast(float, ((cp)a.lbeta)[l]) : 0.0f;
+  it.lora = a.lora_delta != nullptr;
+  it.k = it.lora ? act_consts(a.act_kind, 1.0f, 1.0f, p0, p1) : act_consts(a.act_kind, it.ag, it.au, p0, p1);
+  return it;
+}
+
+// Four consecutive bf16 of a row as floats.
+__device__ __forceinline__ void load_bf16x4(const uint16_t* p, float v[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf16_to_f32(w.x & 0xffffu);
+  v[1] = bf16_to_f32(w.x >> 16);
+  v[2] = bf16_to_f32(w.y & 0xffffu);
+  v[3] = bf16_to_f32(w.y >> 16);
+}
+
+// The activation inputs of four gate/up column pairs: the accumulators as
+// they are, or with a LoRA delta (drow = the pair's delta row at the first
+// gate column; up columns I further) g and u themselves.
+__device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* drow, int I, const float ag4[4],
+                                           const float au4[4], float xg[4], float xu[4]) {
+  if (it.lora) {
+    float dg[4], du[4];
+    load_bf16x4(drow, dg);
+    load_bf16x4(drow + I, du);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xg[e] = __builtin_fmaf(it.ag, ag4[e], dg[e]);
+      xu[e] = __builtin_fmaf(it.au, au4[e], du[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xg[e] = ag4[e];
+      xu[e] = au4[e];
+    }
+  }
+}
+
+// E4M3 code (one byte of `codes`, hardware decode, exact) times 2^(sc - 127), as bf16 bits.
+__device__ __forceinline__ uint32_t e4m3_scaled_bf16(uint32_t codes, int byte, int sc) {
+  float v;
+  switch (byte) {
+    case 0: v = __builtin_amdgcn_cvt_f32_fp8((int)codes, 0); break;
+    case 1: v = __builtin_amdgcn_cvt_f32_fp8((int)codes, 1); break;
+    case 2: v = __builtin_amdgcn_cvt_f32_fp8((int)codes, 2); break;
+    default: v = __builtin_amdgcn_cvt_f32_fp8((int)codes, 3); break;
+  }
+  return f32_to_bf16_rne(__builtin_ldexpf(v, sc - 127));
+}
+
+// Four E4M3 codes (one dword) under scale code sc as four bf16 (two dwords).
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t codes, int sc) {
+  return make_uint2(e4m3_scaled_bf16(codes, 0, sc) | (e4m3_scaled_bf16(codes, 1, sc) << 16),
+                    e4m3_scaled_bf16(codes, 2, sc) | (e4m3_scaled_bf16(codes, 3, sc) << 16));
+}
+
+}  // namespace situ
+
+#include "../../include/situ_moe.h"
+static_assert(situ::kActSitu == SITU_ACTIVATION_SITU && situ::kActSwiglu == SITU_ACTIVATION_SWIGLU &&
+                  situ::kActSwigluBias == SITU_ACTIVATION_SWIGLU_BIAS,
+              "the planner passes the ABI's activation values as the kernels' kinds");

@@ -30,21 +30,28 @@
 // Scheduling.  A persistent grid walks work items (m-tile, column tile); the
 // m-tiles and their experts come from the router's tile list on the device,
 // so no group size is ever read back to the host.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "common.hpp"
 #include "dma.hpp"
+#include "epilogue.hpp"
 #include "internal.hpp"
 
 namespace situ {
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <bool FP8, int TOKT>
+template <bool FP8, int TOKT, bool NV = false>
 __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
+  static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   const int I = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
+  const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
   const int units = I / kFc1ColsPerWave;
   const int n_wgn = (units + 3) / 4;
   const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         wrow[q] = a.w + (ebase + rows[q]) * (int64_t)(K / 2);
-        srow[q] = a.ws + (ebase + rows[q]) * (int64_t)nkb;
+        srow[q] = a.ws + (ebase + rows[q]) * (int64_t)sbr;
       }
     }
 
@@ -96,7 +103,9 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         wv[q] = kin ? ld16(wrow[q] + kb * 16) : make_uint4(0, 0, 0, 0);
-        sv[q] = kin ? srow[q][kb] : 127u;
+        // NVFP4: the two E4M3 scales of this 32-K block in one 16-bit load
+        sv[q] = NV ? (kin ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 2 * kb) : 0x3838u)
+                   : (kin ? (uint32_t)srow[q][kb] : 127u);
       }
       if constexpr (!FP8) {
         uint4 xv[TOKT][4];
@@ -107,12 +116,8 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
             xv[tt][c] = (kin && valid[tt]) ? ld16(xrow[tt] + kb * 64 + 16 * c) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float sc = e8m0_to_f32(sv[q]);
           uint32_t wb[16];
-          fp4x8_to_bf16x8(wv[q].x, sc, wb + 0);
-          fp4x8_to_bf16x8(wv[q].y, sc, wb + 4);
-          fp4x8_to_bf16x8(wv[q].z, sc, wb + 8);
-          fp4x8_to_bf16x8(wv[q].w, sc, wb + 12);
+          dequant_w4a16<NV>(wv[q], sv[q], wb);
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -146,27 +151,33 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       }
     }
 
-    // epilogue: alpha, SiTU, rounding point R1, store h in perm order
-    const float ag = a.alpha_g ? a.alpha_g[l] : 1.0f;
-    const float au = a.alpha_u ? a.alpha_u[l] : 1.0f;
-    const SituK sk = situ_consts(ag, au, a.beta[l], a.lbeta[l]);
+    // epilogue: alpha (and a LoRA delta), the activation, rounding point R1,
+    // store h in perm order (and by expanded index for the down LoRA)
+    const ActItem ai = act_item(a, l);
 #pragma unroll
     for (int tt = 0; tt < TOKT; ++tt) {
       const int64_t p = p0 + 16 * tt + r;
+      const int64_t j = (valid[tt] && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
       float hv[2][4];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int half = 0; half < 2; ++half) {
+        float xg[4], xu[4];
+        const float ag4[4] = {acc[half][tt][0], acc[half][tt][1], acc[half][tt][2], acc[half][tt][3]};
+        const float au4[4] = {acc[2 + half][tt][0], acc[2 + half][tt][1], acc[2 + half][tt][2], acc[2 + half][tt][3]};
+        act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hv[half][i] = situ_h(acc[half][tt][i], acc[2 + half][tt][i], sk);
+        for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+      }
       if constexpr (!FP8) {
         if (valid[tt]) {
           uint16_t* hrow = static_cast<uint16_t*>(a.out) + p * I + n0 + 4 * g;
+          uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
             const uint32_t hi = f32_to_bf16_rne(hv[half][2]) | (f32_to_bf16_rne(hv[half][3]) << 16);
             *reinterpret_cast<uint2*>(hrow + 16 * half) = make_uint2(lo, hi);
+            if (lrow) *reinterpret_cast<uint2*>(lrow + 16 * half) = make_uint2(lo, hi);
           }
         }
       } else {
@@ -181,12 +192,14 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
           const uint32_t code = e8m0_code_for_e4m3(amax);
           const int sh = 127 - (int)code;
           uint8_t* hrow = static_cast<uint8_t*>(a.out) + p * I + n0 + 4 * g;
+          uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             uint32_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__builtin_ldexpf(hv[half][i], sh)) << (8 * i);
             *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
+            if (lrow) *reinterpret_cast<uint2*>(lrow + 16 * half) = e4m3x4_to_bf16x4(packed, (int)code);
           }
           if (g == 0) a.out_scale[p * (I / 32) + n0 / 32] = (uint8_t)code;
         }
@@ -195,13 +208,15 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
   }
 }
 
-template <bool FP8, int TOKT>
+template <bool FP8, int TOKT, bool NV = false>
 __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
+  static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r = lane & 15, g = lane >> 4;
   const int H = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
+  const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
   const int wg_rows = 4 * kFc2RowsPerWave;
   const int n_wgn = (H + wg_rows - 1) / wg_rows;
   const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int64_t row = (int64_t)l * H + min(n0 + 16 * q + r, H - 1);
       wrow[q] = a.w + row * (int64_t)(K / 2);
-      srow[q] = a.ws + row * (int64_t)nkb;
+      srow[q] = a.ws + row * (int64_t)sbr;
     }
 
     f32x4 acc[4][TOKT];
@@ -251,7 +266,8 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
       for (int q = 0; q < 4; ++q) {
         const bool ok = kin && q < ntiles;
         wv[q] = ok ? ld16(wrow[q] + kb * 16) : make_uint4(0, 0, 0, 0);
-        sv[q] = ok ? srow[q][kb] : 127u;
+        sv[q] = NV ? (ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 2 * kb) : 0x3838u)
+                   : (ok ? (uint32_t)srow[q][kb] : 127u);
       }
       if constexpr (!FP8) {
         uint4 xv[TOKT][4];
@@ -262,12 +278,8 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
             xv[tt][c] = (kin && valid[tt]) ? ld16(hrow[tt] + kb * 64 + 16 * c) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float sc = e8m0_to_f32(sv[q]);
           uint32_t wb[16];
-          fp4x8_to_bf16x8(wv[q].x, sc, wb + 0);
-          fp4x8_to_bf16x8(wv[q].y, sc, wb + 4);
-          fp4x8_to_bf16x8(wv[q].z, sc, wb + 8);
-          fp4x8_to_bf16x8(wv[q].w, sc, wb + 12);
+          dequant_w4a16<NV>(wv[q], sv[q], wb);
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -350,29 +362,16 @@ constexpr uint32_t kOob = 0x80000000u;   // an offset past every resource: reads
 // two or not at all, whose ring fits 128 registers (TP8 decode FC1 -1 %, EP8
 // -1.5 %), three elsewhere (FC2's deeper weight ring needs a few more, and a
 // four-way split's partial sums would spill).
-#ifndef SITU_DECODE_DEPTH
-#define SITU_DECODE_DEPTH 1
-#endif
-#ifndef SITU_DECODE_WAVES
-#define SITU_DECODE_WAVES 3
-#endif
-#ifndef SITU_DECODE_WAVES_FC1
-#define SITU_DECODE_WAVES_FC1 4
-#endif
-constexpr int kDecodeDepth = SITU_DECODE_DEPTH;
+constexpr int kDecodeDepth = 1;
 __host__ __device__ constexpr int decode_waves(bool fp8, bool fc1, int ksplit) {
-  return (!fp8 && fc1 && ksplit <= 2) ? SITU_DECODE_WAVES_FC1 : SITU_DECODE_WAVES;
+  return (!fp8 && fc1 && ksplit <= 2) ? 4 : 3;
 }
 // w4a16 weight steps in flight (the activation pieces stay one step ahead):
 // two for FC2 with its K split (EP8 decode FC2 -3 %), one elsewhere (the
 // unsplit three-step FC2 of TP8 decode measured 2 % slower with two, FC1 no
 // faster).
-#ifndef SITU_DECODE_WDEPTH_FC1
-#define SITU_DECODE_WDEPTH_FC1 1
-#endif
-#ifndef SITU_DECODE_WDEPTH_FC2
-#define SITU_DECODE_WDEPTH_FC2 2
-#endif
+constexpr int kDecodeWDepthFc1 = 1;
+constexpr int kDecodeWDepthFc2Split = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -397,12 +396,12 @@ struct DecodeGeo {
   __amdgpu_buffer_rsrc_t wr, xr, xsr;
   uint32_t w_row;          // byte offset of this lane's row of tile 0 in the expert's weights
   uint32_t w_delta[4];     // tile q rows relative to tile 0, in weight bytes (uniform)
-  const uint8_t* s_lds;    // this unit's staged scales: [4 tiles x 16 rows][nkb]
+  const uint8_t* s_lds;    // this unit's staged scales: [4 tiles x 16 rows][sbr]
   uint32_t x_row;          // byte offset of this lane's activation row (kOob if none)
   uint32_t xs_row;
   const uint8_t* x_lds;    // w4a16: the m-tile's activation rows staged in LDS, or null
   uint32_t x_lds_off;      // this lane's row in them (bytes)
-  int nkb, g, r, ntiles;
+  int nkb, sbr, g, r, ntiles;   // sbr: scale bytes per weight row (nkb, or 2 nkb for NVFP4)
 };
 
 // One K step's operands for a wave: four 16-row weight tiles (16 bytes of
@@ -468,18 +467,30 @@ __device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int 
 
 // w4a16 step j: the weight pieces dequantized to bf16 by their E8M0 scales
 // (staged in LDS), times the activation piece.
+template <bool NV = false>
 __device__ __forceinline__ void compute_w4a16(const uint4 w[4], const uint4 x[4], const DecodeGeo& d, int j,
                                               f32x4 acc[4]) {
   const int kb = 4 * j + d.g;
   const bool kin = kb < d.nkb;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u);
     uint32_t wb[16];
-    fp4x8_to_bf16x8(w[q].x, sc, wb + 0);
-    fp4x8_to_bf16x8(w[q].y, sc, wb + 4);
-    fp4x8_to_bf16x8(w[q].z, sc, wb + 8);
-    fp4x8_to_bf16x8(w[q].w, sc, wb + 12);
+    if constexpr (NV) {
+      // NVFP4: two E4M3 scales per 32 K (one per 16), non powers of two
+      const uint8_t* sp = d.s_lds + (16 * q + d.r) * d.sbr + 2 * kb;
+      const float s0 = kin ? e4m3_to_f32(sp[0]) : 1.0f;
+      const float s1 = kin ? e4m3_to_f32(sp[1]) : 1.0f;
+      fp4x8_to_bf16x8_mul(w[q].x, s0, wb + 0);
+      fp4x8_to_bf16x8_mul(w[q].y, s0, wb + 4);
+      fp4x8_to_bf16x8_mul(w[q].z, s1, wb + 8);
+      fp4x8_to_bf16x8_mul(w[q].w, s1, wb + 12);
+    } else {
+      const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.sbr + kb] : 127u);
+      fp4x8_to_bf16x8(w[q].x, sc, wb + 0);
+      fp4x8_to_bf16x8(w[q].y, sc, wb + 4);
+      fp4x8_to_bf16x8(w[q].z, sc, wb + 8);
+      fp4x8_to_bf16x8(w[q].w, sc, wb + 12);
+    }
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const uint32_t xb[4] = {x[qq].x, x[qq].y, x[qq].z, x[qq].w};
@@ -499,7 +510,7 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t av[4] = {b.w[q].x, b.w[q].y, b.w[q].z, b.w[q].w};
-      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
+      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.sbr + kb] : 127u;
       acc[q] = mfma_scale_fp4_fp8(av, xb, sv, b.xs, acc[q]);
     }
   }
@@ -508,8 +519,8 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 // Dynamic LDS of a decode launch: staged scales of the workgroup's units,
 // then one region that holds the staged activation rows during the K loop
 // and the split-K partial sums after it.
-__host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int nkb) {
-  return (uint32_t)(units_per_wg * 64 * nkb + 15) / 16u * 16u;
+__host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int sbr) {
+  return (uint32_t)(units_per_wg * 64 * sbr + 15) / 16u * 16u;
 }
 __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return ksplit > 1 ? 4u * 4u * kWave * 16u : 0u; }
 // w4a16: an m-tile of at most decode_x_rows() tokens has its activation rows
@@ -519,18 +530,18 @@ __host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return kspli
 // weights each step (TP8 decode FC1 -2..5 %, FC2 -6 %).  The rows get what is
 // left of the LDS share of one of the decode_waves() workgroups of a CU after
 // the scales, 16 at most (FC1 at H = 3584: three rows, FC2 at I = 384: 16).
-__host__ __device__ constexpr int decode_x_rows(int ksplit, int nkb, int K, bool fp8, bool fc1) {
+__host__ __device__ constexpr int decode_x_rows(int ksplit, int sbr, int K, bool fp8, bool fc1) {
   const uint32_t budget = 160u * 1024u / (uint32_t)decode_waves(fp8, fc1, ksplit) - 512u;
-  const uint32_t used = decode_lds_scales(4 / ksplit, nkb);
+  const uint32_t used = decode_lds_scales(4 / ksplit, sbr);
   const uint32_t left = budget > used ? budget - used : 0u;
   const int rows = (int)(left / ((uint32_t)K * 2u));
   return fp8 ? 0 : (rows < 16 ? rows : 16);
 }
-__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, bool fc1, int ksplit, int K) {
-  return (uint32_t)decode_x_rows(ksplit, K / 32, K, fp8, fc1) * (uint32_t)K * 2u;
+__host__ __device__ constexpr uint32_t decode_lds_x(bool fp8, bool fc1, int ksplit, int K, int sbr) {
+  return (uint32_t)decode_x_rows(ksplit, sbr, K, fp8, fc1) * (uint32_t)K * 2u;
 }
-__host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int nkb, uint32_t x_bytes) {
-  return decode_lds_scales(4 / ksplit, nkb) + (x_bytes > decode_lds_red(ksplit) ? x_bytes : decode_lds_red(ksplit));
+__host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int sbr, uint32_t x_bytes) {
+  return decode_lds_scales(4 / ksplit, sbr) + (x_bytes > decode_lds_red(ksplit) ? x_bytes : decode_lds_red(ksplit));
 }
 
 // Decode epilogue of one wave's 16-row group: FC1 applies alpha and SiTU and
@@ -543,24 +554,29 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
                                                 int n0, int g, int ntiles) {
   if constexpr (FC1) {
     const int I = a.N;
-    const float ag = a.alpha_g ? __builtin_bit_cast(float, ((cptr)a.alpha_g)[l]) : 1.0f;
-    const float au = a.alpha_u ? __builtin_bit_cast(float, ((cptr)a.alpha_u)[l]) : 1.0f;
-    const SituK sk = situ_consts(ag, au, __builtin_bit_cast(float, ((cptr)a.beta)[l]),
-                                 __builtin_bit_cast(float, ((cptr)a.lbeta)[l]));
+    const ActItem ai = act_item(a, l);
+    // the pair's expanded index: the row of its LoRA delta and down-LoRA input
+    const int64_t j = (valid && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
     float hv[2][4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
+    for (int half = 0; half < 2; ++half) {
+      float xg[4], xu[4];
+      const float ag4[4] = {acc[half][0], acc[half][1], acc[half][2], acc[half][3]};
+      const float au4[4] = {acc[2 + half][0], acc[2 + half][1], acc[2 + half][2], acc[2 + half][3]};
+      act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hv[half][i] = situ_h(acc[half][i], acc[2 + half][i], sk);
+      for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+    }
     if constexpr (!FP8) {
       if (valid) {
         uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+        uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
           const uint32_t hi = f32_to_bf16_rne(hv[half][2]) | (f32_to_bf16_rne(hv[half][3]) << 16);
           *reinterpret_cast<uint2*>(hrow + 16 * half) = make_uint2(lo, hi);
+          if (lrow) *reinterpret_cast<uint2*>(lrow + 16 * half) = make_uint2(lo, hi);
         }
       }
     } else {
@@ -575,12 +591,14 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
         const uint32_t code = e8m0_code_for_e4m3(amax);
         const int sh = 127 - (int)code;
         uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+        uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           uint32_t packed = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) packed |= e4m3_encode(__builtin_ldexpf(hv[half][i], sh)) << (8 * i);
           *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
+          if (lrow) *reinterpret_cast<uint2*>(lrow + 16 * half) = e4m3x4_to_bf16x4(packed, (int)code);
         }
         if (g == 0) a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
       }
@@ -595,8 +613,9 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
   }
 }
 
-template <bool FP8, bool FC1, int KSPLIT>
+template <bool FP8, bool FC1, int KSPLIT, bool NV = false>
 __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
+  static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
   extern __shared__ __align__(16) uint8_t lds[];
   // wave-uniform values are made visibly uniform (readfirstlane, scalar
@@ -608,29 +627,20 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
   const int ks = wave % KSPLIT;
   const int uw = wave / KSPLIT;
   const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
+  const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
   const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
   const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
   const int total = mtiles[a.E_l] * n_wgn;
   const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
   const int n_rows = FC1 ? 2 * a.N : a.N;          // weight rows per expert
-  // contiguous K range of this wave
-  const int per = (steps + KSPLIT - 1) / KSPLIT;
-#ifndef SITU_DECODE_KSPLIT_INTERLEAVE
-#define SITU_DECODE_KSPLIT_INTERLEAVE 1
-#endif
-  // this wave's K steps: every KSPLIT-th step from ks (interleaved, the
-  // default), or a contiguous range
-  constexpr bool kInterleave = SITU_DECODE_KSPLIT_INTERLEAVE != 0;
-  const int j_begin = kInterleave ? ks : min(steps, ks * per);
-  const int j_stride = kInterleave ? KSPLIT : 1;
-  const int my_steps = kInterleave ? (steps > ks ? (steps - ks + KSPLIT - 1) / KSPLIT : 0)
-                                   : min(steps, j_begin + per) - j_begin;
-  auto jstep = [&](int s) { return j_begin + j_stride * s; };
+  // this wave's K steps: every KSPLIT-th step from ks (interleaved)
+  const int my_steps = steps > ks ? (steps - ks + KSPLIT - 1) / KSPLIT : 0;
+  auto jstep = [&](int s) { return ks + KSPLIT * s; };
   // the activation rows during the K loop, then the partial sums [4 waves][4][64]
-  uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, nkb);
+  uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, sbr);
   f32x4* red = reinterpret_cast<f32x4*>(x_stage);
   constexpr bool XL = !FP8;                    // w4a16 may stage its activation rows
-  constexpr int DW = FC1 ? SITU_DECODE_WDEPTH_FC1 : (KSPLIT > 1 ? SITU_DECODE_WDEPTH_FC2 : 1);
+  constexpr int DW = FC1 ? kDecodeWDepthFc1 : (KSPLIT > 1 ? kDecodeWDepthFc2Split : 1);
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = w / n_wgn;
@@ -645,24 +655,24 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
 
     // stage the scales of the workgroup's units in LDS (16-byte loads)
     {
-      const size_t sexp = (size_t)n_rows * nkb;
+      const size_t sexp = (size_t)n_rows * sbr;
       const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ws + (size_t)l * sexp, (uint32_t)sexp);
-      const int chunks_per_unit = 4 * nkb;       // 64 rows x nkb bytes / 16
+      const int chunks_per_unit = 4 * sbr;       // 64 rows x sbr bytes / 16
       for (int c = threadIdx.x; c < UNITS_PER_WG * chunks_per_unit; c += kGemmThreads) {
         const int u = c / chunks_per_unit, cc = c % chunks_per_unit;
         uint32_t src;
         if constexpr (FC1) {
-          const int half = cc / (2 * nkb), within = cc % (2 * nkb);
+          const int half = cc / (2 * sbr), within = cc % (2 * sbr);
           const int row = (half ? a.N : 0) + (unit0 + u) * kFc1ColsPerWave;
-          src = (unit0 + u < units) ? (uint32_t)row * nkb + 16u * within : kOob;
+          src = (unit0 + u < units) ? (uint32_t)row * sbr + 16u * within : kOob;
         } else {
-          src = (uint32_t)(unit0 + u) * kFc2RowsPerWave * nkb + 16u * cc;   // rows past H read 0
+          src = (uint32_t)(unit0 + u) * kFc2RowsPerWave * sbr + 16u * cc;   // rows past H read 0
         }
-        *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * nkb + 16 * cc) = bload16(sr, src);
+        *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * sbr + 16 * cc) = bload16(sr, src);
       }
     }
     // w4a16 with few tokens: stage the m-tile's activation rows (16-byte loads)
-    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, nkb, K, FP8, FC1);   // uniform
+    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, sbr, K, FP8, FC1);   // uniform
     if constexpr (XL) {
       if (x_in_lds) {
         const int row_chunks = K / 8;               // K bf16 values / 16 bytes
@@ -688,6 +698,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
       const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
       d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
       d.nkb = nkb;
+      d.sbr = sbr;
       d.g = g;
       d.r = r;
       uint32_t dr[4];
@@ -703,7 +714,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
 #pragma unroll
       for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
       d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2);
-      d.s_lds = lds + (size_t)uw * 64 * nkb;
+      d.s_lds = lds + (size_t)uw * 64 * sbr;
       d.x_lds = x_in_lds ? x_stage : nullptr;
       d.x_lds_off = valid ? (uint32_t)r * arow_bytes : 0u;
       if constexpr (FC1) {
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
                 else load_x_mem(xr[(u + 1) % 2].x, d, jstep(s + 1));
               }
               __builtin_amdgcn_sched_barrier(0);
-              compute_w4a16(wr[u % NW].w, xr[u % 2].x, d, jstep(s), acc);
+              compute_w4a16<NV>(wr[u % NW].w, xr[u % 2].x, d, jstep(s), acc);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -810,12 +821,9 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
 }
 
 // K split for the decode kernels: long K loops are shared by the four waves.
-#ifndef SITU_DECODE_KSPLIT_MIN_STEPS
-#define SITU_DECODE_KSPLIT_MIN_STEPS 8
-#endif
 static int decode_ksplit(int K) {
   const int steps = (K / 32 + 3) / 4;
-  const int m = SITU_DECODE_KSPLIT_MIN_STEPS;   // steps per wave below which K is not split further
+  const int m = 8;   // steps per wave below which K is not split further
   return steps >= 4 * m ? 4 : (steps >= 2 * m ? 2 : 1);
 }
 
@@ -823,17 +831,24 @@ static int decode_ksplit(int K) {
 // queried once per kernel; a persistent grid is sized to what fits.
 using GemmKernel = void (*)(GemmArgs);
 
+int resident_per_cu(const void* kernel, int threads, uint32_t lds_bytes) {
+  // queried once per (kernel, block size, dynamic LDS size), under a lock:
+  // launches may come from several host threads at once
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, uint32_t>, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_tuple(kernel, threads, lds_bytes);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds_bytes) != hipSuccess || n < 1) n = 1;
+  cache.emplace(key, n);
+  return n;
+}
+
 template <GemmKernel KERNEL>
 static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hipStream_t s, uint32_t lds_bytes = 0) {
-  // occupancy depends on the dynamic LDS size; cache per size
-  static int per_cu = 0;
-  static uint32_t per_cu_lds = 0xffffffffu;
-  if (per_cu_lds != lds_bytes) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERNEL, kGemmThreads, lds_bytes) != hipSuccess || n < 1) n = 1;
-    per_cu = n;
-    per_cu_lds = lds_bytes;
-  }
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(KERNEL), kGemmThreads, lds_bytes);
   const int64_t cap = (int64_t)cus * per_cu;
   const int grid = (int)(work < cap ? work : cap);
   if (grid <= 0) return hipSuccess;
@@ -841,13 +856,21 @@ static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hi
   return hipGetLastError();
 }
 
+template <bool FP8, bool FC1, bool NV>
+hipError_t launch_decode_k(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
+  const int sbr = NV ? a.K / 16 : a.K / 32;   // scale bytes per weight row
+  switch (decode_ksplit(a.K)) {
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1, NV>>(a, work, cus, s, decode_lds_bytes(1, sbr, decode_lds_x(FP8, FC1, 1, a.K, sbr)));
+  }
+}
 template <bool FP8, bool FC1>
 hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
-  switch (decode_ksplit(a.K)) {
-    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4>>(a, work, cus, s, decode_lds_bytes(4, a.K / 32, decode_lds_x(FP8, FC1, 4, a.K)));
-    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2>>(a, work, cus, s, decode_lds_bytes(2, a.K / 32, decode_lds_x(FP8, FC1, 2, a.K)));
-    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1>>(a, work, cus, s, decode_lds_bytes(1, a.K / 32, decode_lds_x(FP8, FC1, 1, a.K)));
+  if constexpr (!FP8) {
+    if (a.nvfp4) return launch_decode_k<false, FC1, true>(a, work, cus, s);
   }
+  return launch_decode_k<FP8, FC1, false>(a, work, cus, s);
 }
 
 // Work items of one launch, upper bound: m-tiles x column units per workgroup.
@@ -864,7 +887,9 @@ hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
   const int64_t work = work_items(true, decode, a, max_mtiles);
   switch (tactic) {
     case FC1_W4A16_M16: return launch_decode<false, true>(a, work, cus, s);
-    case FC1_W4A16_M64: return launch_persistent<fc1_kernel<false, 4>>(a, work, cus, s);
+    case FC1_W4A16_M64:
+      return a.nvfp4 ? launch_persistent<fc1_kernel<false, 4, true>>(a, work, cus, s)
+                     : launch_persistent<fc1_kernel<false, 4>>(a, work, cus, s);
     case FC1_W4A8_M16: return launch_decode<true, true>(a, work, cus, s);
     case FC1_W4A8_M64:
       if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill<true>(a, max_mtiles, cus, s);
@@ -881,7 +906,9 @@ hipError_t launch_fc2(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
   const int64_t work = work_items(false, decode, a, max_mtiles);
   switch (tactic) {
     case FC2_W4A16_M16: return launch_decode<false, false>(a, work, cus, s);
-    case FC2_W4A16_M64: return launch_persistent<fc2_kernel<false, 4>>(a, work, cus, s);
+    case FC2_W4A16_M64:
+      return a.nvfp4 ? launch_persistent<fc2_kernel<false, 4, true>>(a, work, cus, s)
+                     : launch_persistent<fc2_kernel<false, 4>>(a, work, cus, s);
     case FC2_W4A8_M16: return launch_decode<true, false>(a, work, cus, s);
     case FC2_W4A8_M64:   // the LDS kernel addresses h with 32-bit offsets
       if (a.K % 128 == 0 && (int64_t)max_mtiles * 64 * a.K < ((int64_t)1 << 31))

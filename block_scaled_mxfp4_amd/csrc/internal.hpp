@@ -52,11 +52,18 @@ struct GemmArgs {
   int32_t K;                  // contraction length (H for FC1, I for FC2)
   int32_t N;                  // FC1: I (gate columns; up rows at I + n); FC2: H
   int32_t E_l;
-  // FC1 epilogue
+  // FC1 epilogue: the gated activation (kActSitu / kActSwiglu / kActSwigluBias)
+  // and its two per-expert parameters (SiTU: beta, linear beta; SwigluBias:
+  // alpha, beta; SwiGLU: none, may be null)
+  int32_t act_kind;
   const float* beta;
   const float* lbeta;
   const float* alpha_g;       // may be null
   const float* alpha_u;       // may be null
+  const uint16_t* lora_delta; // FC1: bf16 [T*k, 2I] added to the alpha-scaled halves, by expanded index, or null
+  uint16_t* lora_out;         // FC1: bf16 [T*k, I] receives h by expanded index, or null
+  // weights: 0 = MXFP4 (E8M0 per 32 along K), 1 = NVFP4 (E4M3 per 16; w4a16 kernels only)
+  int32_t nvfp4;
   // outputs
   void* out;                  // FC1: h bf16 [P, I] or E4M3 [P, I]; FC2: y float [P, H] or fp16 [P, H]
   uint8_t* out_scale;         // FC1 w4a8: E8M0 [P, I/32]; FC2: null (fp32 y) or y's exponents [ceil(H/64), out_rows]
@@ -73,7 +80,18 @@ struct CombineArgs {
   void* out;                  // [T, H]
   int64_t T;
   int32_t H, k, out_bf16;
+  const float* alpha_down;    // [E_l] per-expert FC2 output scale, or null
+  const int32_t* ids;         // [T, k] global ids (unpacked routing; packed carries them in the low 16 bits)
+  int32_t off;                // local expert offset
 };
+
+// Zero the rows [T*k, I] of pairs outside the shard (inv < 0) in the bf16
+// down-LoRA input (the FC1 epilogues write the local rows).
+hipError_t launch_zero_nonlocal_rows(const int32_t* inv, uint16_t* rows, int64_t TK, int32_t I, hipStream_t s);
+
+// Workgroups of `kernel` resident per CU at this block size and dynamic LDS
+// size (hipOccupancyMaxActiveBlocksPerMultiprocessor, cached; thread-safe).
+int resident_per_cu(const void* kernel, int threads, uint32_t lds_bytes);
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_quant_mxfp8(const QuantArgs& a, hipStream_t s);

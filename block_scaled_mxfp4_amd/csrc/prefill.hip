@@ -29,6 +29,7 @@
 // planner routes other shapes to the 16-row kernels.
 #include "common.hpp"
 #include "dma.hpp"
+#include "epilogue.hpp"
 #include "internal.hpp"
 
 namespace situ {
@@ -48,17 +49,7 @@ constexpr int kStageB = 4 * kTileB;
 constexpr int kStageSA = kPfRows * 4;
 constexpr int kStageSB = kPfTok * 4;
 constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;   // 25856 bytes
-#ifndef SITU_PF_STAGES
-#define SITU_PF_STAGES 3
-#endif
-constexpr int kPfStages = SITU_PF_STAGES;    // 3 x 25856 B: two workgroups per CU
-static_assert(kPfStages >= 2 && kPfStages <= 4, "stage ring of 2..4");
-// Whether a stage wait may count output stores issued after the stage's DMA
-// (only sound if stores and loads leave the vector-memory counter in issue
-// order); 0 = count DMAs only, which also waits for those stores.
-#ifndef SITU_PF_COUNT_STORES
-#define SITU_PF_COUNT_STORES 0
-#endif
+constexpr int kPfStages = 3;    // 3 x 25856 B: two workgroups per CU
 
 constexpr uint32_t kOobPf = kOobOff;
 
@@ -92,19 +83,13 @@ __device__ __forceinline__ void pf_issue(uint32_t st, const PfGeo& d, int j, int
     dma4(d.xsr, st + kStageA + kStageB + kStageSA + wave * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
 }
 
-// `after` = K steps whose DMAs this wave issued after the one to wait for;
-// `st`: the previous item's NST output stores were also issued after it.
-template <int NST>
-__device__ __forceinline__ void step_barrier(int after, bool st) {
-  if (st) {
-    if (after >= 2) dma_barrier<2 * kPfDmas + NST>();
-    else if (after == 1) dma_barrier<kPfDmas + NST>();
-    else dma_barrier<NST>();
-  } else {
-    if (after >= 2) dma_barrier<2 * kPfDmas>();
-    else if (after == 1) dma_barrier<kPfDmas>();
-    else dma_barrier<0>();
-  }
+// `after` = K steps whose DMAs this wave issued after the one to wait for
+// (output stores issued after that DMA are waited for as well: the count
+// covers every vector-memory operation of the wave).
+__device__ __forceinline__ void step_barrier(int after) {
+  if (after >= 2) dma_barrier<2 * kPfDmas>();
+  else if (after == 1) dma_barrier<kPfDmas>();
+  else dma_barrier<0>();
 }
 
 // One K step of one wave: 8 weight tiles x 2 token tiles of MFMAs.  All of
@@ -237,10 +222,11 @@ __device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, cons
   return d;
 }
 
-// Output stores as inline assembly too, a fixed number per wave and item
-// (lanes with nothing to store use an offset past the buffer, which drops
-// the write), so that the waits of the next item's first steps can count
-// them.  The compiler's hazard checks do not look inside inline assembly, so
+// Output stores as inline assembly too (lanes with nothing to store use an
+// offset past the buffer, which drops the write).  The stage waits count
+// every vector-memory operation of the wave, so the waits of the next item's
+// first steps, issued after these stores, wait for them as well.  The
+// compiler's hazard checks do not look inside inline assembly, so
 // these carry their own: the data must not come straight from an MFMA (whose
 // result may still be in flight), so st16 takes it through a VALU add (+0
 // turns -0 into +0) that the compiler orders after the MFMA, with two wait
@@ -257,8 +243,6 @@ __device__ __forceinline__ void st4(const v4i& r, uint32_t voff, uint32_t v) {
 __device__ __forceinline__ void st1(const v4i& r, uint32_t voff, uint32_t v) {
   asm volatile("buffer_store_byte %0, %1, %2, 0 offen\n\ts_nop 3" ::"v"(v), "v"(voff), "s"(r) : "memory");
 }
-constexpr int kPfStoresFc1 = 12;   // 2 token tiles x 2 MXFP8 blocks x (2 code dwords + 1 scale byte)
-constexpr int kPfStoresFc2 = 16;   // 2 token tiles x 2 column halves x 4 row groups of fp32
 static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
@@ -270,11 +254,9 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
   const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
   if constexpr (FC1) {
     const int I = a.N;
-    const cptr ag_p = (cptr)a.alpha_g, au_p = (cptr)a.alpha_u;
-    const float ag = a.alpha_g ? __builtin_bit_cast(float, ag_p[x.l]) : 1.0f;
-    const float au = a.alpha_u ? __builtin_bit_cast(float, au_p[x.l]) : 1.0f;
-    const SituK sk = situ_consts(ag, au, __builtin_bit_cast(float, ((cptr)a.beta)[x.l]),
-                                 __builtin_bit_cast(float, ((cptr)a.lbeta)[x.l]));
+    const ActItem ai = act_item(a, x.l);
+    const float blb = act_blb(ai.k);
+    const bool bridges = ai.lora || a.lora_out;   // uniform
     const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(TOK * I));
     const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
 #pragma unroll
@@ -282,27 +264,35 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
       if (tt >= ntt) break;                          // uniform: a tile of padding rows only
       const int pr = 32 * wm + 16 * tt + r;          // row within the m-tile
       const bool valid = x.p0 + pr < x.p1;
+      // the pair's expanded index: the row of its LoRA delta and down-LoRA input
+      const int64_t j = (bridges && valid) ? (int64_t)a.perm[x.p0 + pr] : 0;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {          // two 32-column MXFP8 blocks per wave
-        // h = q * b*lb with q = situ_q: the block maximum of |h| is b*lb times
-        // that of |q| (rounding is monotone), and h * 2^sh is q * (b*lb * 2^sh)
-        // in one product, exact whenever the block's scale leaves the elements
-        // that get a nonzero E4M3 code in fp32's normal range (sh <= 108);
-        // other blocks (all zero, or below 2^-100) take h and then 2^sh
+        // h = q * blb with q = act_q (SiTU: blb = b*lb, else 1): the block
+        // maximum of |h| is blb times that of |q| (rounding is monotone), and
+        // h * 2^sh is q * (blb * 2^sh) in one product, exact whenever the
+        // block's scale leaves the elements that get a nonzero E4M3 code in
+        // fp32's normal range (sh <= 108); other blocks (all zero, or below
+        // 2^-100) take h and then 2^sh
+        const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
         float qv[2][4];
         float amax = 0.0f;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int i = 2 * blk + h2;
+          float xg[4], xu[4];
+          const float ag4[4] = {acc[i][tt][0], acc[i][tt][1], acc[i][tt][2], acc[i][tt][3]};
+          const float au4[4] = {acc[4 + i][tt][0], acc[4 + i][tt][1], acc[4 + i][tt][2], acc[4 + i][tt][3]};
+          act_inputs(ai, a.lora_delta + j * (2 * I) + col0 + 16 * h2 + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 2 * blk + h2;
-            qv[h2][e] = situ_q(acc[i][tt][e], acc[4 + i][tt][e], sk);
+            qv[h2][e] = act_q(xg[e], xu[e], ai.k);
             amax = fmaxf(amax, fabsf(qv[h2][e]));
           }
+        }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
-        const uint32_t code = e8m0_code_for_e4m3(amax * sk.blb);
+        const uint32_t code = e8m0_code_for_e4m3(amax * blb);
         const int sh = 127 - (int)code;
         // rows past the group are not stored: their blocks do not matter
         const bool direct = __builtin_amdgcn_ballot_w64(valid && sh > 108) == 0;   // uniform
@@ -312,7 +302,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
         // sign (code 0x80, the value zero)
         float sv[2][4];
         if (direct) {
-          const float scl = __builtin_ldexpf(sk.blb, sh);
+          const float scl = __builtin_ldexpf(blb, sh);
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -321,7 +311,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[h2][e] = __builtin_ldexpf(qv[h2][e] * sk.blb, sh);
+            for (int e = 0; e < 4; ++e) sv[h2][e] = __builtin_ldexpf(qv[h2][e] * blb, sh);
         }
         uint32_t packed[2];
 #pragma unroll
@@ -335,6 +325,11 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
         st4(hr, ho, packed[0]);
         st4(hr, valid ? ho + 16u : kOobPf, packed[1]);
         st1(sr, (valid && g == 0) ? (uint32_t)(pr * (I / 32) + col0 / 32) : kOobPf, code);
+        if (a.lora_out && valid) {   // the down LoRA's input: h as bf16 by expanded index
+          uint16_t* lrow = a.lora_out + j * I + col0 + 4 * g;
+          *reinterpret_cast<uint2*>(lrow) = e4m3x4_to_bf16x4(packed[0], (int)code);
+          *reinterpret_cast<uint2*>(lrow + 16) = e4m3x4_to_bf16x4(packed[1], (int)code);
+        }
       }
     }
   } else {
@@ -378,20 +373,8 @@ template <bool FC1>
 __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) uint8_t st0[kStage];
   __shared__ __align__(16) uint8_t st1[kStage];
-#if SITU_PF_STAGES > 2
   __shared__ __align__(16) uint8_t st2[kStage];
-#endif
-#if SITU_PF_STAGES > 3
-  __shared__ __align__(16) uint8_t st3[kStage];
-#endif
-#if SITU_PF_STAGES == 2
-  uint8_t* const stg[kPfStages] = {st0, st1};
-#elif SITU_PF_STAGES == 3
   uint8_t* const stg[kPfStages] = {st0, st1, st2};
-#else
-  uint8_t* const stg[kPfStages] = {st0, st1, st2, st3};
-#endif
-  constexpr int NST = FC1 ? kPfStoresFc1 : kPfStoresFc2;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int r = lane & 15, g = lane >> 4;
@@ -409,9 +392,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
 
   // The ring restarts at stage 0 for every item; the next item's first
   // kPfStages - 1 stages are requested before this item's output stores, so
-  // their latency overlaps the epilogue.  `stores_after` marks an item whose
-  // first stages were requested before the previous item's NST stores: the
-  // waits of its first steps count those stores too.
+  // their latency overlaps the epilogue; the waits of its first steps then
+  // also wait for the previous item's output stores.
   int it = i_begin + slot;
   PfItem cur{0, 0, 0, 0};
   PfGeo d{};
@@ -423,7 +405,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
     for (int u = 0; u < kPfStages - 1; ++u)
       if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
   }
-  bool stores_after = false;
   for (; it < i_end; it += per_xcd_wgs) {
     // the next item's geometry (scalar loads) while the first stages load
     const int it_next = it + per_xcd_wgs;
@@ -443,7 +424,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
       for (int u = 0; u < kPfStages; ++u) {
         const int j = j0 + u;
         if (j < steps) {
-          step_barrier<NST>(min(kPfStages - 2, steps - 1 - j), SITU_PF_COUNT_STORES && stores_after && j < kPfStages - 1);
+          step_barrier(min(kPfStages - 2, steps - 1 - j));
           if (j + kPfStages - 1 < steps)
             pf_issue(lds_addr_of(stg[(u + kPfStages - 1) % kPfStages]), d, j + kPfStages - 1, wave, lane);
           pf_compute(stg[u], FC1, wn, wm, lane, acc);
@@ -459,9 +440,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
       for (int u = 0; u < kPfStages - 1; ++u)
         if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
     }
-    // exactly NST stores per wave; the last stage is free for FC2's transpose
+    // the last stage is free for FC2's transpose
     pf_epilogue<FC1>(a, cur, acc, wn, wm, wave, lane, stg[kPfStages - 1] + wave * 4352);
-    stores_after = true;
     cur = nxt;
   }
 }
@@ -854,10 +834,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
 namespace {
 
 constexpr int kSMaxSteps = 3;
-#ifndef SITU_FC2S_NT_PER_ITEM
-#define SITU_FC2S_NT_PER_ITEM 2
-#endif
-constexpr int kSNtPerItem = SITU_FC2S_NT_PER_ITEM;            // n-tiles per work item
+constexpr int kSNtPerItem = 2;                                // n-tiles per work item
 constexpr int kSH = 0;                                        // activations: [step][8 token tiles]
 constexpr int kSHS = kSH + kSMaxSteps * 8 * kWTileSw;         // [8 token tiles][step][16 tokens] scale dwords
 constexpr int kSW = kSHS + 8 * kSMaxSteps * 16 * 4;           // two weight buffers
@@ -1056,14 +1033,7 @@ template hipError_t launch_prefill_wide<false>(const GemmArgs&, int, int, hipStr
 
 template <bool FC1>
 hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
-  static int per_cu = 0;
-  if (!per_cu) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_gemm_kernel<FC1>, kGemmThreads, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(prefill_gemm_kernel<FC1>), kGemmThreads, 0);
   const int n_tiles = FC1 ? a.N / 128 : (a.N + kPfRows - 1) / kPfRows;
   const int64_t work = (int64_t)max_mtiles * n_tiles;
   int64_t grid = (int64_t)cus * per_cu;

@@ -100,6 +100,13 @@ situ_status validate(const situ_moe_problem* p) {
   if (p->topk_packed != 0 && p->topk_packed != 1) return fail(SITU_E_BAD_SHAPE, "topk_packed must be 0 or 1");
   if (p->out_dtype != SITU_OUT_F32 && p->out_dtype != SITU_OUT_BF16)
     return fail(SITU_E_UNSUPPORTED, "out_dtype %d", p->out_dtype);
+  if (p->activation != SITU_ACTIVATION_SITU && p->activation != SITU_ACTIVATION_SWIGLU &&
+      p->activation != SITU_ACTIVATION_SWIGLU_BIAS)
+    return fail(SITU_E_UNSUPPORTED, "activation %d", p->activation);
+  if (p->weight_format != SITU_WEIGHTS_MXFP4 && p->weight_format != SITU_WEIGHTS_NVFP4)
+    return fail(SITU_E_UNSUPPORTED, "weight_format %d", p->weight_format);
+  if (p->weight_format == SITU_WEIGHTS_NVFP4 && p->act_mode != SITU_ACT_W4A16)
+    return fail(SITU_E_UNSUPPORTED, "NVFP4 weights are served with bf16 activations (w4a16) only");
   const int64_t tk = (int64_t)p->num_tokens * p->top_k;
   if (tk >= (int64_t)1 << 31) return fail(SITU_E_UNSUPPORTED, "num_tokens * top_k = %lld exceeds int32", (long long)tk);
   // activation rows are addressed with 32-bit offsets from one buffer resource
@@ -187,10 +194,25 @@ situ_status check_run_args(const situ_moe_plan_t* plan, const situ_moe_tensors* 
     if (p.act_prequantized && !t->hidden_states_scale)
       return fail(SITU_E_MISSING_SCALE, "w4a8 prequantized input needs hidden_states_scale");
     if (!t->w1 || !t->w1_scale || !t->w2 || !t->w2_scale) return fail(SITU_E_NULL_ARG, "a weight or scale is NULL");
-    if (!t->situ_beta || !t->situ_linear_beta)
+    if (p.activation == SITU_ACTIVATION_SITU && (!t->situ_beta || !t->situ_linear_beta))
       return fail(SITU_E_NULL_ARG, "SiTU needs situ_beta and situ_linear_beta (no default is substituted)");
+    if (p.activation == SITU_ACTIVATION_SWIGLU_BIAS && (!t->swiglu_alpha || !t->swiglu_beta))
+      return fail(SITU_E_NULL_ARG, "SwigluBias needs swiglu_alpha and swiglu_beta (no default is substituted)");
     if (!t->out) return fail(SITU_E_NULL_ARG, "out is NULL");
   }
+  // the kernels move rows in 16-byte pieces from these bases (and 4-byte
+  // words from the per-expert parameter arrays)
+  const struct { const void* ptr; const char* name; uintptr_t align; } ptrs[] = {
+      {t->hidden_states, "hidden_states", 16}, {t->hidden_states_scale, "hidden_states_scale", 16},
+      {t->topk_ids, "topk_ids", 16}, {t->topk_weights, "topk_weights", 16}, {t->topk_packed, "topk_packed", 16},
+      {t->w1, "w1", 16}, {t->w1_scale, "w1_scale", 16}, {t->w2, "w2", 16}, {t->w2_scale, "w2_scale", 16},
+      {t->out, "out", 16}, {t->situ_beta, "situ_beta", 4}, {t->situ_linear_beta, "situ_linear_beta", 4},
+      {t->alpha_gate, "alpha_gate", 4}, {t->alpha_up, "alpha_up", 4}, {t->swiglu_alpha, "swiglu_alpha", 4},
+      {t->swiglu_beta, "swiglu_beta", 4}, {t->alpha_down, "alpha_down", 4},
+      {t->gate_up_lora_delta, "gate_up_lora_delta", 16}, {t->activation_lora_input, "activation_lora_input", 16}};
+  for (const auto& q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q.ptr) % q.align)
+      return fail(SITU_E_BAD_SHAPE, "%s must be %u-byte aligned", q.name, (unsigned)q.align);
   if (!ws && plan->workspace_bytes) return fail(SITU_E_WORKSPACE, "workspace is NULL");
   if (ws_bytes < plan->workspace_bytes)
     return fail(SITU_E_WORKSPACE, "workspace %llu bytes < %llu needed", (unsigned long long)ws_bytes,
@@ -369,10 +391,14 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.tile_expert = ra.tile_expert;
   g.tile_rows = ra.tile_rows;
   g.E_l = p.local_num_experts;
-  g.beta = t->situ_beta;
-  g.lbeta = t->situ_linear_beta;
+  g.act_kind = p.activation;   // the SITU_ACTIVATION_* values are the kernels' kAct* kinds
+  g.beta = p.activation == SITU_ACTIVATION_SITU ? t->situ_beta
+                                                : p.activation == SITU_ACTIVATION_SWIGLU_BIAS ? t->swiglu_alpha : nullptr;
+  g.lbeta = p.activation == SITU_ACTIVATION_SITU ? t->situ_linear_beta
+                                                 : p.activation == SITU_ACTIVATION_SWIGLU_BIAS ? t->swiglu_beta : nullptr;
   g.alpha_g = t->alpha_gate;
   g.alpha_u = t->alpha_up;
+  g.nvfp4 = p.weight_format == SITU_WEIGHTS_NVFP4 ? 1 : 0;
 
   // FC1 + SiTU
   g.act = act;
@@ -385,6 +411,12 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.N = (int32_t)I;
   g.out = at<void>(ws, plan->off_h);
   g.out_scale = w4a8 ? at<uint8_t>(ws, plan->off_hs) : nullptr;
+  g.lora_delta = t->gate_up_lora_delta;
+  g.lora_out = t->activation_lora_input;
+  if (t->activation_lora_input &&
+      (st = launch_status(situ::launch_zero_nonlocal_rows(ra.inv, t->activation_lora_input, (int64_t)T * p.top_k,
+                                                          (int32_t)I, s), "lora rows")) != SITU_OK)
+    return st;
   if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, plan->max_mtiles, cus, s), "fc1")) != SITU_OK) return st;
   if ((st = mark(3)) != SITU_OK) return st;
 
@@ -392,6 +424,8 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.act = at<void>(ws, plan->off_h);
   g.act_scale = w4a8 ? at<uint8_t>(ws, plan->off_hs) : nullptr;
   g.perm = nullptr;
+  g.lora_delta = nullptr;
+  g.lora_out = nullptr;
   g.w = t->w2;
   g.ws = t->w2_scale;
   g.K = (int32_t)I;
@@ -408,7 +442,8 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
                       y16 ? at<uint8_t>(ws, plan->off_y_exp) : nullptr, ra.inv,
                       p.topk_packed ? nullptr : t->topk_weights,
                       p.topk_packed ? t->topk_packed : nullptr, t->out, T, (int32_t)H, p.top_k,
-                      p.out_dtype == SITU_OUT_BF16 ? 1 : 0};
+                      p.out_dtype == SITU_OUT_BF16 ? 1 : 0, t->alpha_down,
+                      p.topk_packed ? nullptr : t->topk_ids, p.local_expert_offset};
   if ((st = launch_status(situ::launch_combine(c, s), "combine")) != SITU_OK) return st;
   return mark(5);
 }

@@ -26,12 +26,22 @@
  *    moeOp.cpp: SiTU's beta arrays are required, never defaulted.
  *  - "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT -- Kimi-K3 SiTU" release
  *    notes, "Changes since 875b7d7": per-expert beta and linear beta; the up
- *    half rescaled by alpha_up / alpha_gate before the tanh.
+ *    half rescaled by alpha_up / alpha_gate before the tanh; the decomposed
+ *    MoE-LoRA op takes a gate_up LoRA delta (added to the FC1 output before
+ *    the activation) and hands back the activation input of the down LoRA,
+ *    and runs the plain pipeline when both are empty.
+ *  - pull request 17865, review of test_kimi_k3_situ_moe.py: the same
+ *    routed skeleton with the SwiGLU and CUTLASS SwigluBias activations
+ *    (gate * sigmoid(gate * alpha) * (linear + beta)); the NVFP4 Kimi-K3
+ *    checkpoint (E2M1 weights with E4M3 scales per 16 elements and a
+ *    per-tensor scale, here the per-expert alphas).
  *
  * Conventions for every entry point:
  *  - Plain C.  Pointers marked (device) are HIP device pointers, (host) are
- *    host pointers.  All arrays are dense, row-major, naturally aligned;
- *    device arrays of 16 bytes or more per row must be 16-byte aligned.
+ *    host pointers.  All arrays are dense and row-major.  The device arrays
+ *    of situ_moe_tensors must be 16-byte aligned, except the per-expert
+ *    float arrays (4-byte aligned); situ_moe_run returns SITU_E_BAD_SHAPE
+ *    otherwise.
  *  - The caller owns every buffer: inputs, the output and the workspace.
  *    The library allocates no device memory and holds no device state.
  *  - Every function returns situ_status; no exception crosses the ABI.  On
@@ -49,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SITU_MOE_ABI_VERSION 1
+#define SITU_MOE_ABI_VERSION 2
 
 typedef enum situ_status {
   SITU_OK = 0,
@@ -64,6 +74,14 @@ typedef enum situ_status {
 
 enum { SITU_ACT_W4A16 = 0, SITU_ACT_W4A8 = 1 };
 enum { SITU_OUT_F32 = 0, SITU_OUT_BF16 = 1 };
+/* Gated activation h = act(g, u) of g = alpha_gate * acc_gate, u = alpha_up * acc_up:
+ *  SiTU        [beta * tanh(g / beta) * sigmoid(g)] * [lbeta * tanh(u / lbeta)]
+ *  SwiGLU      g * sigmoid(g) * u
+ *  SwigluBias  g * sigmoid(g * swiglu_alpha) * (u + swiglu_beta)          */
+enum { SITU_ACTIVATION_SITU = 0, SITU_ACTIVATION_SWIGLU = 1, SITU_ACTIVATION_SWIGLU_BIAS = 2 };
+/* Expert weight format: MXFP4 = E2M1 + E8M0 scale per 32 along K;
+ * NVFP4 = E2M1 + E4M3 scale per 16 along K (w4a16 only). */
+enum { SITU_WEIGHTS_MXFP4 = 0, SITU_WEIGHTS_NVFP4 = 1 };
 
 /* The runtime shape of one shard (host POD). */
 typedef struct situ_moe_problem {
@@ -80,6 +98,8 @@ typedef struct situ_moe_problem {
   int32_t out_dtype;            /* SITU_OUT_F32 or SITU_OUT_BF16 (round-to-nearest-even of the fp32 result) */
   int32_t tactic_fc1;           /* -1 = first valid; else a value from situ_moe_valid_tactics */
   int32_t tactic_fc2;           /* -1 = first valid */
+  int32_t activation;           /* SITU_ACTIVATION_* */
+  int32_t weight_format;        /* SITU_WEIGHTS_* */
 } situ_moe_problem;
 
 /* A resolved plan (host POD, reusable, no device state).  The workspace
@@ -123,15 +143,28 @@ typedef struct situ_moe_tensors {
   const int32_t* topk_ids;            /* (device) int32 [T, k], GLOBAL ids; any id outside the shard is skipped */
   const uint16_t* topk_weights;       /* (device) bf16 [T, k] routing weights, applied in the combine */
   const int32_t* topk_packed;         /* (device) int32 [T, k] = (bf16 weight bits << 16) | (id & 0xFFFF); topk_packed only */
-  const uint8_t* w1;                  /* (device) MXFP4 [E_l, 2I, H/2]: rows [0,I) gate, [I,2I) up; low nibble = even k */
-  const uint8_t* w1_scale;            /* (device) E8M0 [E_l, 2I, H/32] */
-  const uint8_t* w2;                  /* (device) MXFP4 [E_l, H, I/2] */
-  const uint8_t* w2_scale;            /* (device) E8M0 [E_l, H, I/32] */
-  const float* situ_beta;             /* (device) float [E_l], required */
-  const float* situ_linear_beta;      /* (device) float [E_l], required */
+  const uint8_t* w1;                  /* (device) E2M1 [E_l, 2I, H/2]: rows [0,I) gate, [I,2I) up; low nibble = even k */
+  const uint8_t* w1_scale;            /* (device) MXFP4: E8M0 [E_l, 2I, H/32]; NVFP4: E4M3 [E_l, 2I, H/16] */
+  const uint8_t* w2;                  /* (device) E2M1 [E_l, H, I/2] */
+  const uint8_t* w2_scale;            /* (device) MXFP4: E8M0 [E_l, H, I/32]; NVFP4: E4M3 [E_l, H, I/16] */
+  const float* situ_beta;             /* (device) float [E_l]; required with SiTU, else ignored */
+  const float* situ_linear_beta;      /* (device) float [E_l]; required with SiTU, else ignored */
   const float* alpha_gate;            /* (device) float [E_l] or NULL (= 1.0) */
   const float* alpha_up;              /* (device) float [E_l] or NULL (= 1.0) */
   void* out;                          /* (device) [T, H] float or bf16 per out_dtype; every element is written */
+  /* ABI 2 */
+  const float* swiglu_alpha;          /* (device) float [E_l]; required with SwigluBias, else ignored */
+  const float* swiglu_beta;           /* (device) float [E_l]; required with SwigluBias, else ignored */
+  const float* alpha_down;            /* (device) float [E_l] or NULL (= 1.0): per-expert scale of the FC2
+                                         output (the NVFP4 per-tensor scale of w2), applied to the routing
+                                         weight in the combine as one fp32 product */
+  const uint16_t* gate_up_lora_delta; /* (device) bf16 [T*k, 2I] or NULL: a LoRA adapter's FC1 output for
+                                         pair j = t*k + s (gate columns, then up), added in fp32 to the
+                                         alpha-scaled halves before the activation; rows of pairs outside
+                                         the shard are not read */
+  uint16_t* activation_lora_input;    /* (device) bf16 [T*k, I] or NULL: receives h of pair j (the input of
+                                         the down LoRA, after the rounding point; exact in bf16 in both
+                                         modes), zero rows for pairs outside the shard */
 } situ_moe_tensors;
 
 /* Validate a problem and resolve its tactics, block size and workspace

@@ -226,7 +226,36 @@ def mx_dequantize(codes, scale_codes, elem, block=SCALE_BLOCK):
     return vals * np.repeat(decode_e8m0(scale_codes), block, axis=-1)
 
 
+# The two E2M1 values of every byte value, [256, 2] (low nibble first), built
+# from unpack_fp4 and decode_e2m1 above; decoding a packed matrix is then one
+# table lookup per byte.
+_FP4_BYTE_VALUES = decode_e2m1(unpack_fp4(np.arange(256, dtype=np.uint8)[:, None], 2))
+
+
+def _dequant_fp4_blocks(packed, block_scales, block):
+    """Packed E2M1 matrix (..., K/2 bytes) times one float64 scale per `block`
+    consecutive elements along K (block_scales (..., K/block)) -> float64."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lead = packed.shape[:-1]
+    n = packed.shape[-1] * 2
+    vals = _FP4_BYTE_VALUES[packed].reshape(lead + (n // block, block))
+    return (vals * np.asarray(block_scales, np.float64)[..., None]).reshape(lead + (n,))
+
+
 def dequant_mxfp4(packed, scale_codes):
-    """Packed MXFP4 matrix (..., K/2 bytes) + scales (..., K/32) -> float64."""
-    n = np.asarray(packed).shape[-1] * 2
-    return mx_dequantize(unpack_fp4(packed, n), scale_codes, "e2m1")
+    """Packed MXFP4 matrix (..., K/2 bytes) + E8M0 scales (..., K/32) -> float64
+    (the same values as mx_dequantize of the unpacked codes)."""
+    return _dequant_fp4_blocks(packed, decode_e8m0(scale_codes), SCALE_BLOCK)
+
+
+# NVFP4: E2M1 elements with one E4M3 scale per 16 consecutive elements along
+# K (NVIDIA's NVFP4 layout; the pages name the format -- the Kimi-K3 NVFP4
+# checkpoint, the NVFP4 MoE-LoRA op -- without printing it).  A per-tensor
+# fp32 scale completes the format; in this layer it is the per-expert alpha
+# of each GEMM, applied outside the weight decode.
+NVFP4_BLOCK = 16
+
+
+def dequant_nvfp4(packed, scale_codes):
+    """Packed NVFP4 matrix (..., K/2 bytes) + E4M3 scales (..., K/16) -> float64."""
+    return _dequant_fp4_blocks(packed, decode_e4m3(scale_codes), NVFP4_BLOCK)

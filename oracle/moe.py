@@ -111,6 +111,50 @@ def situ(g, u, beta, linear_beta):
     return (beta * np.tanh(g / beta) * sigmoid(g)) * (linear_beta * np.tanh(u / linear_beta))
 
 
+def swiglu(g, u):
+    """SwiGLU: g * sigmoid(g) * u (the trusted fused SwiGLU the pages compare
+    SiTU against; also the limit of SiTU as both betas grow)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g * sigmoid(g) * np.asarray(u, dtype=np.float64)
+
+
+def swiglu_bias(g, u, alpha, beta):
+    """CUTLASS SwigluBias as the review of test_kimi_k3_situ_moe.py writes it
+    (pull request 17865, _swiglu_bias_act): gate * sigmoid(gate * alpha) *
+    (linear + beta), with per-expert alpha and beta."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    return g * sigmoid(g * np.float64(alpha)) * (u + np.float64(beta))
+
+
+ACTIVATIONS = ("situ", "swiglu", "swiglu_bias")
+
+
+def gated_activation(kind, g, u, p0, p1):
+    """h = act(g, u) for one expert: SiTU (p0 = beta, p1 = linear beta),
+    SwiGLU (no parameters) or SwigluBias (p0 = alpha, p1 = beta)."""
+    if kind == "situ":
+        return situ(g, u, p0, p1)
+    if kind == "swiglu":
+        return swiglu(g, u)
+    if kind == "swiglu_bias":
+        return swiglu_bias(g, u, p0, p1)
+    raise ValueError(kind)
+
+
+def activation_params(inp, kind, E_l):
+    """Per-expert (p0, p1) float32 arrays of the activation (zeros for SwiGLU,
+    which has none)."""
+    if kind == "situ":
+        return np.asarray(inp["situ_beta"], np.float32), np.asarray(inp["situ_linear_beta"], np.float32)
+    if kind == "swiglu":
+        z = np.zeros(E_l, np.float32)
+        return z, z
+    if kind == "swiglu_bias":
+        return np.asarray(inp["swiglu_alpha"], np.float32), np.asarray(inp["swiglu_beta"], np.float32)
+    raise ValueError(kind)
+
+
 # --------------------------------------------------------------------------
 # The layer
 
@@ -149,7 +193,8 @@ def topk_of(inp):
 
 def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16",
                 act_prequantized=False, precision="f64", rounding=True, tokens=None,
-                keep_intermediates=False):
+                keep_intermediates=False, activation="situ", weight_format="mxfp4", h_given=None,
+                want_act_lora=False):
     """Partial output of one shard of the routed MXFP4 + SiTU MoE layer.
 
     inp holds numpy arrays:
@@ -159,16 +204,31 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
       topk_packed int32 [T, k]
       w1 uint8 [E_l, 2I, H/2], w1_scale uint8 [E_l, 2I, H/32]
       w2 uint8 [E_l, H, I/2],  w2_scale uint8 [E_l, H, I/32]
-      situ_beta, situ_linear_beta float32 [E_l]
+        (weight_format "nvfp4": E4M3 scales [E_l, 2I, H/16] and [E_l, H, I/16])
+      situ_beta, situ_linear_beta float32 [E_l] (activation "situ"), or
+      swiglu_alpha, swiglu_beta float32 [E_l] (activation "swiglu_bias")
       alpha_gate, alpha_up float32 [E_l] or None (meaning 1.0)
+      alpha_down float32 [E_l] or None: per-expert scale of the FC2 output,
+        applied with the routing weight in the combine
+      gate_up_lora_delta uint16 bf16 bits [T*k, 2I] or None: a low-rank
+        adapter's contribution to the FC1 output of pair j = t*k + s, added
+        to the alpha-scaled gate and up halves before the activation
     tokens: optional array of token indices; only those rows are computed and
     returned (the layer is independent per token, routing is still global).
+    h_given: optional [P, I] FC1 outputs (after the rounding point) in
+    permuted order, used instead of computing FC1: the FC2 and combine of
+    given rows.
     Returns dict(out=float32 [len(tokens) or T, H], out_bf16=uint16 bits,
     counts, offsets, perm, inv, and with keep_intermediates the per-pair h
-    (float64 after R1) and y (float64) in permuted order for the computed pairs).
+    (float64 after R1) and y (float64) in permuted order for the computed
+    pairs; with want_act_lora the FC1 output rows by expanded index
+    [T*k, I] (float64, zero rows for pairs outside the shard or not computed).
     """
     if precision not in ("f64", "f32"):
         raise ValueError(precision)
+    if weight_format not in ("mxfp4", "nvfp4"):
+        raise ValueError(weight_format)
+    dequant = F.dequant_mxfp4 if weight_format == "mxfp4" else F.dequant_nvfp4
     E_l = int(local_num_experts)
     ids, wts = topk_of(inp)
     T, k = ids.shape
@@ -183,14 +243,15 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
     ones = np.ones(E_l, dtype=np.float32)
     a_g = ones if inp.get("alpha_gate") is None else np.asarray(inp["alpha_gate"], np.float32)
     a_u = ones if inp.get("alpha_up") is None else np.asarray(inp["alpha_up"], np.float32)
-    beta = np.asarray(inp["situ_beta"], np.float32)
-    lbeta = np.asarray(inp["situ_linear_beta"], np.float32)
+    a_d = None if inp.get("alpha_down") is None else np.asarray(inp["alpha_down"], np.float32)
+    p0, p1 = activation_params(inp, activation, E_l)
+    delta = inp.get("gate_up_lora_delta")
+    if delta is not None:
+        delta = F.bf16_to_f64(np.asarray(delta).reshape(T * k, 2 * I))
 
     if tokens is None:
         tokens = np.arange(T)
     tokens = np.asarray(tokens, dtype=np.int64)
-    want = np.zeros(T, dtype=bool)
-    want[tokens] = True
 
     dt = np.float64 if precision == "f64" else np.float32
     if precision == "f64" and rounding:
@@ -210,46 +271,66 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
     Hq = np.zeros((need.shape[0], I), dtype=np.float64) if keep_intermediates else None
     Acc = np.zeros((need.shape[0], 2 * I), dtype=np.float64) if keep_intermediates else None
     Hpre = np.zeros((need.shape[0], I), dtype=np.float64) if keep_intermediates else None
+    ActLora = np.zeros((T * k, I), dtype=np.float64) if want_act_lora else None
 
     for l in range(E_l):
-        p0, p1 = int(offsets[l]), int(offsets[l + 1])
-        pos = need[(need >= p0) & (need < p1)]
+        p_lo, p_hi = int(offsets[l]), int(offsets[l + 1])
+        pos = need[(need >= p_lo) & (need < p_hi)]
         if pos.shape[0] == 0:
             continue
-        rows_t = perm[pos] // k
-        xa = xf[rows_t].astype(dt)
-        W1d = F.dequant_mxfp4(w1[l], w1s[l]).astype(dt)           # [2I, H]
-        acc = rnd(xa @ W1d.T)                                      # [n, 2I]
-        if precision == "f64":
-            g = rnd(np.float64(a_g[l]) * acc[:, :I])
-            u = rnd(np.float64(a_u[l]) * acc[:, I:])
-            h = rnd(situ(g, u, beta[l], lbeta[l]))
-        else:
-            g = np.float32(a_g[l]) * acc[:, :I]
-            u = np.float32(a_u[l]) * acc[:, I:]
-            h = situ(g, u, beta[l], lbeta[l]).astype(np.float32)
-        if rounding:
-            if act_mode == "w4a16":
-                hq = F.bf16_to_f64(F.f32_to_bf16_rne(_f32(h)))
+        if h_given is None:
+            rows_t = perm[pos] // k
+            xa = xf[rows_t].astype(dt)
+            W1d = dequant(w1[l], w1s[l]).astype(dt, copy=False)    # [2I, H]
+            acc = rnd(xa @ W1d.T)                                  # [n, 2I]
+            if precision == "f64":
+                g = rnd(np.float64(a_g[l]) * acc[:, :I])
+                u = rnd(np.float64(a_u[l]) * acc[:, I:])
+                if delta is not None:
+                    g = rnd(g + delta[perm[pos], :I])
+                    u = rnd(u + delta[perm[pos], I:])
+                h = rnd(gated_activation(activation, g, u, p0[l], p1[l]))
             else:
-                hc, hs = F.mx_quantize(np.asarray(h, np.float64), "e4m3")
-                hq = F.mx_dequantize(hc, hs, "e4m3")
+                g = np.float32(a_g[l]) * acc[:, :I]
+                u = np.float32(a_u[l]) * acc[:, I:]
+                if delta is not None:
+                    g = g + delta[perm[pos], :I].astype(np.float32)
+                    u = u + delta[perm[pos], I:].astype(np.float32)
+                h = gated_activation(activation, g, u, p0[l], p1[l]).astype(np.float32)
+            if rounding:
+                if act_mode == "w4a16":
+                    hq = F.bf16_to_f64(F.f32_to_bf16_rne(_f32(h)))
+                else:
+                    hc, hs = F.mx_quantize(np.asarray(h, np.float64), "e4m3")
+                    hq = F.mx_dequantize(hc, hs, "e4m3")
+            else:
+                hq = np.asarray(h, np.float64)
         else:
-            hq = np.asarray(h, np.float64)
-        W2d = F.dequant_mxfp4(w2[l], w2s[l]).astype(dt)            # [H, I]
+            hq = np.asarray(h_given, np.float64)[pos]
+        W2d = dequant(w2[l], w2s[l]).astype(dt, copy=False)        # [H, I]
         Y[compact[pos]] = rnd(hq.astype(dt) @ W2d.T)               # [n, H]
         if keep_intermediates:
             Hq[compact[pos]] = hq
-            Acc[compact[pos]] = acc
-            Hpre[compact[pos]] = np.asarray(h, np.float64)
+            if h_given is None:
+                Acc[compact[pos]] = acc
+                Hpre[compact[pos]] = np.asarray(h, np.float64)
+        if want_act_lora:
+            ActLora[perm[pos]] = hq
 
     # Combine in slot order; a token with no local slot keeps its zero row.
+    # The FC2 output scale alpha_down, where given, multiplies the routing
+    # weight (one fp32 product per slot).
     out = np.zeros((tokens.shape[0], H), dtype=np.float64)
     for s in range(k):
         p = slot_pos[:, s]
         has = p >= 0
         if has.any():
-            out[has] += wts[tokens[has], s][:, None] * Y[compact[p[has]]].astype(np.float64)
+            wsl = wts[tokens[has], s]
+            if a_d is not None:
+                wsl = wsl * a_d[ids[tokens[has], s] - int(local_expert_offset)].astype(np.float64)
+                if rounding or precision == "f32":
+                    wsl = _f32(wsl).astype(np.float64)
+            out[has] += wsl[:, None] * Y[compact[p[has]]].astype(np.float64)
     out32 = _f32(out) if (rounding or precision == "f32") else out
     res = dict(out=out32, counts=counts, offsets=offsets, perm=perm, inv=inv, P=P,
                tokens=tokens)
@@ -257,10 +338,13 @@ def moe_forward(inp, *, local_expert_offset, local_num_experts, act_mode="w4a16"
         res["out_bf16"] = F.f32_to_bf16_rne(out32)
     if keep_intermediates:
         res["pairs"] = need          # permuted positions of the rows below
-        res["acc"] = Acc
-        res["h_pre"] = Hpre        # SiTU output before the rounding point R1
         res["h"] = Hq
         res["y"] = Y.astype(np.float64)
+        if h_given is None:
+            res["acc"] = Acc
+            res["h_pre"] = Hpre        # activation output before the rounding point R1
+    if want_act_lora:
+        res["act_lora"] = ActLora
     return res
 
 

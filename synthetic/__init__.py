@@ -100,6 +100,24 @@ def draw_mxfp4(seed_words, rows, K):
     return _BYTE_TABLE[idx], (np.uint8(_SCALE_CODES[0]) + sidx).astype(np.uint8)
 
 
+# NVFP4 weights (E2M1 with an E4M3 scale per 16 along K) are drawn in the
+# encoded domain as well: elements from the middle table above, block scales
+# uniformly from the E4M3 codes of [0.5, 2) (0x30..0x3F), and the per-tensor
+# scale that makes them stand for N(0, 0.02) weights (2^-7) goes into the
+# per-expert alphas.
+NVFP4_TENSOR_SCALE = 2.0 ** -7
+
+
+def draw_nvfp4(seed_words, rows, K):
+    """One NVFP4 matrix [rows, K]: (packed bytes [rows, K/2], E4M3 scale codes [rows, K/16])."""
+    assert K % 32 == 0
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed_words)))
+    sc = (0x30 + rng.integers(0, 16, size=(rows, K // 16))).astype(np.uint8)
+    bits = np.frombuffer(rng.bytes(rows * (K // 2) * 2), dtype=np.uint16).reshape(rows, K // 2)
+    idx = (np.int32(1) << 16) | bits.astype(np.int32)      # the scale-120 element table
+    return _BYTE_TABLE[idx], sc
+
+
 def bf16_truncate(x):
     """float32 -> bf16 bit pattern by keeping the upper 16 bits."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
@@ -132,6 +150,9 @@ def spec_of(cfg):
     s.setdefault("seed", 0)
     s.setdefault("n_dead", 0)
     s.setdefault("no_local_frac", 0.0)
+    s.setdefault("activation", "situ")
+    s.setdefault("weight_format", "mxfp4")
+    s.setdefault("lora", False)
     return s
 
 
@@ -156,6 +177,12 @@ def generate(cfg, weights=True):
     situ_beta, situ_linear_beta, alpha_gate, alpha_up (float32 [E_l]); spec.
     With weights=False the expert weights are skipped (routing-only use); the
     draws after them then differ, so such inputs are never mixed with full ones.
+    Spec options drawn after everything above (so they leave those draws
+    unchanged): activation "swiglu_bias" adds swiglu_alpha ~ U[0.5, 2] and
+    swiglu_beta ~ U[0.5, 1.5]; weight_format "nvfp4" draws NVFP4 weights, folds
+    the per-tensor scale into alpha_gate / alpha_up and adds alpha_down (the
+    same scale times U[0.8, 1.2]); lora adds gate_up_lora_delta, bf16
+    [T*k, 2I] ~ N(0, 0.05), a LoRA adapter's FC1 contribution per pair.
     """
     s = spec_of(cfg)
     T, H, I, E_g, E_l, off, k = (s[x] for x in ("T", "H", "I", "E_g", "E_l", "off", "k"))
@@ -206,12 +233,18 @@ def generate(cfg, weights=True):
         w2 = np.empty((E_l, H, I // 2), dtype=np.uint8)
         w2s = np.empty((E_l, H, I // 32), dtype=np.uint8)
 
+        nv = s["weight_format"] == "nvfp4"
+        if nv:
+            w1s = np.empty((E_l, 2 * I, H // 16), dtype=np.uint8)
+            w2s = np.empty((E_l, H, I // 16), dtype=np.uint8)
+        draw = draw_nvfp4 if nv else draw_mxfp4
+
         def fill(job):
             which, l = job
             if which == 1:
-                w1[l], w1s[l] = draw_mxfp4([s["seed"], 1, l], 2 * I, H)
+                w1[l], w1s[l] = draw([s["seed"], 1, l], 2 * I, H)
             else:
-                w2[l], w2s[l] = draw_mxfp4([s["seed"], 2, l], H, I)
+                w2[l], w2s[l] = draw([s["seed"], 2, l], H, I)
 
         jobs = [(1, l) for l in range(E_l)] + [(2, l) for l in range(E_l)]
         with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
@@ -221,4 +254,14 @@ def generate(cfg, weights=True):
     out["situ_linear_beta"] = rng.uniform(0.5, 2.0, E_l).astype(np.float32)
     out["alpha_gate"] = rng.uniform(0.8, 1.2, E_l).astype(np.float32)
     out["alpha_up"] = rng.uniform(0.8, 1.2, E_l).astype(np.float32)
+    if s["activation"] == "swiglu_bias":
+        out["swiglu_alpha"] = rng.uniform(0.5, 2.0, E_l).astype(np.float32)
+        out["swiglu_beta"] = rng.uniform(0.5, 1.5, E_l).astype(np.float32)
+    if s["weight_format"] == "nvfp4":
+        g = np.float32(NVFP4_TENSOR_SCALE)
+        out["alpha_gate"] = (out["alpha_gate"] * g).astype(np.float32)
+        out["alpha_up"] = (out["alpha_up"] * g).astype(np.float32)
+        out["alpha_down"] = (rng.uniform(0.8, 1.2, E_l).astype(np.float32) * g).astype(np.float32)
+    if s["lora"]:
+        out["gate_up_lora_delta"] = bf16_truncate(rng.standard_normal((T * k, 2 * I), dtype=np.float32) * 0.05)
     return out

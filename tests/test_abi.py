@@ -30,9 +30,9 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert B.situ_moe_abi_version() == 1
+    assert B.situ_moe_abi_version() == B.ABI_VERSION == 2
     info = B.situ_moe_build_info()
-    assert "gfx950" in info and "abi 1" in info
+    assert "gfx950" in info and "abi 2" in info
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -105,6 +105,12 @@ def _status(fn):
     (dict(tactic=(0, -1)), "SITU_OK"),
     (dict(num_tokens=0), "SITU_OK"),
     (dict(num_tokens=300000), "SITU_E_UNSUPPORTED"),   # 2.15 GB of hidden states
+    (dict(activation="swiglu"), "SITU_OK"),
+    (dict(activation="swiglu_bias", act_mode="w4a8"), "SITU_OK"),
+    (dict(activation=3), "SITU_E_UNSUPPORTED"),
+    (dict(weight_format="nvfp4"), "SITU_OK"),
+    (dict(weight_format="nvfp4", act_mode="w4a8"), "SITU_E_UNSUPPORTED"),   # NVFP4 with bf16 activations only
+    (dict(weight_format=2), "SITU_E_UNSUPPORTED"),
 ])
 def test_plan_validation(kw, want):
     assert _status(lambda: B.situ_moe_plan(_prob(**kw))) == want
@@ -180,6 +186,19 @@ def test_run_argument_errors_before_any_device_work():
     assert run(plan8, ws_bytes=plan8.workspace_bytes) == 4      # MXFP8 input without its scales
     assert lib.situ_moe_run(None, None, None, 0, None) == 1
     assert "NULL" in B.situ_moe_last_error() or "null" in B.situ_moe_last_error().lower()
+    # 16-byte alignment of the row arrays, 4-byte of the per-expert floats
+    assert run(plan, w1=fake + 8) == 2 and "w1" in B.situ_moe_last_error()
+    assert run(plan, hidden_states=fake + 2) == 2
+    assert run(plan, out=fake + 4) == 2
+    assert run(plan, alpha_gate=fake + 4) != 2              # 4-byte aligned floats pass the alignment check
+    assert run(plan, situ_beta=fake + 2) == 2
+    assert run(plan, gate_up_lora_delta=fake + 8) == 2
+    # SwigluBias needs its two parameter arrays; SwiGLU needs none, SiTU's betas are then ignored
+    pb = _prob(num_tokens=4, hidden_size=256, intermediate_size=64, num_experts=8, local_num_experts=8, top_k=2,
+               activation="swiglu_bias")
+    planb = B.situ_moe_plan(pb)
+    assert run(planb, ws_bytes=planb.workspace_bytes) == 1
+    assert run(planb, ws_bytes=planb.workspace_bytes, swiglu_alpha=fake) == 1
 
 
 def test_no_device_reports_device_error():

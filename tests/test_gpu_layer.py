@@ -1,11 +1,14 @@
 """GPU parity of the HIP layer against the CPU oracle, through the C ABI.
 
 Bit-exact: routing (counts, offsets, perm, inv) and the MXFP8 quantizer.
-Within the parity bar (cosine >= 0.9995, max-abs <= 1e-2 x RMS of the oracle,
-fp32 outputs): the whole layer, on small shapes that span several tiles and
-ragged tails, and on every benchmark workload at full size with the launch
-configuration the benchmark times (sampled tokens, plus properties that hold
-for every token).
+The layer (gpu_helpers.layer_check): every element of the FC1 output h is the
+oracle's rounding of its value, or -- only where that value lies within its
+tolerance of a rounding boundary -- another rounding inside the tolerance;
+the output is within the bar (cosine >= 0.9995, max-abs <= 1e-2 x RMS, fp32
+outputs, nothing discounted) against the oracle's FC2 and combine of the
+GPU's own h, and, on the benchmark workloads at full size (every token, in
+the launch configuration the benchmark times), against the plain oracle.
+Small shapes span several tiles, ragged tails and the m-tile boundaries.
 """
 
 import numpy as np
@@ -17,8 +20,8 @@ import synthetic as S
 from oracle import formats as F
 from oracle import moe as M
 
-from gpu_helpers import (config_inputs, dev, oracle_out, parity, read_y, rounding_allowance, run_layer, ws_region,
-                         y_rounding_allowance)
+from gpu_helpers import (check_h, config_inputs, dev, gpu_h, layer_check, oracle_out, parity, read_y, run_layer,
+                         ws_region)
 
 pytestmark = pytest.mark.gpu
 
@@ -204,8 +207,7 @@ def test_layer_parity_small(name, mode, bm):
     inp = S.generate(spec)
     tac = {("w4a16", 16): (0, 16), ("w4a16", 64): (1, 17), ("w4a8", 16): (2, 18), ("w4a8", 64): (3, 19)}[(mode, bm)]
     got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tac)
-    ref = oracle_out(inp, spec, mode=mode, keep=True)
-    parity(got, ref["out"], f"{name} {mode} m{bm}", rounding_allowance(inp, spec, ref, mode))
+    ref = layer_check(got, inp, spec, mode, plan, ws, what=f"{name} {mode} m{bm}")
     # tokens with no local slot are exact (+0) zero rows
     none = np.all(ref["inv"].reshape(spec["T"], spec["k"]) < 0, axis=1)
     assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
@@ -217,8 +219,7 @@ def test_layer_parity_small_w4a8_m128(name):
     inp = S.generate(spec)
     got, plan, ws, _ = run_layer(inp, spec, mode="w4a8", tactic=(4, 20))
     assert plan.block_m == 128
-    ref = oracle_out(inp, spec, mode="w4a8", keep=True)
-    parity(got, ref["out"], f"{name} w4a8 m128", rounding_allowance(inp, spec, ref, "w4a8"))
+    ref = layer_check(got, inp, spec, "w4a8", plan, ws, what=f"{name} w4a8 m128")
     none = np.all(ref["inv"].reshape(spec["T"], spec["k"]) < 0, axis=1)
     assert np.all(got[none] == 0) and not np.any(np.signbit(got[none]))
 
@@ -240,8 +241,7 @@ def test_layer_parity_decode_split_k(mode):
     tac = (0, 16) if mode == "w4a16" else (2, 18)
     got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tac)
     assert plan.block_m == 16
-    ref = oracle_out(inp, spec, mode=mode, keep=True)
-    parity(got, ref["out"], f"decode split-K {mode}", rounding_allowance(inp, spec, ref, mode))
+    layer_check(got, inp, spec, mode, plan, ws, what=f"decode split-K {mode}")
 
 
 # Groups whose sizes sit on and around the m-tile boundaries (16, 17, 32, 33,
@@ -278,19 +278,17 @@ def test_layer_parity_group_boundaries(I, mode, tactic):
     assert counts.tolist() == BOUNDARY_COUNTS
     assert np.all(inp["topk_ids"][:, 0] != inp["topk_ids"][:, 1])
     got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tactic)
-    ref = oracle_out(inp, spec, mode=mode, keep=True)
-    parity(got, ref["out"], f"group boundaries I={I} {mode} {tactic}", rounding_allowance(inp, spec, ref, mode))
+    layer_check(got, inp, spec, mode, plan, ws, what=f"group boundaries I={I} {mode} {tactic}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "wide"])
 def test_w4a8_prequantized_equals_library_quantized(name):
     spec = S.spec_of(SMALL[name])
     inp = S.generate(spec)
-    a, *_ = run_layer(inp, spec, mode="w4a8", prequantized=True)
+    a, plan, ws, _ = run_layer(inp, spec, mode="w4a8", prequantized=True)
+    layer_check(a, inp, spec, "w4a8", plan, ws, what=f"{name} prequantized")
     b, *_ = run_layer(inp, spec, mode="w4a8", prequantized=False)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    ref = oracle_out(inp, spec, mode="w4a8", prequantized=True, keep=True)
-    parity(a, ref["out"], f"{name} prequantized", rounding_allowance(inp, spec, ref, "w4a8"))
 
 
 @pytest.mark.parametrize("mode,name,tactic", [("w4a16", "wide", (-1, -1)), ("w4a8", "wide", (-1, -1)),
@@ -301,24 +299,16 @@ def test_intermediate_h_matches_oracle(mode, name, tactic):
     got, plan, ws, _ = run_layer(inp, spec, mode=mode, tactic=tactic)
     ref = oracle_out(inp, spec, mode=mode, keep=True)
     P, I = int(ref["offsets"][-1]), spec["I"]
-    if mode == "w4a16":
-        h = ws_region(plan, ws, "h", torch.int16, (P, I)).view(np.uint16)
-        hg = F.bf16_to_f64(h)
-    else:
-        hc = ws_region(plan, ws, "h", torch.uint8, (P, I))
-        hs = ws_region(plan, ws, "hs", torch.uint8, (P, I // 32))
-        hg = F.mx_dequantize(hc, hs, "e4m3")
-    hr = np.zeros((P, I))
-    hr[ref["pairs"]] = ref["h"]
-    # one element-grid step at most (a rounding decision may differ by one ulp)
-    step = 2.0 ** -7 if mode == "w4a16" else 2.0 ** -3
-    rel = np.abs(hg - hr) / np.maximum(np.abs(hr), 1e-3 * np.sqrt(np.mean(hr ** 2)))
-    assert np.mean(rel <= 1e-6) > 0.97, np.mean(rel <= 1e-6)
-    assert np.max(rel) <= step * 1.01 + 1e-6
+    hg = gpu_h(plan, ws, P, I, mode)
+    n_diff = check_h(hg, inp, spec, ref, mode, f"h {name} {mode} {tactic}")
+    assert n_diff <= 1e-3 * P * I
+    # y of every pair against the oracle's FC2 of the GPU's own h, at the bar
+    # per pair row set (nothing discounted)
     y = read_y(plan, ws, P, spec["H"])
+    cond = oracle_out(inp, spec, mode=mode, keep=True, h_given=hg["vals"])
     yr = np.zeros_like(y, dtype=np.float64)
-    yr[ref["pairs"]] = ref["y"]
-    parity(y, yr, f"y {mode}", y_rounding_allowance(inp, spec, ref, mode, P))
+    yr[cond["pairs"]] = cond["y"]
+    parity(y, yr, f"y {name} {mode} {tactic}")
 
 
 @pytest.mark.parametrize("name,mode,tactic", [("wide", "w4a16", (-1, -1)), ("prefill_c", "w4a8", (4, 20))])
@@ -415,15 +405,16 @@ def test_alpha_null_means_one():
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_layer_parity_full_size(cfg):
+    """Every token of each benchmark workload, in the launch configuration the
+    benchmark times: h valid element by element, the output within the bar
+    against the oracle's FC2 and combine of the GPU's h, and within the bar
+    against the plain oracle."""
     inp = config_inputs(cfg)
     spec = inp["spec"]
     got, plan, ws, _ = run_layer(inp, spec)
     T = spec["T"]
-    rng = np.random.default_rng(100 + cfg)
-    tokens = np.arange(T) if T <= 16 else np.sort(rng.choice(T, 12, replace=False))
-    ref = oracle_out(inp, spec, tokens=tokens, keep=True)
-    parity(got[tokens], ref["out"], f"config {cfg} ({spec['name']}) sampled tokens",
-           rounding_allowance(inp, spec, ref, spec["mode"]))
+    ref = layer_check(got, inp, spec, spec["mode"], plan, ws, raw_required=True,
+                      what=f"config {cfg} ({spec['name']}) all {T} tokens")
     none = np.all(ref["inv"].reshape(T, spec["k"]) < 0, axis=1)
     assert np.all(got[none] == 0)
     assert np.all(np.isfinite(got))

@@ -68,13 +68,13 @@ MOE_MUTATIONS = [
     ("perm ordered by j only", "order = np.lexsort((jl, ll))", "order = np.argsort(jl, kind='stable')"),
     ("off-by-one shard filter", "local = (l >= 0) & (l < local_num_experts)", "local = (l >= 0) & (l <= local_num_experts)"),
     ("token index from wrong divisor", "rows_t = perm[pos] // k", "rows_t = perm[pos] % T"),
-    ("combine weight of wrong slot", "out[has] += wts[tokens[has], s][:, None]", "out[has] += wts[tokens[has], 0][:, None]"),
+    ("combine weight of wrong slot", "wsl = wts[tokens[has], s]", "wsl = wts[tokens[has], 0]"),
     ("no bf16 rounding of h", "hq = F.bf16_to_f64(F.f32_to_bf16_rne(_f32(h)))", "hq = np.asarray(h, np.float64)"),
     ("activation scale applied twice",
      "return F.mx_dequantize(codes, scales, \"e4m3\"), codes, scales",
      "return F.mx_dequantize(codes, scales, \"e4m3\") * F.mx_dequantize(np.full_like(codes, 0x38), scales, \"e4m3\"), codes, scales"),
-    ("W2 transposed operand", "W2d = F.dequant_mxfp4(w2[l], w2s[l]).astype(dt)            # [H, I]",
-     "W2d = F.dequant_mxfp4(w2[l], w2s[l]).astype(dt)[::-1]"),
+    ("W2 transposed operand", "W2d = dequant(w2[l], w2s[l]).astype(dt, copy=False)        # [H, I]",
+     "W2d = dequant(w2[l], w2s[l]).astype(dt, copy=False)[::-1]"),
 ]
 
 
