@@ -1,25 +1,43 @@
 """Benchmark of the MXFP4 + SiTU routed-MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--decode-config D]
+                    [--no-cpu-baseline] [--no-decode]
 
 A step is one call of the whole layer (routing, FC1 + SiTU, FC2, combine)
-over one batch of synthetic tokens already resident in HBM.  The default
-workload is the TP8-shard decode batch the metric is quoted on (config 1:
-64 tokens, hidden 3584, 896 local experts, intermediate 384, top-16,
-w4a16); --config selects another shard shape.  The w4a8 prefill shards take
-their activations MXFP8-quantized per token, as the workload defines them
-(quantized once by the library before timing); the step with bf16 input and
-the library's own quantization is reported beside it.
+over one batch of synthetic tokens already resident in HBM.  The headline
+workload is the largest single-GPU shard, the EP8 prefill batch (config 4:
+32768 tokens, hidden 3584, 112 of 896 experts at offset 336, intermediate
+3072, top-16, packed routing, MXFP8 activations, 30 % of the tokens with no
+local expert and 8 local experts with none), measured against the FP8 matrix
+core peak; the TP8 decode batch (config 1: 64 tokens, 896 local experts,
+intermediate 384, w4a16), measured against HBM bandwidth, is reported beside
+it under "decode".  --config / --decode-config select other shard shapes.
+The w4a8 prefill shards take their activations MXFP8-quantized per token,
+as the workload defines them (quantized once by the library before timing);
+the step with bf16 input and the library's own quantization is reported
+beside it.
 
-value comes from plain (eager) calls.  The step is also captured once into a
-HIP graph and replayed (the layer runs no host synchronization and records
-no memset node); the replay time and whether its output equals the eager
-one bit for bit are reported beside it.
+value comes from K plain (eager) calls between two synchronizations.  A
+second pass times every call on its own (HIP events on the stream) for the
+median, p10 and p90; a third records six events per call at the stage
+boundaries (situ_moe_run_profiled) for each kernel's average duration on the
+stream it runs on.  For the decode workload a fourth pass writes a 512 MiB
+buffer before every call (outside the timed events) so that no weight is
+left in the 256 MiB MALL.  The step is also captured into a HIP graph and
+replayed; its time and whether its output equals the eager one bit for bit
+are reported.
 
 Prints one JSON line: tokens/s, ms per step, the roofline of the dominant
-kernel (algorithmic bytes or flops per launch over its average duration
-from HIP events on the stream it runs on), per-stage times, and the CPU
-oracle timed on a bounded sample of the same workload.
+kernel (algorithmic bytes or flops per launch over its average duration),
+per-stage times, and the CPU oracle timed on a bounded sample of the same
+workload.
+
+    python bench.py --summarize-stats DIR --workload W --command "..."
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --workload W --stage S --command "..."
+    python bench.py --summarize-pmc DIR --workload W --command "..."
+
+turn rocprofv3 CSV output (kernel stats, FETCH_SIZE / WRITE_SIZE passes, or
+any counter pass) into the text summaries kept under profiles/.
 """
 
 import argparse
@@ -39,7 +57,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 GEMM_SOURCES = ("block_scaled_mxfp4_amd/csrc/gemm.hip", "block_scaled_mxfp4_amd/csrc/prefill.hip",
                 "block_scaled_mxfp4_amd/csrc/dma.hpp",
                 "block_scaled_mxfp4_amd/csrc/common.hpp", "block_scaled_mxfp4_amd/csrc/internal.hpp",
-                "block_scaled_mxfp4_amd/build.py")
+                "block_scaled_mxfp4_amd/csrc/epilogue.hpp", "block_scaled_mxfp4_amd/build.py")
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 STAGES = ("route", "quantize", "fc1", "fc2", "combine")
 
@@ -119,8 +137,20 @@ def copy_probe(mib, reps):
     _log(f"copy probe: {reps} x {mib} MiB device-to-device")
 
 
+def _first_tokens(inp, n):
+    """The same batch cut to its first n tokens (the layer is independent per
+    token: each kept token's output row is unchanged)."""
+    sub = dict(inp)
+    for key in ("hidden_states", "topk_ids", "topk_weights", "topk_packed"):
+        if sub.get(key) is not None:
+            sub[key] = np.ascontiguousarray(sub[key][:n])
+    return sub
+
+
 def cpu_baseline(inp, spec, budget_s=15.0):
-    """The oracle (float32 mode, as it stands) on a bounded sample of tokens."""
+    """The oracle (float32 mode, as it stands) on a bounded sample: the first n
+    tokens of the same batch, n chosen for about budget_s seconds of CPU work
+    (w4a8: including the oracle's own MXFP8 quantization of those tokens)."""
     from oracle import moe as M
     try:
         from threadpoolctl import threadpool_info
@@ -130,49 +160,37 @@ def cpu_baseline(inp, spec, budget_s=15.0):
         threads = os.cpu_count()
     cores = len(os.sched_getaffinity(0))
     T = spec["T"]
+
+    def run(n):
+        t0 = time.perf_counter()
+        M.moe_forward(_first_tokens(inp, n), local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
+                      act_mode=spec["mode"], precision="f32")
+        return time.perf_counter() - t0
+
     n = min(T, 4)
-    tokens = np.arange(n)
-    t0 = time.perf_counter()
-    M.moe_forward(inp, local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
-                  act_mode=spec["mode"], precision="f32", tokens=tokens)
-    dt = time.perf_counter() - t0
+    dt = run(n)
     if dt < budget_s / 3 and n < T:
         n = int(min(T, max(n + 1, n * budget_s / max(dt, 1e-3) * 0.6)))
-        tokens = np.arange(n)
-        t0 = time.perf_counter()
-        M.moe_forward(inp, local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
-                      act_mode=spec["mode"], precision="f32", tokens=tokens)
-        dt = time.perf_counter() - t0
+        dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
             "sample": f"first {n} of {T} tokens of the same batch, float32 numpy/OpenBLAS oracle, "
                       f"{dt:.1f} s wall, {threads} BLAS threads on {cores} host cores"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
-    args = ap.parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this layer computes one TP/EP shard's partial output "
-              f"on one MI355X (the cross-GPU all-reduce is the caller's); --gpus {args.gpus} is not run.",
-              file=sys.stderr)
-        return 2
+def _percentiles(ms):
+    a = np.asarray(ms, np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.quantile(a, 0.1)), 5),
+            "p90": round(float(np.quantile(a, 0.9)), 5)}
 
+
+def measure(cfg, steps, warmup, dev, want_cpu, mall_flush):
+    """Time one workload; returns the result fields of its line."""
     import torch
     import block_scaled_mxfp4_amd as B
     import synthetic as S
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    spec = S.spec_of(args.config)
-    _log(f"generating inputs for config {args.config} ({spec['name']})")
+    spec = S.spec_of(cfg)
+    _log(f"generating inputs for config {cfg} ({spec['name']})")
     t0 = time.perf_counter()
     inp = S.generate(spec)
     _log(f"generated in {time.perf_counter() - t0:.1f} s")
@@ -217,12 +235,12 @@ def main(argv=None):
     _log(f"plan: fc1={B.situ_moe_tactic_name(plan.fc1_tactic)} fc2={B.situ_moe_tactic_name(plan.fc2_tactic)} "
          f"block_m={plan.block_m} workspace={plan.workspace_bytes / 2**20:.1f} MiB")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         B.situ_moe_run(plan, ts, ws)
     torch.cuda.synchronize()
 
     # Timed region: K plain calls between two synchronizations -> value.
-    K = args.steps
+    K = steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -234,11 +252,33 @@ def main(argv=None):
     wall = time.perf_counter() - wall0
     eager_ms = start.elapsed_time(end) / K
     eager_out = tens["out"].clone()
+    _log(f"config {cfg}: {eager_ms:.4f} ms per step")
+
+    # Every call timed on its own: median / p10 / p90.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        B.situ_moe_run(plan, ts, ws)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    per_call = [a_.elapsed_time(b_) for a_, b_ in evs]
+
+    flushed = None
+    if mall_flush:   # a 512 MiB write before every call, outside its events
+        junk = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for a_, b_ in fevs:
+            junk.fill_(1.0)
+            a_.record(stream)
+            B.situ_moe_run(plan, ts, ws)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        flushed = _percentiles([a_.elapsed_time(b_) for a_, b_ in fevs])
+        flushed["note"] = "each call preceded by a 512 MiB device write (the MALL holds 256 MiB)"
+        del junk
 
     # The same step captured once into a HIP graph, replayed K times.
-    graph_ms = None
-    graph_same = None
-    graph_error = None
+    graph_ms = graph_same = graph_error = None
     try:
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
@@ -263,7 +303,6 @@ def main(argv=None):
         del graph
     except Exception as e:   # capture unavailable: reported, the eager number stands regardless
         graph_error = f"{type(e).__name__}: {e}"
-    ms_per_step = eager_ms
 
     bf16_input_ms = None
     if w4a8:   # bf16 activations, quantized by the library inside the step
@@ -288,27 +327,26 @@ def main(argv=None):
     # Kernel durations: K more calls, each recording six HIP events on the
     # library's stream at the stage boundaries (the events themselves add a
     # few microseconds per call, so they stay out of the value above).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     for i in range(K):
-        B.situ_moe_run_profiled(plan, ts, ws, evs[i])
+        B.situ_moe_run_profiled(plan, ts, ws, sevs[i])
     torch.cuda.synchronize()
     stage_ms = {}
     for j, name in enumerate(STAGES):
-        stage_ms[name] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+        stage_ms[name] = float(np.mean([sevs[i][j].elapsed_time(sevs[i][j + 1]) for i in range(K)]))
 
     counts = B.workspace_view(plan, ws, "counts", torch.int32, (spec["E_l"],)).cpu().numpy()
     inv = B.workspace_view(plan, ws, "inv", torch.int32, (T * k,)).cpu().numpy().reshape(T, k)
     tokens_used = int(np.count_nonzero((inv >= 0).any(axis=1)))
     work = algorithmic_work(spec, counts, tokens_used, plan.y_format)
 
-    dom = "fc1" if stage_ms["fc1"] >= stage_ms["fc2"] else "fc2"
     workload = f"{spec['name']}_{spec['mode']}"
-    traffic = stored_traffic(workload, dom)
+    peak_tf = MFMA_PEAK_TFLOPS["mxfp8"] if w4a8 else MFMA_PEAK_TFLOPS["bf16"]
+
     def roofline(stage):
         """The stage's kernel against the roofline that bounds it: the larger
         of its algorithmic bytes / HBM peak and its flops / MFMA peak."""
         t = stage_ms[stage] * 1e-3
-        peak_tf = MFMA_PEAK_TFLOPS["mxfp8"] if w4a8 else MFMA_PEAK_TFLOPS["bf16"]
         t_hbm = work[f"{stage}_bytes"] / (HBM_PEAK_GBS * 1e9)
         t_mfma = work[f"{stage}_flops"] / (peak_tf * 1e12)
         if t_hbm >= t_mfma:
@@ -321,43 +359,225 @@ def main(argv=None):
                 "frac": round(achieved / peak_tf, 4), "kernel": stage,
                 "algorithmic_flops_per_launch": work[f"{stage}_flops"], "avg_launch_ms": round(stage_ms[stage], 5)}
 
+    # the dominant kernel: the GEMM further from its roofline in time spent
+    dom = "fc1" if stage_ms["fc1"] >= stage_ms["fc2"] else "fc2"
     roof = roofline(dom)
-    roof["traffic"] = traffic
+    roof["traffic"] = stored_traffic(workload, dom)
     other = roofline("fc2" if dom == "fc1" else "fc1")
-    layer_gbs = work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9
+    other["traffic"] = stored_traffic(workload, other["kernel"])
+    layer_gbs = work["layer_bytes"] / (eager_ms * 1e-3) / 1e9
+    layer_tf = (work["fc1_flops"] + work["fc2_flops"]) / (eager_ms * 1e-3) / 1e12
 
     res = {
-        "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
-        "value": round(T / (ms_per_step * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": round(T / (eager_ms * 1e-3), 1),
+        "ms_per_step": round(eager_ms, 5),
+        "step_ms": _percentiles(per_call),
         "dtype": "mxfp8" if w4a8 else "bf16",
-        "data": "synthetic",
         "config": {"workload": workload, "tokens": T, "hidden": H, "intermediate": I,
                    "experts_global": spec["E_g"], "experts_local": spec["E_l"],
-                   "local_expert_offset": spec["off"], "top_k": k, "topk_format": "packed" if packed else "ids+weights",
+                   "local_expert_offset": spec["off"], "top_k": k,
+                   "topk_format": "packed" if packed else "ids+weights",
                    "active_local_experts": work["A"], "local_pairs": work["P"],
                    "fc1_tactic": B.situ_moe_tactic_name(plan.fc1_tactic),
                    "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic)},
         "roofline": roof,
-        "roofline_other_gemm": {kk: other[kk] for kk in ("kernel", "bound", "achieved", "unit", "frac")},
+        "roofline_other_gemm": {kk: other[kk] for kk in ("kernel", "bound", "achieved", "unit", "frac", "traffic")},
         "stage_ms": {kk: round(v, 5) for kk, v in stage_ms.items()},
         "layer_hbm_gbs": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "layer_tflops": round(layer_tf, 1),
+        "layer_mfma_frac": round(layer_tf / peak_tf, 4),
         "wall_s_timed_region": round(wall, 4),
         "graph_replay": {"ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
                          "bitwise_equal_to_eager": graph_same, "error": graph_error},
         "activations": "MXFP8 per token (prequantized)" if w4a8 else "bf16",
     }
+    if flushed is not None:
+        res["step_ms_mall_flushed"] = flushed
     if bf16_input_ms is not None:
         res["bf16_input"] = {"ms_per_step": round(bf16_input_ms, 5),
                              "tokens_per_s": round(T / (bf16_input_ms * 1e-3), 1),
                              "note": "the same step with bf16 activations quantized by the library (eager)"}
-    if not args.no_cpu_baseline:
+    if want_cpu:
         _log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(inp, spec)
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- rocprofv3 summaries
+
+def _csvs(directory, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize_stats(directory, workload, command):
+    """profiles/<workload>_kernel_stats.txt from rocprofv3 --kernel-trace --stats output."""
+    import csv
+    files = _csvs(directory, "kernel_stats.csv")
+    assert files, f"no *kernel_stats.csv under {directory}"
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# kernel durations, {workload}", f"# command: {command}",
+             "# source: rocprofv3 --kernel-trace --stats, kernel_stats.csv (durations in microseconds)",
+             f"{'kernel':66s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:66]:66s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def _counter_rows(directory):
+    import csv
+    files = _csvs(directory, "counter_collection.csv")
+    assert files, f"no *counter_collection.csv under {directory}"
+    return list(csv.DictReader(open(files[0])))
+
+
+def _per_kernel(rows, counter):
+    """{kernel name: [value per dispatch, in dispatch order]} for one counter."""
+    out = {}
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        if r["Counter_Name"] == counter:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+STAGE_KERNELS = {"fc1": ("decode_gemm_kernel<false, true", "decode_gemm_kernel<true, true", "fc1_kernel",
+                         "prefill_wide_kernel<true>", "prefill_gemm_kernel<true>"),
+                 "fc2": ("decode_gemm_kernel<false, false", "decode_gemm_kernel<true, false", "fc2_kernel",
+                         "prefill_wide_kernel<false>", "prefill_gemm_kernel<false>", "prefill_fc2_short_kernel")}
+
+
+def _stage_kernel(names, stage):
+    for n in names:
+        if any(p in n for p in STAGE_KERNELS[stage]):
+            return n
+    raise SystemExit(f"no {stage} kernel among {sorted(names)}")
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, stage, command):
+    """profiles/<workload>_<stage>_traffic.txt: HBM bytes per launch of the
+    stage's kernel from a FETCH_SIZE pass and a WRITE_SIZE pass, each scaled
+    by the same counter's reading for the last three dispatches of the run (a
+    512 MiB device copy, bench.py --copy-probe-mib 512)."""
+    f = _per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    w = _per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+    kern = _stage_kernel(f.keys(), stage)
+    copy = [n for n in f if "copyBuffer" in n]
+    assert copy, "the runs need the copy probe"
+    cf = float(np.mean(f[copy[0]][-3:]))
+    cw = float(np.mean(w[copy[0]][-3:]))
+    ff, wf = 524288.0 / cf, 524288.0 / cw
+    fk = float(np.median(f[kern][1:] or f[kern]))     # the first dispatch is the cold warm-up
+    wk = float(np.median(w[kern][1:] or w[kern]))
+    hbm = int(round((fk * ff + wk * wf) * 1024))
+    lines = [f"# HBM traffic of the {stage.upper()} kernel, {workload}", f"# kernel: {kern}",
+             "# commands (one counter per run):"] + [f"#   {c}" for c in command.split(" ;; ")] + [
+        "# calibration: the runs end with three 512 MiB device-to-device copies (the last three dispatches);",
+        f"#   FETCH_SIZE reads {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for 524288 KiB moved,",
+        f"#   so fetch is scaled by {ff:.4f} and write by {wf:.4f}.",
+        f"# per launch (median over dispatches after the first): fetch {fk:.1f} KiB x {ff:.4f} + write {wk:.1f} KiB"
+        f" x {wf:.4f} = {hbm / 1e6:.1f} MB",
+        "# sources_digest: sha256 prefix of the GEMM sources the counters were taken on",
+        json.dumps({"workload": workload, "stage": stage, "kernel": kern, "fetch_kib_per_dispatch": round(fk, 1),
+                    "write_kib_per_dispatch": round(wk, 1), "dispatches": [len(f[kern]), len(w[kern])],
+                    "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1), "fetch_factor": round(ff, 4),
+                    "write_factor": round(wf, 4), "hbm_bytes_per_launch": hbm,
+                    "sources_digest": gemm_sources_digest()})]
+    path = os.path.join(ROOT, "profiles", f"{workload}_{stage}_traffic.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def summarize_pmc(directory, workload, command, tag):
+    """profiles/<workload>_<tag>_counters.txt: every counter of one rocprofv3
+    --pmc pass, per GEMM kernel (median over dispatches after the first)."""
+    rows = _counter_rows(directory)
+    names = sorted({r["Counter_Name"] for r in rows})
+    lines = [f"# hardware counters of the GEMM kernels, {workload}", f"# command: {command}",
+             "# values: median per dispatch over the dispatches after the first (the cold warm-up)"]
+    per = {c: _per_kernel(rows, c) for c in names}
+    kernels = set()
+    for c in names:
+        kernels |= set(per[c].keys())
+    for stage in ("fc1", "fc2"):
+        try:
+            kern = _stage_kernel(kernels, stage)
+        except SystemExit:
+            continue
+        lines.append(f"{stage}: {kern}")
+        for c in names:
+            v = per[c].get(kern, [])
+            if v:
+                lines.append(f"  {c:40s} {float(np.median(v[1:] or v)):18.1f}")
+    path = os.path.join(ROOT, "profiles", f"{workload}_{tag}_counters.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="headline workload (default: the EP8 prefill shard)")
+    ap.add_argument("--decode-config", type=int, default=1, help="workload reported beside it (-1: none)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--workload")
+    ap.add_argument("--stage")
+    ap.add_argument("--tag", default="pmc")
+    ap.add_argument("--command", default="")
+    args = ap.parse_args(argv)
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.workload, args.command)
+        return 0
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.workload, args.stage, args.command)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.workload, args.command, args.tag)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer computes one TP/EP shard's partial output "
+              f"on one MI355X (the cross-GPU all-reduce is the caller's); --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False)
+    res = {
+        "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
+        "value": head.pop("value"),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic",
+        "config": head.pop("config"),
+        "roofline": head.pop("roofline"),
+    }
+    cpu = head.pop("cpu_baseline", None)
+    res.update(head)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    if not args.no_decode and args.decode_config >= 0 and args.decode_config != args.config:
+        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True)
+        res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)
     print(json.dumps(res), flush=True)

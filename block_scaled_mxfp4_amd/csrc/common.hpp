@@ -205,9 +205,8 @@ __device__ __forceinline__ float situ_h(float acc_g, float acc_u, const SituK& k
 //          (CUTLASS SwigluBias, the same review's _swiglu_bias_act);
 // for kinds 1 and 2, q = (kg*x_g) * (ku*x_u + kb) / (1 + 2^(ke*x_g)) with one
 // exponential and one reciprocal, blb = 1.  The inputs x_g, x_u are the
-// accumulators (alpha folded into the constants), or -- with a LoRA delta,
-// which is added after alpha -- g and u themselves (constants built with
-// unit alphas).
+// accumulators (alpha folded into the constants; a LoRA delta enters divided
+// by alpha).
 enum : int { kActSitu = 0, kActSwiglu = 1, kActSwigluBias = 2 };
 struct ActK {
   int kind;
@@ -240,11 +239,11 @@ __device__ __forceinline__ float act_q(float xg, float xu, const ActK& k) {
 __device__ __forceinline__ float act_h(float xg, float xu, const ActK& k) { return act_q(xg, xu, k) * k.s.blb; }
 
 // Per-expert activation constants of one FC1 work item and its LoRA mode:
-// `lora` set when a delta is added (then the constants take unit alphas and
-// the inputs are g = fma(ag, acc_g, d_g), u = fma(au, acc_u, d_u)).
+// `lora` set when a delta is added (the inputs are then acc + d / alpha, with
+// rag = 1 / alpha_g and rau = 1 / alpha_u).
 struct ActItem {
   ActK k;
-  float ag, au;
+  float ag, au, rag, rau;
   bool lora;
 };
 

@@ -8,6 +8,11 @@
 // back as the down LoRA's input, and with no bridges the op is the plain
 // pipeline.  The delta is in the layer's real-valued domain, so it is added
 // after the alpha scaling: g = alpha_g * acc_g + d_g, u = alpha_u * acc_u + d_u.
+// The activation constants fold alpha in (act_consts), so the delta enters
+// as acc_g + d_g / alpha_g; a zero delta element leaves the accumulator
+// untouched, so an all-zero delta gives the plain pipeline bit for bit (the
+// release notes' zero-B adapters equal to the base output).  With a delta,
+// alpha_gate and alpha_up must be nonzero.
 #pragma once
 
 #include "common.hpp"
@@ -24,7 +29,9 @@ __device__ __forceinline__ ActItem act_item(const GemmArgs& a, int l) {
   const float p0 = a.beta ? __builtin_bit_cast(float, ((cp)a.beta)[l]) : 0.0f;
   const float p1 = a.lbeta ? __builtin_bit_cast(float, ((cp)a.lbeta)[l]) : 0.0f;
   it.lora = a.lora_delta != nullptr;
-  it.k = it.lora ? act_consts(a.act_kind, 1.0f, 1.0f, p0, p1) : act_consts(a.act_kind, it.ag, it.au, p0, p1);
+  it.k = act_consts(a.act_kind, it.ag, it.au, p0, p1);
+  it.rag = 1.0f / it.ag;
+  it.rau = 1.0f / it.au;
   return it;
 }
 
@@ -37,9 +44,9 @@ __device__ __forceinline__ void load_bf16x4(const uint16_t* p, float v[4]) {
   v[3] = bf16_to_f32(w.y >> 16);
 }
 
-// The activation inputs of four gate/up column pairs: the accumulators as
-// they are, or with a LoRA delta (drow = the pair's delta row at the first
-// gate column; up columns I further) g and u themselves.
+// The activation inputs of four gate/up column pairs: the accumulators, plus
+// with a LoRA delta (drow = the pair's delta row at the first gate column;
+// up columns I further) the delta divided by alpha.
 __device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* drow, int I, const float ag4[4],
                                            const float au4[4], float xg[4], float xu[4]) {
   if (it.lora) {
@@ -48,8 +55,8 @@ __device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* dr
     load_bf16x4(drow + I, du);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      xg[e] = __builtin_fmaf(it.ag, ag4[e], dg[e]);
-      xu[e] = __builtin_fmaf(it.au, au4[e], du[e]);
+      xg[e] = dg[e] != 0.0f ? __builtin_fmaf(dg[e], it.rag, ag4[e]) : ag4[e];
+      xu[e] = du[e] != 0.0f ? __builtin_fmaf(du[e], it.rau, au4[e]) : au4[e];
     }
   } else {
 #pragma unroll

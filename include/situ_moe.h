@@ -160,8 +160,10 @@ typedef struct situ_moe_tensors {
                                          weight in the combine as one fp32 product */
   const uint16_t* gate_up_lora_delta; /* (device) bf16 [T*k, 2I] or NULL: a LoRA adapter's FC1 output for
                                          pair j = t*k + s (gate columns, then up), added in fp32 to the
-                                         alpha-scaled halves before the activation; rows of pairs outside
-                                         the shard are not read */
+                                         alpha-scaled halves before the activation (alpha_gate and alpha_up
+                                         must then be nonzero); an all-zero delta gives the output of a
+                                         call without it bit for bit; rows of pairs outside the shard are
+                                         not read */
   uint16_t* activation_lora_input;    /* (device) bf16 [T*k, I] or NULL: receives h of pair j (the input of
                                          the down LoRA, after the rounding point; exact in bf16 in both
                                          modes), zero rows for pairs outside the shard */

@@ -184,8 +184,12 @@ def h_tolerance(inp, spec, ref, mode, q, cols):
             j = perm[pairs[qs]]
             g = g + delta[j, cs]
             u = u + delta[j, I + cs]
-        dg = a_g[l] * ag_err + 2 * _ulp32(g)
-        du = a_u[l] * au_err + 2 * _ulp32(u)
+        # the GPU adds a LoRA delta as acc + d / alpha: a few more roundings of
+        # the terms' own size
+        extra_g = 2 * (_ulp32(a_g[l] * acc[qs, cs]) + _ulp32(g - a_g[l] * acc[qs, cs]))
+        extra_u = 2 * (_ulp32(a_u[l] * acc[qs, I + cs]) + _ulp32(u - a_u[l] * acc[qs, I + cs]))
+        dg = a_g[l] * ag_err + 2 * _ulp32(g) + extra_g
+        du = a_u[l] * au_err + 2 * _ulp32(u) + extra_u
         h0 = M.gated_activation(act, g, u, p0[l], p1[l])
         d = np.zeros_like(h0)
         for sg, su in ((1, 0), (-1, 0), (0, 1), (0, -1)):
@@ -285,20 +289,25 @@ def layer_check(got, inp, spec, mode, plan, ws, tokens=None, raw_required=False,
     """The layer's parity checks: (1) the GPU's h is valid element by element
     (check_h); (2) the oracle's FC2 and combine run on the GPU's own h give
     the GPU output within the bar, with nothing discounted; (3) the GPU output
-    against the plain oracle output -- asserted at the bar where
-    raw_required, else only reported (on small shapes a single legitimate
-    rounding decision of h moves an output element by a visible fraction of
-    the RMS).  got holds the rows of `tokens` (all tokens if None)."""
+    against the plain oracle output: raw_required True asserts the whole
+    bar, "cosine" asserts the cosine and reports max-abs, False reports both
+    (a legitimately different rounding decision of one element of h moves
+    the output elements of its token by up to several percent of the RMS:
+    on small shapes, and in w4a8 at full size, where the matrix cores' FP8
+    accumulation makes such decisions differ for ~1 in 2000 elements).  got
+    holds the rows of `tokens` (all tokens if None)."""
     ref = oracle_out(inp, spec, mode=mode, tokens=tokens, keep=True)
     P, I = int(ref["offsets"][-1]), spec["I"]
     hg = gpu_h(plan, ws, P, I, mode)
     check_h(hg, inp, spec, ref, mode, what)
     cond = oracle_out(inp, spec, mode=mode, tokens=tokens, h_given=hg["vals"])
     parity(got, cond["out"], f"{what} vs oracle FC2 + combine of the GPU's h")
-    if raw_required:
+    if raw_required is True:
         parity(got, ref["out"], f"{what} vs oracle (raw)")
     else:
-        report(got, ref["out"], f"{what} vs oracle (raw, reported)")
+        cos, _ = report(got, ref["out"], f"{what} vs oracle (raw, max-abs reported)")
+        if raw_required == "cosine":
+            assert cos >= COS_MIN, f"{what}: raw cosine {cos}"
     return ref
 
 
