@@ -9,7 +9,8 @@ sidecar does: "Runtime API", importing loads nothing).  If it has not been
 built, every entry point raises; there is no CPU fallback.
 
 Names mirror the C entry points: situ_moe_plan, situ_moe_valid_tactics,
-situ_moe_run, situ_moe_run_profiled, situ_moe_route, situ_moe_quantize_mxfp8, situ_moe_status_string,
+situ_moe_run, situ_moe_run_profiled, situ_moe_run_static, situ_moe_route, situ_moe_quantize_mxfp8,
+situ_moe_status_string,
 situ_moe_last_error, situ_moe_build_info, situ_moe_tactic_name,
 situ_moe_abi_version.  situ_moe(...) is the keyword-only one-call form.
 """
@@ -19,7 +20,8 @@ import os
 
 __all__ = [
     "SituMoeError", "SituMoeProblem", "SituMoePlan", "SituMoeTensors", "library_path", "load",
-    "situ_moe_plan", "situ_moe_valid_tactics", "situ_moe_run", "situ_moe_run_profiled", "situ_moe_route",
+    "situ_moe_plan", "situ_moe_valid_tactics", "situ_moe_run", "situ_moe_run_profiled", "situ_moe_run_static",
+    "situ_moe_route",
     "situ_moe_quantize_mxfp8", "situ_moe_status_string", "situ_moe_last_error",
     "situ_moe_build_info", "situ_moe_tactic_name", "situ_moe_abi_version", "situ_moe",
     "make_problem", "make_tensors", "new_workspace", "workspace_view", "ACT_W4A16", "ACT_W4A8", "OUT_F32", "OUT_BF16",
@@ -100,6 +102,7 @@ def load():
         "situ_moe_run": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp, c_u64, vp]),
         "situ_moe_route": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp, c_u64, vp]),
         "situ_moe_run_profiled": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp, c_u64, vp, P(vp), c_int]),
+        "situ_moe_run_static": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp]),
         "situ_moe_quantize_mxfp8": (c_int, [vp, c_i64, c_int, vp, vp, vp]),
         "situ_moe_status_string": (ctypes.c_char_p, [c_int]),
         "situ_moe_last_error": (ctypes.c_char_p, []),
@@ -171,6 +174,16 @@ def situ_moe_valid_tactics(problem):
 def situ_moe_run(plan, tensors, workspace, stream=None):
     ws, nbytes = _ws(workspace)
     _check(load().situ_moe_run(ctypes.byref(plan), ctypes.byref(tensors), ws, nbytes, _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 128 * 1024 * 1024   # SITU_MOE_STATIC_SCRATCH_BYTES
+
+
+def situ_moe_run_static(plan, tensors, stream=None):
+    """situ_moe_run on the library's own per-device scratch array: no
+    workspace, no allocation (plans needing more than STATIC_SCRATCH_BYTES
+    raise SITU_E_WORKSPACE; overlapping calls on one device race)."""
+    _check(load().situ_moe_run_static(ctypes.byref(plan), ctypes.byref(tensors), _stream(stream)))
 
 
 def situ_moe_run_profiled(plan, tensors, workspace, events, stream=None):

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/situ_moe.h"
+
 namespace situ {
 
 constexpr int kMaxLocalExperts = 1024;
@@ -88,6 +90,10 @@ struct CombineArgs {
 // Zero the rows [T*k, I] of pairs outside the shard (inv < 0) in the bf16
 // down-LoRA input (the FC1 epilogues write the local rows).
 hipError_t launch_zero_nonlocal_rows(const int32_t* inv, uint16_t* rows, int64_t TK, int32_t I, hipStream_t s);
+
+// Record a formatted message for situ_moe_last_error() and return `status`
+// (the planner's error reporting, shared with the other entry points).
+situ_status fail_status(situ_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // Workgroups of `kernel` resident per CU at this block size and dynamic LDS
 // size (hipOccupancyMaxActiveBlocksPerMultiprocessor, cached; thread-safe).

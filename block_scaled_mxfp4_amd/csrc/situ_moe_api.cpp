@@ -40,6 +40,22 @@ situ_status fail(situ_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+namespace situ {
+situ_status fail_status(situ_status status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+}  // namespace situ
+
+namespace {
+
 constexpr uint64_t kAlign = 256;
 constexpr int64_t kRouteSingleMax = 32768;   // pairs routed by a single workgroup
 constexpr double kWideRowsPerExpert = 192.0; // mean group size above which 128-row m-tiles come first

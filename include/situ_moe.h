@@ -197,6 +197,20 @@ situ_status situ_moe_run_profiled(const situ_moe_plan_t* plan, const situ_moe_te
                                   void* workspace, uint64_t workspace_bytes, void* hip_stream,
                                   void* const* hip_events, int32_t n_events);
 
+/* situ_moe_run without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the routing tables and intermediates go
+ * to the library's own scratch array of SITU_MOE_STATIC_SCRATCH_BYTES, one
+ * per device, held from the first call on that device until the process
+ * ends.  Allocates nothing.  A plan whose workspace_bytes exceed the array
+ * returns SITU_E_WORKSPACE (decode-sized shards fit; prefill shards need
+ * situ_moe_run).  Calls that overlap in time on one device race on the
+ * array; the array keeps the last call's contents and nothing in it is
+ * assumed to start at zero.  Otherwise exactly situ_moe_run (same kernels,
+ * same results bit for bit). */
+#define SITU_MOE_STATIC_SCRATCH_BYTES (128u * 1024u * 1024u)
+situ_status situ_moe_run_static(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors, void* hip_stream);
+
 /* The routing stage alone: fills counts, offsets, mtiles, perm and inv in
  * the workspace (offsets in the plan).  Reads only the top-k tensors. */
 situ_status situ_moe_route(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors,
