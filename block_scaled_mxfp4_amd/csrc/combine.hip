@@ -19,9 +19,10 @@ namespace situ {
 // The routing weight of slot s (bf16 bits wb) as fp32, times the FC2 output
 // scale alpha_down of the slot's expert where one is given (one fp32
 // product; the expert comes from the slot's global id).
+template <bool AD>
 __device__ __forceinline__ float slot_weight(const CombineArgs& a, int64_t t, int s, int pos, uint32_t wb, cptr pk) {
   float w = bf16_to_f32(wb);
-  if (a.alpha_down && pos >= 0) {
+  if (AD && pos >= 0) {
     const int id = a.packed ? (int)((uint32_t)pk[s] & 0xffffu) : a.ids[t * a.k + s];
     w = w * a.alpha_down[id - a.off];
   }
@@ -32,7 +33,8 @@ constexpr int kCombineThreads = 128;
 constexpr int kCombineCols = kCombineThreads * 4;   // columns per workgroup
 constexpr int kSlotBatch = 8;                       // slot loads kept in flight together
 
-template <bool Y16>
+// AD: a per-expert FC2 output scale (alpha_down) is given.
+template <bool Y16, bool AD>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
   const int nblk = (a.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = a.T * nblk;
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         const int s = s0 + u;
         pos[u] = s < a.k ? inv[s] : -1;
         const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
-        wgt[u] = slot_weight(a, t, s, pos[u], wb, pk);
+        wgt[u] = slot_weight<AD>(a, t, s, pos[u], wb, pk);
       }
       if constexpr (Y16) {
         const int64_t nb64 = (a.H + 63) / 64;
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 // per lane; the token's slot positions and weights come through scalar loads.
 constexpr int kY16Cols = 512;
 
+template <bool AD>
 __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
   const int nblk = (a.H + kY16Cols - 1) / kY16Cols;
   const int64_t items = a.T * nblk;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kWave) void combine_y16_kernel(CombineArgs a) {
         const int s = s0 + u;
         pos[u] = s < a.k ? inv[s] : -1;
         const uint32_t wb = s < a.k ? (a.packed ? ((uint32_t)pk[s] >> 16) : a.weights[t * a.k + s]) : 0u;
-        wgt[u] = slot_weight(a, t, s, pos[u], wb, pk);
+        wgt[u] = slot_weight<AD>(a, t, s, pos[u], wb, pk);
       }
       uint4 hv[kSlotBatch];
       uint32_t ev[kSlotBatch];
@@ -179,15 +182,20 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t nblk = (a.H + kCombineCols - 1) / kCombineCols;
   const int64_t items = a.T * nblk;
   const int64_t grid = items < (1 << 20) ? items : (1 << 20);
+  const bool ad = a.alpha_down != nullptr;
   if (a.y16 && a.H % 8 == 0) {
     const int64_t nb16 = (a.H + kY16Cols - 1) / kY16Cols;
     const int64_t it16 = a.T * nb16;
     const int64_t g16 = it16 < (1 << 20) ? it16 : (1 << 20);
-    hipLaunchKernelGGL(combine_y16_kernel, dim3((unsigned)g16), dim3(kWave), 0, s, a);
-  } else if (a.y16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+    if (ad) hipLaunchKernelGGL(combine_y16_kernel<true>, dim3((unsigned)g16), dim3(kWave), 0, s, a);
+    else hipLaunchKernelGGL(combine_y16_kernel<false>, dim3((unsigned)g16), dim3(kWave), 0, s, a);
+  } else if (a.y16) {
+    if (ad) hipLaunchKernelGGL((combine_kernel<true, true>), dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<true, false>), dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+  } else {
+    if (ad) hipLaunchKernelGGL((combine_kernel<false, true>), dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<false, false>), dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -35,6 +35,14 @@ __device__ __forceinline__ ActItem act_item(const GemmArgs& a, int l) {
   return it;
 }
 
+// SiTU constants of expert l for the plain epilogue (no LoRA bridges).
+__device__ __forceinline__ SituK situ_item(const GemmArgs& a, int l) {
+  typedef const int32_t __attribute__((address_space(4)))* cp;
+  const float ag = a.alpha_g ? __builtin_bit_cast(float, ((cp)a.alpha_g)[l]) : 1.0f;
+  const float au = a.alpha_u ? __builtin_bit_cast(float, ((cp)a.alpha_u)[l]) : 1.0f;
+  return situ_consts(ag, au, __builtin_bit_cast(float, ((cp)a.beta)[l]), __builtin_bit_cast(float, ((cp)a.lbeta)[l]));
+}
+
 // Four consecutive bf16 of a row as floats.
 __device__ __forceinline__ void load_bf16x4(const uint16_t* p, float v[4]) {
   const uint2 w = *reinterpret_cast<const uint2*>(p);

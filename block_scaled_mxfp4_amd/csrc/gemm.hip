@@ -43,7 +43,7 @@ namespace situ {
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <bool FP8, int TOKT, bool NV = false>
+template <bool FP8, int TOKT, bool NV = false, bool GEN = false>
 __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
   static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -153,25 +153,34 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
 
     // epilogue: alpha (and a LoRA delta), the activation, rounding point R1,
     // store h in perm order (and by expanded index for the down LoRA)
-    const ActItem ai = act_item(a, l);
+    ActItem ai{};
+    SituK sk{};
+    if constexpr (GEN) ai = act_item(a, l);
+    else sk = situ_item(a, l);
 #pragma unroll
     for (int tt = 0; tt < TOKT; ++tt) {
       const int64_t p = p0 + 16 * tt + r;
-      const int64_t j = (valid[tt] && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
+      const int64_t j = (GEN && valid[tt] && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
       float hv[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float xg[4], xu[4];
-        const float ag4[4] = {acc[half][tt][0], acc[half][tt][1], acc[half][tt][2], acc[half][tt][3]};
-        const float au4[4] = {acc[2 + half][tt][0], acc[2 + half][tt][1], acc[2 + half][tt][2], acc[2 + half][tt][3]};
-        act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
+        if constexpr (GEN) {
+          float xg[4], xu[4];
+          const float ag4[4] = {acc[half][tt][0], acc[half][tt][1], acc[half][tt][2], acc[half][tt][3]};
+          const float au4[4] = {acc[2 + half][tt][0], acc[2 + half][tt][1], acc[2 + half][tt][2],
+                                acc[2 + half][tt][3]};
+          act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+          for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[half][i] = situ_h(acc[half][tt][i], acc[2 + half][tt][i], sk);
+        }
       }
       if constexpr (!FP8) {
         if (valid[tt]) {
           uint16_t* hrow = static_cast<uint16_t*>(a.out) + p * I + n0 + 4 * g;
-          uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
+          uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
           const uint32_t code = e8m0_code_for_e4m3(amax);
           const int sh = 127 - (int)code;
           uint8_t* hrow = static_cast<uint8_t*>(a.out) + p * I + n0 + 4 * g;
-          uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
+          uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             uint32_t packed = 0;
@@ -401,7 +410,7 @@ struct DecodeGeo {
   uint32_t xs_row;
   const uint8_t* x_lds;    // w4a16: the m-tile's activation rows staged in LDS, or null
   uint32_t x_lds_off;      // this lane's row in them (bytes)
-  int nkb, sbr, g, r, ntiles;   // sbr: scale bytes per weight row (nkb, or 2 nkb for NVFP4)
+  int nkb, sbr, g, r, ntiles;   // sbr: NVFP4 scale bytes per weight row (2 nkb)
 };
 
 // One K step's operands for a wave: four 16-row weight tiles (16 bytes of
@@ -485,7 +494,7 @@ __device__ __forceinline__ void compute_w4a16(const uint4 w[4], const uint4 x[4]
       fp4x8_to_bf16x8_mul(w[q].z, s1, wb + 8);
       fp4x8_to_bf16x8_mul(w[q].w, s1, wb + 12);
     } else {
-      const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.sbr + kb] : 127u);
+      const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u);
       fp4x8_to_bf16x8(w[q].x, sc, wb + 0);
       fp4x8_to_bf16x8(w[q].y, sc, wb + 4);
       fp4x8_to_bf16x8(w[q].z, sc, wb + 8);
@@ -510,7 +519,7 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t av[4] = {b.w[q].x, b.w[q].y, b.w[q].z, b.w[q].w};
-      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.sbr + kb] : 127u;
+      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
       acc[q] = mfma_scale_fp4_fp8(av, xb, sv, b.xs, acc[q]);
     }
   }
@@ -549,28 +558,37 @@ __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int sbr, uin
 // fp32 y.  acc[q] holds weight tile q x the group's 16 tokens; this lane owns
 // token p (valid: inside the group) and rows 4g..4g+3 of each tile.
 // Per-expert parameters come through scalar loads.
-template <bool FP8, bool FC1>
+template <bool FP8, bool FC1, bool GEN>
 __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 acc[4], int l, int p, bool valid,
                                                 int n0, int g, int ntiles) {
   if constexpr (FC1) {
     const int I = a.N;
-    const ActItem ai = act_item(a, l);
-    // the pair's expanded index: the row of its LoRA delta and down-LoRA input
-    const int64_t j = (valid && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
     float hv[2][4];
+    int64_t j = 0;
+    if constexpr (GEN) {
+      const ActItem ai = act_item(a, l);
+      // the pair's expanded index: the row of its LoRA delta and down-LoRA input
+      j = (valid && (ai.lora || a.lora_out)) ? (int64_t)a.perm[p] : 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float xg[4], xu[4];
-      const float ag4[4] = {acc[half][0], acc[half][1], acc[half][2], acc[half][3]};
-      const float au4[4] = {acc[2 + half][0], acc[2 + half][1], acc[2 + half][2], acc[2 + half][3]};
-      act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
+      for (int half = 0; half < 2; ++half) {
+        float xg[4], xu[4];
+        const float ag4[4] = {acc[half][0], acc[half][1], acc[half][2], acc[half][3]};
+        const float au4[4] = {acc[2 + half][0], acc[2 + half][1], acc[2 + half][2], acc[2 + half][3]};
+        act_inputs(ai, a.lora_delta + j * (2 * I) + n0 + 16 * half + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+        for (int i = 0; i < 4; ++i) hv[half][i] = act_h(xg[i], xu[i], ai.k);
+      }
+    } else {   // SiTU without LoRA bridges
+      const SituK sk = situ_item(a, l);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[half][i] = situ_h(acc[half][i], acc[2 + half][i], sk);
     }
     if constexpr (!FP8) {
       if (valid) {
         uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
-        uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
+        uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const uint32_t lo = f32_to_bf16_rne(hv[half][0]) | (f32_to_bf16_rne(hv[half][1]) << 16);
@@ -591,7 +609,7 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
         const uint32_t code = e8m0_code_for_e4m3(amax);
         const int sh = 127 - (int)code;
         uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
-        uint16_t* lrow = a.lora_out ? a.lora_out + j * I + n0 + 4 * g : nullptr;
+        uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           uint32_t packed = 0;
@@ -613,7 +631,7 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
   }
 }
 
-template <bool FP8, bool FC1, int KSPLIT, bool NV = false>
+template <bool FP8, bool FC1, int KSPLIT, bool NV = false, bool GEN = false>
 __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
   static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
@@ -698,7 +716,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
       const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
       d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
       d.nkb = nkb;
-      d.sbr = sbr;
+      if constexpr (NV) d.sbr = sbr;
       d.g = g;
       d.r = r;
       uint32_t dr[4];
@@ -815,7 +833,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
       }
     }
 
-    if (lead) decode_epilogue<FP8, FC1>(a, acc, l, p, valid, n0, g, ntiles);
+    if (lead) decode_epilogue<FP8, FC1, GEN>(a, acc, l, p, valid, n0, g, ntiles);
     __syncthreads();   // staged scales and partial sums are reused by the next work item
   }
 }
@@ -856,21 +874,24 @@ static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hi
   return hipGetLastError();
 }
 
-template <bool FP8, bool FC1, bool NV>
+template <bool FP8, bool FC1, bool NV, bool GEN>
 hipError_t launch_decode_k(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
   const int sbr = NV ? a.K / 16 : a.K / 32;   // scale bytes per weight row
   switch (decode_ksplit(a.K)) {
-    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
-    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));
-    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1, NV>>(a, work, cus, s, decode_lds_bytes(1, sbr, decode_lds_x(FP8, FC1, 1, a.K, sbr)));
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV, GEN>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV, GEN>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1, NV, GEN>>(a, work, cus, s, decode_lds_bytes(1, sbr, decode_lds_x(FP8, FC1, 1, a.K, sbr)));
   }
 }
 template <bool FP8, bool FC1>
 hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
+  const bool gen = FC1 && general_epilogue(a);
   if constexpr (!FP8) {
-    if (a.nvfp4) return launch_decode_k<false, FC1, true>(a, work, cus, s);
+    if (a.nvfp4) return gen ? launch_decode_k<false, FC1, true, FC1>(a, work, cus, s)
+                            : launch_decode_k<false, FC1, true, false>(a, work, cus, s);
   }
-  return launch_decode_k<FP8, FC1, false>(a, work, cus, s);
+  return gen ? launch_decode_k<FP8, FC1, false, FC1>(a, work, cus, s)
+             : launch_decode_k<FP8, FC1, false, false>(a, work, cus, s);
 }
 
 // Work items of one launch, upper bound: m-tiles x column units per workgroup.
@@ -888,12 +909,16 @@ hipError_t launch_fc1(int tactic, const GemmArgs& a, int max_mtiles, int cus, hi
   switch (tactic) {
     case FC1_W4A16_M16: return launch_decode<false, true>(a, work, cus, s);
     case FC1_W4A16_M64:
+      if (general_epilogue(a))
+        return a.nvfp4 ? launch_persistent<fc1_kernel<false, 4, true, true>>(a, work, cus, s)
+                       : launch_persistent<fc1_kernel<false, 4, false, true>>(a, work, cus, s);
       return a.nvfp4 ? launch_persistent<fc1_kernel<false, 4, true>>(a, work, cus, s)
                      : launch_persistent<fc1_kernel<false, 4>>(a, work, cus, s);
     case FC1_W4A8_M16: return launch_decode<true, true>(a, work, cus, s);
     case FC1_W4A8_M64:
       if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill<true>(a, max_mtiles, cus, s);
-      return launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
+      return general_epilogue(a) ? launch_persistent<fc1_kernel<true, 4, false, true>>(a, work, cus, s)
+                                 : launch_persistent<fc1_kernel<true, 4>>(a, work, cus, s);
     case FC1_W4A8_M128:   // offered only where K and N are multiples of 128
       if (a.K % 128 == 0 && a.N % 128 == 0) return launch_prefill_wide<true>(a, max_mtiles, cus, s);
       return hipErrorInvalidValue;

@@ -91,6 +91,13 @@ struct CombineArgs {
 // down-LoRA input (the FC1 epilogues write the local rows).
 hipError_t launch_zero_nonlocal_rows(const int32_t* inv, uint16_t* rows, int64_t TK, int32_t I, hipStream_t s);
 
+// FC1 epilogues come in two compiled forms: SiTU without LoRA bridges (the
+// default path, with the fewest registers), and the general one (every
+// activation kind, the LoRA delta and the down-LoRA rows).
+inline bool general_epilogue(const GemmArgs& a) {
+  return a.act_kind != 0 || a.lora_delta != nullptr || a.lora_out != nullptr;
+}
+
 // Record a formatted message for situ_moe_last_error() and return `status`
 // (the planner's error reporting, shared with the other entry points).
 situ_status fail_status(situ_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

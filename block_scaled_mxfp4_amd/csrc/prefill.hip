@@ -247,16 +247,23 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
-template <bool FC1, int TOK = kPfTok>
-__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 acc[8][2], int wn, int wm,
-                                            int wave, int lane, uint8_t* scratch, int ntt = 2) {
+// NCOL: gate columns of an FC1 work item;
+// the token tiles used are acc[.][tt0 .. tt0 + 1] of an [8][TT] accumulator set.
+// GEN: the general FC1 epilogue (every activation kind, LoRA bridges); else
+// SiTU only, with the fewest registers.
+template <bool FC1, int TOK = kPfTok, int NCOL = 128, int TT = 2, bool GEN = false>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 (&acc)[8][TT], int wn, int wm,
+                                            int wave, int lane, uint8_t* scratch, int ntt = 2, int tt0 = 0) {
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
+  const int n0 = FC1 ? x.nt * NCOL : x.nt * kPfRows;
   if constexpr (FC1) {
     const int I = a.N;
-    const ActItem ai = act_item(a, x.l);
-    const float blb = act_blb(ai.k);
-    const bool bridges = ai.lora || a.lora_out;   // uniform
+    ActItem ai{};
+    SituK sk{};
+    if constexpr (GEN) ai = act_item(a, x.l);
+    else sk = situ_item(a, x.l);
+    const float blb = GEN ? act_blb(ai.k) : sk.blb;
+    const bool bridges = GEN && (ai.lora || a.lora_out);   // uniform
     const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(TOK * I));
     const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
 #pragma unroll
@@ -280,15 +287,21 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int i = 2 * blk + h2;
-          float xg[4], xu[4];
-          const float ag4[4] = {acc[i][tt][0], acc[i][tt][1], acc[i][tt][2], acc[i][tt][3]};
-          const float au4[4] = {acc[4 + i][tt][0], acc[4 + i][tt][1], acc[4 + i][tt][2], acc[4 + i][tt][3]};
-          act_inputs(ai, a.lora_delta + j * (2 * I) + col0 + 16 * h2 + 4 * g, I, ag4, au4, xg, xu);
+          const f32x4& gv = acc[i][tt0 + tt];
+          const f32x4& uv = acc[4 + i][tt0 + tt];
+          if constexpr (GEN) {
+            float xg[4], xu[4];
+            const float ag4[4] = {gv[0], gv[1], gv[2], gv[3]};
+            const float au4[4] = {uv[0], uv[1], uv[2], uv[3]};
+            act_inputs(ai, a.lora_delta + j * (2 * I) + col0 + 16 * h2 + 4 * g, I, ag4, au4, xg, xu);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qv[h2][e] = act_q(xg[e], xu[e], ai.k);
-            amax = fmaxf(amax, fabsf(qv[h2][e]));
+            for (int e = 0; e < 4; ++e) qv[h2][e] = act_q(xg[e], xu[e], ai.k);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qv[h2][e] = situ_q(gv[e], uv[e], sk);
           }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(qv[h2][e]));
         }
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
@@ -325,7 +338,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
         st4(hr, ho, packed[0]);
         st4(hr, valid ? ho + 16u : kOobPf, packed[1]);
         st1(sr, (valid && g == 0) ? (uint32_t)(pr * (I / 32) + col0 / 32) : kOobPf, code);
-        if (a.lora_out && valid) {   // the down LoRA's input: h as bf16 by expanded index
+        if (GEN && a.lora_out && valid) {   // the down LoRA's input: h as bf16 by expanded index
           uint16_t* lrow = a.lora_out + j * I + col0 + 4 * g;
           *reinterpret_cast<uint2*>(lrow) = e4m3x4_to_bf16x4(packed[0], (int)code);
           *reinterpret_cast<uint2*>(lrow + 16) = e4m3x4_to_bf16x4(packed[1], (int)code);
@@ -347,7 +360,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<f32x4*>(scratch + r * kRowPitch + (16 * i + 4 * g) * 4) = acc[4 * half + i][tt];
+          *reinterpret_cast<f32x4*>(scratch + r * kRowPitch + (16 * i + 4 * g) * 4) = acc[4 * half + i][tt0 + tt];
         const int tok = lane >> 4, chunk = lane & 15;
         const int col = n0 + 16 * 8 * wn + 64 * half + 4 * chunk;
         // all four reads first: the stores below are ordered memory operations
@@ -369,7 +382,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
 
 }  // namespace
 
-template <bool FC1>
+template <bool FC1, bool GEN = false>
 __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) uint8_t st0[kStage];
   __shared__ __align__(16) uint8_t st1[kStage];
@@ -441,7 +454,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
         if (u < steps) pf_issue(lds_addr_of(stg[u]), d, u, wave, lane);
     }
     // the last stage is free for FC2's transpose
-    pf_epilogue<FC1>(a, cur, acc, wn, wm, wave, lane, stg[kPfStages - 1] + wave * 4352);
+    pf_epilogue<FC1, kPfTok, 128, 2, GEN>(a, cur, acc, wn, wm, wave, lane, stg[kPfStages - 1] + wave * 4352);
     cur = nxt;
   }
 }
@@ -717,7 +730,7 @@ __device__ __forceinline__ PfItem pw_item(const GemmArgs& a, int it, int n_tiles
 
 }  // namespace
 
-template <bool FC1>
+template <bool FC1, bool GEN = false>
 __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) {
   __shared__ __align__(16) uint8_t st0[kWStage];
   __shared__ __align__(16) uint8_t st1[kWStage];
@@ -806,7 +819,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
     }
     // the second stage is free for FC2's output transpose
     if constexpr (FC1) {
-      pf_epilogue<true, kWTok>(a, cur, acc, wn, wm, wave, lane, nullptr, ntt);
+      pf_epilogue<true, kWTok, 128, 2, GEN>(a, cur, acc, wn, wm, wave, lane, nullptr, ntt);
     } else {
       pw_y16_prepare(acc, lane, st1 + wave * kWYScratch, yp);
       px = cur;
@@ -1024,7 +1037,10 @@ hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipSt
   int64_t grid = cus;                                        // one workgroup per CU
   if (grid > work) grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_wide_kernel<FC1>, dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
+  if (FC1 && general_epilogue(a))
+    hipLaunchKernelGGL((prefill_wide_kernel<FC1, FC1>), dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_wide_kernel<FC1, false>), dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1033,13 +1049,19 @@ template hipError_t launch_prefill_wide<false>(const GemmArgs&, int, int, hipStr
 
 template <bool FC1>
 hipError_t launch_prefill(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
-  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(prefill_gemm_kernel<FC1>), kGemmThreads, 0);
+  const bool gen = FC1 && general_epilogue(a);
+  const void* kern = gen ? reinterpret_cast<const void*>(prefill_gemm_kernel<FC1, FC1>)
+                         : reinterpret_cast<const void*>(prefill_gemm_kernel<FC1, false>);
+  const int per_cu = resident_per_cu(kern, kGemmThreads, 0);
   const int n_tiles = FC1 ? a.N / 128 : (a.N + kPfRows - 1) / kPfRows;
   const int64_t work = (int64_t)max_mtiles * n_tiles;
   int64_t grid = (int64_t)cus * per_cu;
   if (grid > work) grid = (work + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_gemm_kernel<FC1>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a);
+  if (gen)
+    hipLaunchKernelGGL((prefill_gemm_kernel<FC1, FC1>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<FC1, false>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
 }
 
