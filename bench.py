@@ -447,9 +447,9 @@ def _per_kernel(rows, counter):
 
 
 STAGE_KERNELS = {"fc1": ("decode_gemm_kernel<false, true", "decode_gemm_kernel<true, true", "fc1_kernel",
-                         "prefill_wide_kernel<true>", "prefill_gemm_kernel<true>"),
+                         "prefill_wide_kernel<true", "prefill_gemm_kernel<true"),
                  "fc2": ("decode_gemm_kernel<false, false", "decode_gemm_kernel<true, false", "fc2_kernel",
-                         "prefill_wide_kernel<false>", "prefill_gemm_kernel<false>", "prefill_fc2_short_kernel")}
+                         "prefill_wide_kernel<false", "prefill_gemm_kernel<false", "prefill_fc2_short_kernel")}
 
 
 def _stage_kernel(names, stage):
@@ -493,27 +493,65 @@ def summarize_traffic(fetch_dir, write_dir, workload, stage, command):
     print(path)
 
 
-def summarize_pmc(directory, workload, command, tag):
-    """profiles/<workload>_<tag>_counters.txt: every counter of one rocprofv3
-    --pmc pass, per GEMM kernel (median over dispatches after the first)."""
-    rows = _counter_rows(directory)
-    names = sorted({r["Counter_Name"] for r in rows})
-    lines = [f"# hardware counters of the GEMM kernels, {workload}", f"# command: {command}",
-             "# values: median per dispatch over the dispatches after the first (the cold warm-up)"]
-    per = {c: _per_kernel(rows, c) for c in names}
-    kernels = set()
-    for c in names:
-        kernels |= set(per[c].keys())
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs a CU; GRBM_GUI_ACTIVE reads once per XCD.
+_XCDS, _CUS, _SIMDS = 8, 256, 1024
+
+
+def _derived(v):
+    """Ratios a reader needs from one kernel's counters (those present)."""
+    out = []
+    gui = v.get("GRBM_GUI_ACTIVE")
+    cyc = gui / _XCDS if gui else None              # the kernel's duration in GPU clocks
+    if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+        out.append(("MFMA busy, % of SIMD cycles", 100.0 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * _SIMDS)))
+    if "SQ_LDS_BANK_CONFLICT" in v and v.get("SQ_LDS_IDX_ACTIVE"):
+        out.append(("LDS bank-conflict cycles, % of LDS active", 100.0 * v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]))
+    if cyc and "TA_TA_BUSY" in v:
+        out.append(("TA busy, % of CU cycles", 100.0 * v["TA_TA_BUSY"] / (cyc * _CUS)))
+    if cyc and "TA_ADDR_STALLED_BY_TC_CYCLES" in v:
+        out.append(("TA address path stalled by the L1, % of CU cycles", 100.0 * v["TA_ADDR_STALLED_BY_TC_CYCLES"] / (cyc * _CUS)))
+    if cyc and "TCP_PENDING_STALL_CYCLES" in v:
+        out.append(("L1 stalled on data pending from L2, % of CU cycles", 100.0 * v["TCP_PENDING_STALL_CYCLES"] / (cyc * _CUS)))
+    if cyc and "SQ_VMEM_TA_CMD_FIFO_FULL" in v:
+        out.append(("vector-memory command FIFO full, % of CU cycles", 100.0 * v["SQ_VMEM_TA_CMD_FIFO_FULL"] / (cyc * _CUS)))
+    if v.get("TCC_REQ") and "TCC_HIT" in v:
+        out.append(("L2 hit rate, %", 100.0 * v["TCC_HIT"] / v["TCC_REQ"]))
+    if v.get("TCP_TCC_READ_REQ") and "TCP_TCC_READ_REQ_LATENCY" in v:
+        out.append(("L1->L2 read latency, cycles (mean)", v["TCP_TCC_READ_REQ_LATENCY"] / v["TCP_TCC_READ_REQ"]))
+        if cyc:
+            out.append(("L1->L2 reads in flight per CU (mean)", v["TCP_TCC_READ_REQ_LATENCY"] / (cyc * _CUS)))
+    if "SQ_INSTS_MFMA" in v:
+        out.append(("16x16x128 MFMAs, TFLOP issued (x 65536 flop)", v["SQ_INSTS_MFMA"] * 65536 / 1e12))
+    return out
+
+
+def summarize_pmc(directories, workload, command, tag):
+    """profiles/<workload>_<tag>_counters.txt: the counters of one or more
+    rocprofv3 --pmc passes (comma-separated directories), per GEMM kernel
+    (median per dispatch over the dispatches after the first), with the
+    ratios they give."""
+    per = {}
+    for directory in directories.split(","):
+        rows = _counter_rows(directory)
+        for c in sorted({r["Counter_Name"] for r in rows}):
+            for kern, vals in _per_kernel(rows, c).items():
+                per.setdefault(kern, {})[c] = float(np.median(vals[1:] or vals))
+    lines = [f"# hardware counters of the GEMM kernels, {workload}",
+             "# commands (one pass each):"] + [f"#   {c}" for c in command.split(" ;; ")] + [
+             "# values: median per dispatch over the dispatches after the first (the cold warm-up);",
+             "# sums over the chip's instances; GRBM_GUI_ACTIVE once per XCD (8), so duration = it / 8 clocks",
+             f"# sources_digest: {gemm_sources_digest()}"]
     for stage in ("fc1", "fc2"):
         try:
-            kern = _stage_kernel(kernels, stage)
+            kern = _stage_kernel(per.keys(), stage)
         except SystemExit:
             continue
+        v = per[kern]
         lines.append(f"{stage}: {kern}")
-        for c in names:
-            v = per[c].get(kern, [])
-            if v:
-                lines.append(f"  {c:40s} {float(np.median(v[1:] or v)):18.1f}")
+        for c in sorted(v):
+            lines.append(f"  {c:44s} {v[c]:20.1f}")
+        for name, x in _derived(v):
+            lines.append(f"  = {name:52s} {x:10.2f}")
     path = os.path.join(ROOT, "profiles", f"{workload}_{tag}_counters.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
