@@ -183,7 +183,7 @@ def _percentiles(ms):
             "p90": round(float(np.quantile(a, 0.9)), 5)}
 
 
-def measure(cfg, steps, warmup, dev, want_cpu, mall_flush):
+def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
     """Time one workload; returns the result fields of its line."""
     import torch
     import block_scaled_mxfp4_amd as B
@@ -208,7 +208,7 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush):
         return B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
                               local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
                               act_mode=spec["mode"], act_prequantized=prequantized, topk_packed=packed,
-                              out_dtype="f32")
+                              out_dtype="f32", tactic=tactic)
 
     x_bf16 = d(inp["hidden_states"])
     prob = problem(w4a8)
@@ -566,6 +566,8 @@ def main(argv=None):
     ap.add_argument("--decode-config", type=int, default=1, help="workload reported beside it (-1: none)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tactic", default="-1,-1", help="FC1,FC2 tactic ids of the headline workload (-1,-1: the planner's)")
+    ap.add_argument("--decode-tactic", default="-1,-1", help="FC1,FC2 tactic ids of the workload beside it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -596,7 +598,9 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False)
+    tac = tuple(int(v) for v in args.tactic.split(","))
+    dtac = tuple(int(v) for v in args.decode_tactic.split(","))
+    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac)
     res = {
         "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
         "value": head.pop("value"),
@@ -614,7 +618,7 @@ def main(argv=None):
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_decode and args.decode_config >= 0 and args.decode_config != args.config:
-        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True)
+        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac)
         res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)

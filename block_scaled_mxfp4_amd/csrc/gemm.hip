@@ -474,6 +474,22 @@ __device__ __forceinline__ void load_step(Step<FP8>& b, const DecodeGeo& d, int 
   }
 }
 
+// w4a8 step j with the activation rows in LDS (the fused kernel's FC2 reads
+// its m-tile's h there: E4M3 [16][K], then the E8M0 scales [16][K / 32]):
+// the weights from memory, this lane's pieces and scale from LDS.
+__device__ __forceinline__ void load_step_x8_lds(Step<true>& b, const DecodeGeo& d, int j) {
+  load_w(b.w, d, j);
+  const int kb = 4 * j + d.g;
+  const bool has = d.x_row != kOob;
+  const bool lo_ok = has && 4 * j + (d.g >> 1) < d.nkb, hi_ok = has && 4 * j + 2 + (d.g >> 1) < d.nkb;
+  const uint8_t* row = d.x_lds + d.x_lds_off + 128u * j + 16u * d.g;
+  const uint4 lo = *reinterpret_cast<const uint4*>(lo_ok ? row : d.x_lds);
+  const uint4 hi = *reinterpret_cast<const uint4*>(hi_ok ? row + 64 : d.x_lds);
+  b.x[0] = lo_ok ? lo : make_uint4(0, 0, 0, 0);
+  b.x[1] = hi_ok ? hi : make_uint4(0, 0, 0, 0);
+  b.xs = (has && kb < d.nkb) ? (uint32_t)d.x_lds[16 * 32 * d.nkb + d.xs_row + kb] : 127u;
+}
+
 // w4a16 step j: the weight pieces dequantized to bf16 by their E8M0 scales
 // (staged in LDS), times the activation piece.
 template <bool NV = false>
@@ -531,7 +547,10 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 __host__ __device__ constexpr uint32_t decode_lds_scales(int units_per_wg, int sbr) {
   return (uint32_t)(units_per_wg * 64 * sbr + 15) / 16u * 16u;
 }
-__host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) { return ksplit > 1 ? 4u * 4u * kWave * 16u : 0u; }
+// split-K partial sums: one 4-tile set per wave that is not its unit's lead
+__host__ __device__ constexpr uint32_t decode_lds_red(int ksplit) {
+  return ksplit > 1 ? (uint32_t)((4 / ksplit) * (ksplit - 1)) * 4u * kWave * 16u : 0u;
+}
 // w4a16: an m-tile of at most decode_x_rows() tokens has its activation rows
 // staged in LDS once per work item; its pieces then travel in the register
 // ring from LDS instead of every wave loading its lanes' pieces (mostly past
@@ -558,9 +577,12 @@ __host__ __device__ constexpr uint32_t decode_lds_bytes(int ksplit, int sbr, uin
 // fp32 y.  acc[q] holds weight tile q x the group's 16 tokens; this lane owns
 // token p (valid: inside the group) and rows 4g..4g+3 of each tile.
 // Per-expert parameters come through scalar loads.
-template <bool FP8, bool FC1, bool GEN>
+// FUSED (FC1 of the fused decode kernel): h goes to the m-tile's rows in LDS
+// at hb (bf16 [16][I], or E4M3 [16][I] then the E8M0 scales [16][I / 32])
+// instead of to memory; row p - p0.
+template <bool FP8, bool FC1, bool GEN, bool FUSED = false>
 __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 acc[4], int l, int p, bool valid,
-                                                int n0, int g, int ntiles) {
+                                                int n0, int g, int ntiles, uint8_t* hb = nullptr, int p0 = 0) {
   if constexpr (FC1) {
     const int I = a.N;
     float hv[2][4];
@@ -587,7 +609,8 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
     }
     if constexpr (!FP8) {
       if (valid) {
-        uint16_t* hrow = static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+        uint16_t* hrow = FUSED ? reinterpret_cast<uint16_t*>(hb) + (p - p0) * I + n0 + 4 * g
+                               : static_cast<uint16_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
         uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -608,7 +631,7 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
       if (valid) {
         const uint32_t code = e8m0_code_for_e4m3(amax);
         const int sh = 127 - (int)code;
-        uint8_t* hrow = static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
+        uint8_t* hrow = FUSED ? hb + (p - p0) * I + n0 + 4 * g : static_cast<uint8_t*>(a.out) + (int64_t)p * I + n0 + 4 * g;
         uint16_t* lrow = (GEN && a.lora_out) ? a.lora_out + j * I + n0 + 4 * g : nullptr;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -618,7 +641,10 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
           *reinterpret_cast<uint32_t*>(hrow + 16 * half) = packed;
           if (lrow) *reinterpret_cast<uint2*>(lrow + 16 * half) = e4m3x4_to_bf16x4(packed, (int)code);
         }
-        if (g == 0) a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
+        if (g == 0) {
+          if (FUSED) hb[16 * I + (p - p0) * (I / 32) + n0 / 32] = (uint8_t)code;
+          else a.out_scale[(int64_t)p * (I / 32) + n0 / 32] = (uint8_t)code;
+        }
       }
     }
   } else {
@@ -631,11 +657,15 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
   }
 }
 
-template <bool FP8, bool FC1, int KSPLIT, bool NV = false, bool GEN = false>
-__global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
+// One work item of a decode GEMM: the workgroup's UNITS_PER_WG units (weight
+// row groups) starting at unit0 for m-tile mt.  FUSED: a pass of the fused
+// decode kernel, whose m-tile rows of h live in LDS at hb: FC1 writes them
+// there (and stages no activation rows), FC2 reads them there.
+template <bool FP8, bool FC1, int KSPLIT, bool NV, bool GEN, bool FUSED>
+__device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int mt, int unit0, uint8_t* hb) {
   static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
+  static_assert(!(FUSED && NV), "the fused decode kernel takes MXFP4 weights");
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
-  extern __shared__ __align__(16) uint8_t lds[];
   // wave-uniform values are made visibly uniform (readfirstlane, scalar
   // loads of the routing tables) so buffer resources stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -647,195 +677,207 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
   const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
   const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
   const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
-  const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
-  const int total = mtiles[a.E_l] * n_wgn;
   const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
   const int n_rows = FC1 ? 2 * a.N : a.N;          // weight rows per expert
   // this wave's K steps: every KSPLIT-th step from ks (interleaved)
   const int my_steps = steps > ks ? (steps - ks + KSPLIT - 1) / KSPLIT : 0;
   auto jstep = [&](int s) { return ks + KSPLIT * s; };
-  // the activation rows during the K loop, then the partial sums [4 waves][4][64]
+  // the activation rows during the K loop, then the split-K partial sums
   uint8_t* const x_stage = lds + decode_lds_scales(UNITS_PER_WG, sbr);
   f32x4* red = reinterpret_cast<f32x4*>(x_stage);
   constexpr bool XL = !FP8;                    // w4a16 may stage its activation rows
   constexpr int DW = FC1 ? kDecodeWDepthFc1 : (KSPLIT > 1 ? kDecodeWDepthFc2Split : 1);
 
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int mt = w / n_wgn;
-    const int unit0 = (w % n_wgn) * UNITS_PER_WG;
-    const int unit = unit0 + uw;
-    const bool active = unit < units;  // uniform per wave; idle waves still meet the barriers
-    const int l = tile_expert[mt];
-    const int p0 = offsets[l] + (mt - mtiles[l]) * 16;
-    const int p1 = min(offsets[l + 1], p0 + 16);
-    const int p = p0 + r;
-    const bool valid = p < p1;
+  const int unit = unit0 + uw;
+  const bool active = unit < units;  // uniform per wave; idle waves still meet the barriers
+  const int l = tile_expert[mt];
+  const int p0 = offsets[l] + (mt - mtiles[l]) * 16;
+  const int p1 = min(offsets[l + 1], p0 + 16);
+  const int p = p0 + r;
+  const bool valid = p < p1;
 
-    // stage the scales of the workgroup's units in LDS (16-byte loads)
-    {
-      const size_t sexp = (size_t)n_rows * sbr;
-      const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ws + (size_t)l * sexp, (uint32_t)sexp);
-      const int chunks_per_unit = 4 * sbr;       // 64 rows x sbr bytes / 16
-      for (int c = threadIdx.x; c < UNITS_PER_WG * chunks_per_unit; c += kGemmThreads) {
-        const int u = c / chunks_per_unit, cc = c % chunks_per_unit;
-        uint32_t src;
-        if constexpr (FC1) {
-          const int half = cc / (2 * sbr), within = cc % (2 * sbr);
-          const int row = (half ? a.N : 0) + (unit0 + u) * kFc1ColsPerWave;
-          src = (unit0 + u < units) ? (uint32_t)row * sbr + 16u * within : kOob;
-        } else {
-          src = (uint32_t)(unit0 + u) * kFc2RowsPerWave * sbr + 16u * cc;   // rows past H read 0
-        }
-        *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * sbr + 16 * cc) = bload16(sr, src);
-      }
-    }
-    // w4a16 with few tokens: stage the m-tile's activation rows (16-byte loads)
-    const bool x_in_lds = p1 - p0 <= decode_x_rows(KSPLIT, sbr, K, FP8, FC1);   // uniform
-    if constexpr (XL) {
-      if (x_in_lds) {
-        const int row_chunks = K / 8;               // K bf16 values / 16 bytes
-        // FC1 rows x[perm[p] / k]; FC2 rows h[p], addressed from the m-tile's first
-        const __amdgpu_buffer_rsrc_t xr =
-            FC1 ? make_rsrc(a.act, 0x7fffffff)
-                : make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
-        for (int c = threadIdx.x; c < (p1 - p0) * row_chunks; c += kGemmThreads) {
-          const int i = c / row_chunks, cc = c % row_chunks;
-          const uint32_t row = FC1 ? (uint32_t)(a.perm[p0 + i] / a.top_k) : (uint32_t)i;
-          *reinterpret_cast<uint4*>(x_stage + (size_t)i * K * 2 + 16 * cc) = bload16(xr, row * arow_bytes + 16u * cc);
-        }
-      }
-    }
-
-    f32x4 acc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    DecodeGeo d;
-    int n0 = 0, ntiles = 4;
-    if (active) {
-      const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
-      d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
-      d.nkb = nkb;
-      if constexpr (NV) d.sbr = sbr;
-      d.g = g;
-      d.r = r;
-      uint32_t dr[4];
+  // stage the scales of the workgroup's units in LDS (16-byte loads)
+  {
+    const size_t sexp = (size_t)n_rows * sbr;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ws + (size_t)l * sexp, (uint32_t)sexp);
+    const int chunks_per_unit = 4 * sbr;       // 64 rows x sbr bytes / 16
+    for (int c = threadIdx.x; c < UNITS_PER_WG * chunks_per_unit; c += kGemmThreads) {
+      const int u = c / chunks_per_unit, cc = c % chunks_per_unit;
+      uint32_t src;
       if constexpr (FC1) {
-        n0 = unit * kFc1ColsPerWave;
-        dr[0] = 0; dr[1] = 16; dr[2] = a.N; dr[3] = a.N + 16;
+        const int half = cc / (2 * sbr), within = cc % (2 * sbr);
+        const int row = (half ? a.N : 0) + (unit0 + u) * kFc1ColsPerWave;
+        src = (unit0 + u < units) ? (uint32_t)row * sbr + 16u * within : kOob;
       } else {
-        n0 = unit * kFc2RowsPerWave;
-        ntiles = min(4, (a.N - n0) / 16);
-        dr[0] = 0; dr[1] = 16; dr[2] = 32; dr[3] = 48;
+        src = (uint32_t)(unit0 + u) * kFc2RowsPerWave * sbr + 16u * cc;   // rows past H read 0
       }
-      d.ntiles = ntiles;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
-      d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2);
-      d.s_lds = lds + (size_t)uw * 64 * sbr;
-      d.x_lds = x_in_lds ? x_stage : nullptr;
-      d.x_lds_off = valid ? (uint32_t)r * arow_bytes : 0u;
-      if constexpr (FC1) {
-        const uint32_t t = valid ? (uint32_t)(a.perm[p] / a.top_k) : 0u;
-        d.xr = make_rsrc(a.act, 0x7fffffff);
-        d.x_row = valid ? t * arow_bytes : kOob;
-        d.xsr = make_rsrc(FP8 ? a.act_scale : a.act, 0x7fffffff);
-        d.xs_row = t * (uint32_t)nkb;
-      } else {
-        d.xr = make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
-        d.x_row = valid ? (uint32_t)r * arow_bytes : kOob;
-        d.xsr = make_rsrc(FP8 ? a.act_scale + (size_t)p0 * nkb : static_cast<const uint8_t*>(a.act),
-                          16u * (uint32_t)nkb);
-        d.xs_row = (uint32_t)r * (uint32_t)nkb;
-      }
+      *reinterpret_cast<uint4*>(lds + (size_t)u * 64 * sbr + 16 * cc) = bload16(sr, src);
     }
-    if constexpr (XL) {
-      // w4a16: weights DW steps ahead in a ring of DW + 1 register sets (the
-      // first DW requested before the staging barrier), the activation piece
-      // of the next step in a ring of two, read during the current step from
-      // LDS (staged m-tile) or from memory; NU steps per pass keep both ring
-      // indices compile-time constants
-      constexpr int NW = DW + 1, NU = NW % 2 == 0 ? NW : 2 * NW;
-      Step<FP8> wr[NW], xr[2];           // .w of the one ring, .x of the other
-      if (active) {
-#pragma unroll
-        for (int u = 0; u < DW; ++u)
-          if (u < my_steps) load_w(wr[u].w, d, jstep(u));
-        if (!x_in_lds && my_steps > 0) load_x_mem(xr[0].x, d, jstep(0));
-      }
-      __syncthreads();   // staged scales and activation rows visible
-      if (active) {
-        if (x_in_lds && my_steps > 0) load_x_lds(xr[0].x, d, jstep(0));
-#pragma unroll 1
-        for (int i = 0; i < my_steps; i += NU) {
-#pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            const int s = i + u;
-            if (s < my_steps) {
-              if (s + DW < my_steps) load_w(wr[(u + DW) % NW].w, d, jstep(s + DW));
-              if (s + 1 < my_steps) {
-                if (x_in_lds) load_x_lds(xr[(u + 1) % 2].x, d, jstep(s + 1));
-                else load_x_mem(xr[(u + 1) % 2].x, d, jstep(s + 1));
-              }
-              __builtin_amdgcn_sched_barrier(0);
-              compute_w4a16<NV>(wr[u % NW].w, xr[u % 2].x, d, jstep(s), acc);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
-      }
-    } else {
-      // w4a8: the weights and activation pieces of the next kDecodeDepth
-      // steps are in flight while the current one is computed (the first
-      // ones requested before the staging barrier); a ring of kDecodeDepth + 1
-      // register buffers rotated by unrolling (compile-time indices);
-      // sched_barrier(0) keeps each prefetch ahead of its compute
-      constexpr int NB = kDecodeDepth + 1;
-      Step<FP8> buf[NB];
-      if (active) {
-#pragma unroll
-        for (int u = 0; u < kDecodeDepth; ++u)
-          if (u < my_steps) load_step<FP8>(buf[u], d, jstep(u));
-      }
-      __syncthreads();   // staged scales visible
-      if (active) {
-#pragma unroll 1
-        for (int i = 0; i < my_steps; i += NB) {
-#pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            if (i + u < my_steps) {
-              if (i + u + kDecodeDepth < my_steps)
-                load_step<FP8>(buf[(u + kDecodeDepth) % NB], d, jstep(i + u + kDecodeDepth));
-              __builtin_amdgcn_sched_barrier(0);
-              compute_step<FP8>(buf[u], d, jstep(i + u), acc);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
-      }
-    }
-
-    // split-K reduction in a fixed order
-    bool lead = active;
-    if constexpr (KSPLIT > 1) {
-      if (XL && x_in_lds) __syncthreads();   // uniform: every wave is done with the staged rows
-      if (active && ks != 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) red[(wave * 4 + q) * kWave + lane] = acc[q];
-      }
-      __syncthreads();
-      lead = active && ks == 0;
-      if (lead) {
-#pragma unroll
-        for (int s2 = 1; s2 < KSPLIT; ++s2)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] += red[((wave + s2) * 4 + q) * kWave + lane];
-      }
-    }
-
-    if (lead) decode_epilogue<FP8, FC1, GEN>(a, acc, l, p, valid, n0, g, ntiles);
-    __syncthreads();   // staged scales and partial sums are reused by the next work item
   }
+  // w4a16 with few tokens: stage the m-tile's activation rows (16-byte loads);
+  // the fused FC2 finds its rows (h) in LDS already, the fused FC1 reads x from memory
+  const bool x_in_lds = FUSED ? !FC1 : p1 - p0 <= decode_x_rows(KSPLIT, sbr, K, FP8, FC1);   // uniform
+  if constexpr (XL && !FUSED) {
+    if (x_in_lds) {
+      const int row_chunks = K / 8;               // K bf16 values / 16 bytes
+      // FC1 rows x[perm[p] / k]; FC2 rows h[p], addressed from the m-tile's first
+      const __amdgpu_buffer_rsrc_t xr =
+          FC1 ? make_rsrc(a.act, 0x7fffffff)
+              : make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
+      for (int c = threadIdx.x; c < (p1 - p0) * row_chunks; c += kGemmThreads) {
+        const int i = c / row_chunks, cc = c % row_chunks;
+        const uint32_t row = FC1 ? (uint32_t)(a.perm[p0 + i] / a.top_k) : (uint32_t)i;
+        *reinterpret_cast<uint4*>(x_stage + (size_t)i * K * 2 + 16 * cc) = bload16(xr, row * arow_bytes + 16u * cc);
+      }
+    }
+  }
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  DecodeGeo d;
+  int n0 = 0, ntiles = 4;
+  if (active) {
+    const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+    d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
+    d.nkb = nkb;
+    if constexpr (NV) d.sbr = sbr;
+    d.g = g;
+    d.r = r;
+    uint32_t dr[4];
+    if constexpr (FC1) {
+      n0 = unit * kFc1ColsPerWave;
+      dr[0] = 0; dr[1] = 16; dr[2] = a.N; dr[3] = a.N + 16;
+    } else {
+      n0 = unit * kFc2RowsPerWave;
+      ntiles = min(4, (a.N - n0) / 16);
+      dr[0] = 0; dr[1] = 16; dr[2] = 32; dr[3] = 48;
+    }
+    d.ntiles = ntiles;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
+    d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2);
+    d.s_lds = lds + (size_t)uw * 64 * sbr;
+    d.x_lds = x_in_lds ? (FUSED ? hb : x_stage) : nullptr;
+    d.x_lds_off = valid ? (uint32_t)r * arow_bytes : 0u;
+    if constexpr (FC1) {
+      const uint32_t t = valid ? (uint32_t)(a.perm[p] / a.top_k) : 0u;
+      d.xr = make_rsrc(a.act, 0x7fffffff);
+      d.x_row = valid ? t * arow_bytes : kOob;
+      d.xsr = make_rsrc(FP8 ? a.act_scale : a.act, 0x7fffffff);
+      d.xs_row = t * (uint32_t)nkb;
+    } else {
+      d.xr = make_rsrc(static_cast<const uint8_t*>(a.act) + (size_t)p0 * arow_bytes, 16u * arow_bytes);
+      d.x_row = valid ? (uint32_t)r * arow_bytes : kOob;
+      d.xsr = make_rsrc(FP8 ? a.act_scale + (size_t)p0 * nkb : static_cast<const uint8_t*>(a.act),
+                        16u * (uint32_t)nkb);
+      d.xs_row = (uint32_t)r * (uint32_t)nkb;
+      if constexpr (FUSED && FP8) d.x_lds = hb;
+    }
+  }
+  if constexpr (XL) {
+    // w4a16: weights DW steps ahead in a ring of DW + 1 register sets (the
+    // first DW requested before the staging barrier), the activation piece
+    // of the next step in a ring of two, read during the current step from
+    // LDS (staged m-tile) or from memory; NU steps per pass keep both ring
+    // indices compile-time constants
+    constexpr int NW = DW + 1, NU = NW % 2 == 0 ? NW : 2 * NW;
+    Step<FP8> wr[NW], xr[2];           // .w of the one ring, .x of the other
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < DW; ++u)
+        if (u < my_steps) load_w(wr[u].w, d, jstep(u));
+      if (!x_in_lds && my_steps > 0) load_x_mem(xr[0].x, d, jstep(0));
+    }
+    __syncthreads();   // staged scales and activation rows visible
+    if (active) {
+      if (x_in_lds && my_steps > 0) load_x_lds(xr[0].x, d, jstep(0));
+#pragma unroll 1
+      for (int i = 0; i < my_steps; i += NU) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int s = i + u;
+          if (s < my_steps) {
+            if (s + DW < my_steps) load_w(wr[(u + DW) % NW].w, d, jstep(s + DW));
+            if (s + 1 < my_steps) {
+              if (x_in_lds) load_x_lds(xr[(u + 1) % 2].x, d, jstep(s + 1));
+              else load_x_mem(xr[(u + 1) % 2].x, d, jstep(s + 1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            compute_w4a16<NV>(wr[u % NW].w, xr[u % 2].x, d, jstep(s), acc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  } else {
+    // w4a8: the weights and activation pieces of the next kDecodeDepth
+    // steps are in flight while the current one is computed (the first
+    // ones requested before the staging barrier); a ring of kDecodeDepth + 1
+    // register buffers rotated by unrolling (compile-time indices);
+    // sched_barrier(0) keeps each prefetch ahead of its compute
+    constexpr int NB = kDecodeDepth + 1;
+    Step<FP8> buf[NB];
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < kDecodeDepth; ++u)
+        if (u < my_steps) {
+          if constexpr (FUSED && FP8 && !FC1) load_step_x8_lds(buf[u], d, jstep(u));
+          else load_step<FP8>(buf[u], d, jstep(u));
+        }
+    }
+    __syncthreads();   // staged scales visible
+    if (active) {
+#pragma unroll 1
+      for (int i = 0; i < my_steps; i += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (i + u < my_steps) {
+            if (i + u + kDecodeDepth < my_steps) {
+              if constexpr (FUSED && FP8 && !FC1) load_step_x8_lds(buf[(u + kDecodeDepth) % NB], d, jstep(i + u + kDecodeDepth));
+              else load_step<FP8>(buf[(u + kDecodeDepth) % NB], d, jstep(i + u + kDecodeDepth));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step<FP8>(buf[u], d, jstep(i + u), acc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  }
+
+  // split-K reduction in a fixed order
+  bool lead = active;
+  if constexpr (KSPLIT > 1) {
+    if (XL && x_in_lds) __syncthreads();   // uniform: every wave is done with the staged rows
+    if (active && ks != 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[((uw * (KSPLIT - 1) + ks - 1) * 4 + q) * kWave + lane] = acc[q];
+    }
+    __syncthreads();
+    lead = active && ks == 0;
+    if (lead) {
+#pragma unroll
+      for (int s2 = 1; s2 < KSPLIT; ++s2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += red[((uw * (KSPLIT - 1) + s2 - 1) * 4 + q) * kWave + lane];
+    }
+  }
+
+  if (lead) decode_epilogue<FP8, FC1, GEN, FUSED && FC1>(a, acc, l, p, valid, n0, g, ntiles, hb, p0);
+  __syncthreads();   // staged scales and partial sums are reused by the next work item
+}
+
+template <bool FP8, bool FC1, int KSPLIT, bool NV = false, bool GEN = false>
+__global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
+  constexpr int UNITS_PER_WG = 4 / KSPLIT;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
+  const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
+  for (int w = blockIdx.x; w < total; w += gridDim.x)
+    decode_pass<FP8, FC1, KSPLIT, NV, GEN, false>(a, lds, w / n_wgn, (w % n_wgn) * UNITS_PER_WG, nullptr);
 }
 
 // K split for the decode kernels: long K loops are shared by the four waves.
@@ -872,6 +914,83 @@ static hipError_t launch_persistent(const GemmArgs& a, int64_t work, int cus, hi
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(kGemmThreads), lds_bytes, s, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode (the MegaMoE idea of PR 17865, one kernel for both GEMMs, on
+// this library's decode kernels): a workgroup takes one 16-row m-tile through
+// all of FC1 and then all of FC2, and the m-tile's rows of h never leave the
+// CU: FC1's epilogue writes them (bf16, or E4M3 with their E8M0 scales) to
+// LDS, and FC2 reads its activation pieces there.  One launch instead of two,
+// no h round trip through memory, and a CU that finishes its FC1 share goes
+// on to FC2 without waiting for the rest of the grid.  The passes are the
+// unfused kernels' work items (same K split, reduction order and epilogue),
+// so the output equals the unfused path's bit for bit.  Offered where h of
+// one m-tile is small (I <= 768: at most 24 KB of bf16) and FC2's K is not
+// split; MXFP4 weights.  Measured slower than the two unfused launches at 64
+// tokens x 896 experts (H 3584, I 384: 0.326 against 0.282 ms for both
+// GEMMs): its work item is a whole m-tile, about 700 of them for 1024
+// workgroup slots, where the unfused kernels cut each expert into six FC1
+// and fourteen FC2 items; so it is not the planner's first choice.
+struct FusedArgs {
+  GemmArgs fc1, fc2;
+};
+
+__host__ __device__ constexpr uint32_t fused_h_offset(int ks1, int nkb1, int nkb2) {
+  const uint32_t s1 = decode_lds_scales(4 / ks1, nkb1) + decode_lds_red(ks1);
+  const uint32_t s2 = decode_lds_scales(4, nkb2);
+  return ((s1 > s2 ? s1 : s2) + 15u) / 16u * 16u;
+}
+__host__ __device__ constexpr uint32_t fused_h_bytes(bool fp8, int I) {
+  return fp8 ? 16u * (uint32_t)I + 16u * (uint32_t)(I / 32) : 32u * (uint32_t)I;
+}
+
+template <bool FP8, int KS1, bool GEN>
+__global__ __launch_bounds__(kGemmThreads, 4) void decode_fused_kernel(FusedArgs f) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int I = f.fc1.N, H = f.fc2.N;
+  uint8_t* hb = lds + fused_h_offset(KS1, H / 32, I / 32);
+  const int units1 = I / kFc1ColsPerWave, units2 = (H + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
+  const int total = ((cptr)f.fc1.mtiles)[f.fc1.E_l];
+  for (int mt = blockIdx.x; mt < total; mt += gridDim.x) {
+    // every pass ends with a workgroup barrier: FC2 starts on complete rows
+    // of h, and the next m-tile's FC1 overwrites them only after FC2
+    for (int u0 = 0; u0 < units1; u0 += 4 / KS1) decode_pass<FP8, true, KS1, false, GEN, true>(f.fc1, lds, mt, u0, hb);
+    for (int u0 = 0; u0 < units2; u0 += 4) decode_pass<FP8, false, 1, false, false, true>(f.fc2, lds, mt, u0, hb);
+  }
+}
+
+bool fused_decode_ok(int H, int I) {
+  return I % kFc1ColsPerWave == 0 && I <= 768 && (I / 32 + 3) / 4 < 16 && H % 32 == 0;
+}
+
+template <bool FP8, int KS1, bool GEN>
+static hipError_t launch_fused_k(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
+  const uint32_t lds = fused_h_offset(KS1, f.fc1.K / 32, f.fc2.K / 32) + fused_h_bytes(FP8, f.fc1.N);
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(decode_fused_kernel<FP8, KS1, GEN>), kGemmThreads, lds);
+  const int64_t cap = (int64_t)cus * per_cu;
+  const int grid = (int)(max_mtiles < cap ? max_mtiles : cap);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_fused_kernel<FP8, KS1, GEN>), dim3(grid), dim3(kGemmThreads), lds, s, f);
+  return hipGetLastError();
+}
+
+template <bool FP8, bool GEN>
+static hipError_t launch_fused_g(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
+  switch (decode_ksplit(f.fc1.K)) {
+    case 4: return launch_fused_k<FP8, 4, GEN>(f, max_mtiles, cus, s);
+    case 2: return launch_fused_k<FP8, 2, GEN>(f, max_mtiles, cus, s);
+    default: return launch_fused_k<FP8, 1, GEN>(f, max_mtiles, cus, s);
+  }
+}
+
+hipError_t launch_fused_decode(const GemmArgs& fc1, const GemmArgs& fc2, bool fp8, int max_mtiles, int cus,
+                               hipStream_t s) {
+  if (fc1.nvfp4 || !fused_decode_ok(fc2.N, fc1.N) || decode_ksplit(fc2.K) != 1) return hipErrorInvalidValue;
+  const FusedArgs f{fc1, fc2};
+  const bool gen = general_epilogue(fc1);
+  if (fp8) return gen ? launch_fused_g<true, true>(f, max_mtiles, cus, s) : launch_fused_g<true, false>(f, max_mtiles, cus, s);
+  return gen ? launch_fused_g<false, true>(f, max_mtiles, cus, s) : launch_fused_g<false, false>(f, max_mtiles, cus, s);
 }
 
 template <bool FP8, bool FC1, bool NV, bool GEN>

@@ -127,12 +127,22 @@ enum Tactic : int32_t {
   FC1_W4A8_M16 = 2,
   FC1_W4A8_M64 = 3,
   FC1_W4A8_M128 = 4,
+  FC1_FUSED_W4A16_M16 = 5,   // the fused decode kernel: both GEMMs in one launch
+  FC1_FUSED_W4A8_M16 = 6,
   FC2_W4A16_M16 = 16,
   FC2_W4A16_M64 = 17,
   FC2_W4A8_M16 = 18,
   FC2_W4A8_M64 = 19,
   FC2_W4A8_M128 = 20,
+  FC2_FUSED_W4A16_M16 = 21,  // the FC2 half of the fused pairs
+  FC2_FUSED_W4A8_M16 = 22,
 };
+
+// The fused decode kernel (FC1 then FC2 per 16-row m-tile, h kept in LDS):
+// offered for these sizes (hidden H, intermediate I).
+bool fused_decode_ok(int H, int I);
+hipError_t launch_fused_decode(const GemmArgs& fc1, const GemmArgs& fc2, bool fp8, int max_mtiles, int cus,
+                               hipStream_t s);
 
 // Workgroup shapes of the grouped GEMMs (4 waves of 64 lanes).
 constexpr int kGemmThreads = 256;

@@ -75,11 +75,15 @@ const TacticInfo kTactics[] = {
     {situ::FC1_W4A8_M16, "fc1_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, true},
     {situ::FC1_W4A8_M64, "fc1_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, true},
     {situ::FC1_W4A8_M128, "fc1_w4a8_scalemfma_m128", SITU_ACT_W4A8, 128, true},
+    {situ::FC1_FUSED_W4A16_M16, "fused_decode_w4a16_bf16mfma_m16", SITU_ACT_W4A16, 16, true},
+    {situ::FC1_FUSED_W4A8_M16, "fused_decode_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, true},
     {situ::FC2_W4A16_M16, "fc2_w4a16_bf16mfma_m16", SITU_ACT_W4A16, 16, false},
     {situ::FC2_W4A16_M64, "fc2_w4a16_bf16mfma_m64", SITU_ACT_W4A16, 64, false},
     {situ::FC2_W4A8_M16, "fc2_w4a8_scalemfma_m16", SITU_ACT_W4A8, 16, false},
     {situ::FC2_W4A8_M64, "fc2_w4a8_scalemfma_m64", SITU_ACT_W4A8, 64, false},
     {situ::FC2_W4A8_M128, "fc2_w4a8_scalemfma_m128", SITU_ACT_W4A8, 128, false},
+    {situ::FC2_FUSED_W4A16_M16, "fused_decode_w4a16_fc2_half", SITU_ACT_W4A16, 16, false},
+    {situ::FC2_FUSED_W4A8_M16, "fused_decode_w4a8_fc2_half", SITU_ACT_W4A8, 16, false},
 };
 
 const TacticInfo* find_tactic(int32_t id) {
@@ -143,18 +147,23 @@ int valid_pairs(const situ_moe_problem* p, int32_t* fc1, int32_t* fc2, int cap) 
   const int32_t m64[2] = {w4a8 ? situ::FC1_W4A8_M64 : situ::FC1_W4A16_M64,
                           w4a8 ? situ::FC2_W4A8_M64 : situ::FC2_W4A16_M64};
   const int32_t m128[2] = {situ::FC1_W4A8_M128, situ::FC2_W4A8_M128};
+  // the fused decode pair (both GEMMs in one launch, h kept on chip)
+  const int32_t fused[2] = {w4a8 ? situ::FC1_FUSED_W4A8_M16 : situ::FC1_FUSED_W4A16_M16,
+                            w4a8 ? situ::FC2_FUSED_W4A8_M16 : situ::FC2_FUSED_W4A16_M16};
+  const bool fuse = p->weight_format == SITU_WEIGHTS_MXFP4 && situ::fused_decode_ok(p->hidden_size, p->intermediate_size);
   const int64_t TK = (int64_t)p->num_tokens * p->top_k;
   const int64_t mt128 = (TK + 127) / 128 + p->local_num_experts;
   const bool wide = w4a8 && p->hidden_size % 128 == 0 && p->intermediate_size % 128 == 0 &&
                     mt128 * 128 * p->intermediate_size < ((int64_t)1 << 31);
   const double rows_per_expert = (double)TK / p->local_num_experts;
-  const int32_t* order[3] = {m16, m64, m128};
+  const int32_t* order[4] = {m16, m64, m128, fused};
   int n_order = wide ? 3 : 2;
   if (wide && rows_per_expert > kWideRowsPerExpert) {
     order[0] = m128; order[1] = m64; order[2] = m16;
   } else if (rows_per_expert > 48.0) {
     order[0] = m64; order[1] = m16;
   }
+  if (fuse) order[n_order++] = fused;
   int n = 0;
   for (int i = 0; i < n_order; ++i) {
     if (n < cap) { fc1[n] = order[i][0]; fc2[n] = order[i][1]; }
@@ -433,8 +442,12 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
       (st = launch_status(situ::launch_zero_nonlocal_rows(ra.inv, t->activation_lora_input, (int64_t)T * p.top_k,
                                                           (int32_t)I, s), "lora rows")) != SITU_OK)
     return st;
-  if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, plan->max_mtiles, cus, s), "fc1")) != SITU_OK) return st;
-  if ((st = mark(3)) != SITU_OK) return st;
+  const bool fused = plan->fc1_tactic == situ::FC1_FUSED_W4A16_M16 || plan->fc1_tactic == situ::FC1_FUSED_W4A8_M16;
+  if (!fused) {
+    if ((st = launch_status(situ::launch_fc1(plan->fc1_tactic, g, plan->max_mtiles, cus, s), "fc1")) != SITU_OK) return st;
+    if ((st = mark(3)) != SITU_OK) return st;
+  }
+  const situ::GemmArgs g1 = g;
 
   // FC2
   g.act = at<void>(ws, plan->off_h);
@@ -449,7 +462,13 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.out = at<void>(ws, plan->off_y);
   g.out_scale = plan->y_format == 1 ? at<uint8_t>(ws, plan->off_y_exp) : nullptr;
   g.out_rows = (int32_t)((int64_t)T * p.top_k);
-  if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, plan->max_mtiles, cus, s), "fc2")) != SITU_OK) return st;
+  if (fused) {   // one launch for both GEMMs: its time is the FC1 stage's
+    if ((st = launch_status(situ::launch_fused_decode(g1, g, w4a8, plan->max_mtiles, cus, s), "fused fc1+fc2")) != SITU_OK)
+      return st;
+    if ((st = mark(3)) != SITU_OK) return st;
+  } else if ((st = launch_status(situ::launch_fc2(plan->fc2_tactic, g, plan->max_mtiles, cus, s), "fc2")) != SITU_OK) {
+    return st;
+  }
   if ((st = mark(4)) != SITU_OK) return st;
 
   // combine
