@@ -186,8 +186,12 @@ def _percentiles(ms):
             "p90": round(float(np.quantile(a, 0.9)), 5)}
 
 
-def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
-    """Time one workload; returns the result fields of its line."""
+def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled"):
+    """Time one workload; returns the result fields of its line.  weights:
+    "tiled" hands the layer its MXFP4 weights in the fragment-tiled layout
+    (made once by situ_moe_tile_weights before timing; the same values, so
+    the same output bit for bit) and times the row-major weights beside it;
+    "rows" times the row-major weights only."""
     import torch
     import block_scaled_mxfp4_amd as B
     import synthetic as S
@@ -207,11 +211,14 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
     w4a8 = spec["mode"] == "w4a8"
 
-    def problem(prequantized):
+    tiled = weights == "tiled"
+    wf = "mxfp4_tiled" if tiled else "mxfp4"
+
+    def problem(prequantized, weight_format=wf):
         return B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
                               local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
                               act_mode=spec["mode"], act_prequantized=prequantized, topk_packed=packed,
-                              out_dtype="f32", tactic=tactic)
+                              out_dtype="f32", tactic=tactic, weight_format=weight_format)
 
     x_bf16 = d(inp["hidden_states"])
     prob = problem(w4a8)
@@ -232,6 +239,11 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
     else:
         tens["topk_ids"] = d(inp["topk_ids"])
         tens["topk_weights"] = d(inp["topk_weights"])
+    row_major = {key: tens[key] for key in ("w1", "w1_scale", "w2", "w2_scale")}
+    if tiled:   # the weights' one-time rearrangement, outside every timed region
+        tens["w1"], tens["w1_scale"] = B.situ_moe_tile_weights(tens["w1"], tens["w1_scale"])
+        tens["w2"], tens["w2_scale"] = B.situ_moe_tile_weights(tens["w2"], tens["w2_scale"])
+        torch.cuda.synchronize()
     ts = B.make_tensors(prob, **tens)
     ws = B.new_workspace(plan, dev)
     stream = torch.cuda.current_stream(dev)
@@ -306,6 +318,25 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
         del graph
     except Exception as e:   # capture unavailable: reported, the eager number stands regardless
         graph_error = f"{type(e).__name__}: {e}"
+
+    rows_ms = None
+    if tiled:   # the same step from the row-major weights
+        plan_r = B.situ_moe_plan(problem(w4a8, "mxfp4"))
+        assert plan_r.workspace_bytes <= plan.workspace_bytes
+        out_r = torch.empty_like(tens["out"])
+        ts_r = B.make_tensors(plan_r.prob, **dict(tens, out=out_r, **row_major))
+        for _ in range(3):
+            B.situ_moe_run(plan_r, ts_r, ws)
+        torch.cuda.synchronize()
+        rs, re_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        rs.record(stream)
+        for _ in range(K):
+            B.situ_moe_run(plan_r, ts_r, ws)
+        re_.record(stream)
+        torch.cuda.synchronize()
+        rows_ms = rs.elapsed_time(re_) / K
+        rows_same = bool(torch.equal(out_r.view(torch.int32), eager_out.view(torch.int32)))
+        del out_r
 
     bf16_input_ms = None
     if w4a8:   # bf16 activations, quantized by the library inside the step
@@ -392,7 +423,9 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
                    "topk_format": "packed" if packed else "ids+weights",
                    "active_local_experts": work["A"], "local_pairs": work["P"],
                    "fc1_tactic": B.situ_moe_tactic_name(plan.fc1_tactic),
-                   "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic)},
+                   "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic),
+                   "weights": "MXFP4, fragment-tiled once by situ_moe_tile_weights before timing" if tiled
+                              else "MXFP4, row-major"},
         "roofline": roof,
         "roofline_other_gemm": {kk: other[kk] for kk in ("kernel", "bound", "achieved", "unit", "frac", "traffic")},
         "stage_ms": {kk: round(v, 5) for kk, v in stage_ms.items()},
@@ -407,6 +440,10 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1)):
     }
     if flushed is not None:
         res["step_ms_mall_flushed"] = flushed
+    if rows_ms is not None:
+        res["row_major_weights"] = {"ms_per_step": round(rows_ms, 5), "tokens_per_s": round(T / (rows_ms * 1e-3), 1),
+                                    "bitwise_equal_to_tiled": rows_same,
+                                    "note": "the same step from the row-major MXFP4 weights"}
     if bf16_input_ms is not None:
         res["bf16_input"] = {"ms_per_step": round(bf16_input_ms, 5),
                              "tokens_per_s": round(T / (bf16_input_ms * 1e-3), 1),
@@ -581,6 +618,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tactic", default="-1,-1", help="FC1,FC2 tactic ids of the headline workload (-1,-1: the planner's)")
     ap.add_argument("--decode-tactic", default="-1,-1", help="FC1,FC2 tactic ids of the workload beside it")
+    ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
+                    help="MXFP4 weight layout handed to the layer (tiled: the row-major step is timed beside it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -613,7 +652,7 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     tac = tuple(int(v) for v in args.tactic.split(","))
     dtac = tuple(int(v) for v in args.decode_tactic.split(","))
-    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac)
+    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac, weights=args.weights)
     res = {
         "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
         "value": head.pop("value"),
@@ -631,7 +670,7 @@ def main(argv=None):
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_decode and args.decode_config >= 0 and args.decode_config != args.config:
-        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac)
+        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac, weights=args.weights)
         res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)

@@ -10,7 +10,7 @@ built, every entry point raises; there is no CPU fallback.
 
 Names mirror the C entry points: situ_moe_plan, situ_moe_valid_tactics,
 situ_moe_run, situ_moe_run_profiled, situ_moe_run_static, situ_moe_route, situ_moe_quantize_mxfp8,
-situ_moe_status_string,
+situ_moe_tile_weights, situ_moe_status_string,
 situ_moe_last_error, situ_moe_build_info, situ_moe_tactic_name,
 situ_moe_abi_version.  situ_moe(...) is the keyword-only one-call form.
 """
@@ -22,7 +22,7 @@ __all__ = [
     "SituMoeError", "SituMoeProblem", "SituMoePlan", "SituMoeTensors", "library_path", "load",
     "situ_moe_plan", "situ_moe_valid_tactics", "situ_moe_run", "situ_moe_run_profiled", "situ_moe_run_static",
     "situ_moe_route",
-    "situ_moe_quantize_mxfp8", "situ_moe_status_string", "situ_moe_last_error",
+    "situ_moe_quantize_mxfp8", "situ_moe_tile_weights", "situ_moe_status_string", "situ_moe_last_error",
     "situ_moe_build_info", "situ_moe_tactic_name", "situ_moe_abi_version", "situ_moe",
     "make_problem", "make_tensors", "new_workspace", "workspace_view", "ACT_W4A16", "ACT_W4A8", "OUT_F32", "OUT_BF16",
 ]
@@ -30,8 +30,8 @@ __all__ = [
 ACT_W4A16, ACT_W4A8 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 ACTIVATIONS = {"situ": 0, "swiglu": 1, "swiglu_bias": 2}
-WEIGHT_FORMATS = {"mxfp4": 0, "nvfp4": 1}
-ABI_VERSION = 2
+WEIGHT_FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxfp4_tiled": 2}
+ABI_VERSION = 3
 STATUS_NAMES = {0: "SITU_OK", 1: "SITU_E_NULL_ARG", 2: "SITU_E_BAD_SHAPE", 3: "SITU_E_UNSUPPORTED",
                 4: "SITU_E_MISSING_SCALE", 5: "SITU_E_DEVICE", 6: "SITU_E_WORKSPACE", 7: "SITU_E_LAUNCH"}
 
@@ -104,6 +104,7 @@ def load():
         "situ_moe_run_profiled": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp, c_u64, vp, P(vp), c_int]),
         "situ_moe_run_static": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp]),
         "situ_moe_quantize_mxfp8": (c_int, [vp, c_i64, c_int, vp, vp, vp]),
+        "situ_moe_tile_weights": (c_int, [vp, vp, c_int, c_int, c_int, vp, vp, vp]),
         "situ_moe_status_string": (ctypes.c_char_p, [c_int]),
         "situ_moe_last_error": (ctypes.c_char_p, []),
         "situ_moe_build_info": (ctypes.c_char_p, []),
@@ -216,6 +217,35 @@ def situ_moe_quantize_mxfp8(x, codes, scales, stream=None):
     _check(load().situ_moe_quantize_mxfp8(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
+def tiled_shapes(experts, rows, k):
+    """Shapes of the fragment-tiled weights and scales of an [experts, rows, k] MXFP4 matrix."""
+    steps = (k // 32 + 3) // 4
+    return (experts, rows // 16, steps, 1024), (experts, rows // 16, steps, 64)
+
+
+def situ_moe_tile_weights(w, w_scale, w_tiled=None, scale_tiled=None, stream=None):
+    """MXFP4 weights w uint8 [E, rows, k/2] with scales uint8 [E, rows, k/32]
+    (cuda) in the fragment-tiled layout of situ_moe_tile_weights; returns
+    (w_tiled, scale_tiled), allocated here when not given."""
+    import torch
+    if w.dim() != 3:
+        raise SituMoeError(2, "w must be [experts, rows, k/2]")
+    E, R, half_k = w.shape
+    k = 2 * half_k
+    _need(w, torch.uint8, (E, R, half_k), "w")
+    _need(w_scale, torch.uint8, (E, R, k // 32), "w_scale")
+    ws_shape, ss_shape = tiled_shapes(E, R, k)
+    if w_tiled is None:
+        w_tiled = torch.empty(ws_shape, dtype=torch.uint8, device=w.device)
+    if scale_tiled is None:
+        scale_tiled = torch.empty(ss_shape, dtype=torch.uint8, device=w.device)
+    _need(w_tiled, torch.uint8, ws_shape, "w_tiled")
+    _need(scale_tiled, torch.uint8, ss_shape, "scale_tiled")
+    _check(load().situ_moe_tile_weights(_ptr(w), _ptr(w_scale), E, R, k, _ptr(w_tiled), _ptr(scale_tiled),
+                                        _stream(stream)))
+    return w_tiled, scale_tiled
+
+
 # ------------------------------------------------------------------ helpers
 
 def _ptr(t):
@@ -275,11 +305,17 @@ def make_tensors(problem, *, hidden_states, hidden_states_scale=None, topk_ids=N
     else:
         _need(topk_ids, torch.int32, (T, k), "topk_ids")
         _need(topk_weights, torch.bfloat16, (T, k), "topk_weights")
-    sblk = 16 if p.weight_format == WEIGHT_FORMATS["nvfp4"] else 32   # K elements per weight scale
-    _need(w1, torch.uint8, (E, 2 * I, H // 2), "w1")
-    _need(w1_scale, torch.uint8, (E, 2 * I, H // sblk), "w1_scale")
-    _need(w2, torch.uint8, (E, H, I // 2), "w2")
-    _need(w2_scale, torch.uint8, (E, H, I // sblk), "w2_scale")
+    if p.weight_format == WEIGHT_FORMATS["mxfp4_tiled"]:
+        w1_shape, s1_shape = tiled_shapes(E, 2 * I, H)
+        w2_shape, s2_shape = tiled_shapes(E, H, I)
+    else:
+        sblk = 16 if p.weight_format == WEIGHT_FORMATS["nvfp4"] else 32   # K elements per weight scale
+        w1_shape, s1_shape = (E, 2 * I, H // 2), (E, 2 * I, H // sblk)
+        w2_shape, s2_shape = (E, H, I // 2), (E, H, I // sblk)
+    _need(w1, torch.uint8, w1_shape, "w1")
+    _need(w1_scale, torch.uint8, s1_shape, "w1_scale")
+    _need(w2, torch.uint8, w2_shape, "w2")
+    _need(w2_scale, torch.uint8, s2_shape, "w2_scale")
     required = {0: ("situ_beta", "situ_linear_beta"), 1: (), 2: ("swiglu_alpha", "swiglu_beta")}[p.activation]
     params = {"situ_beta": situ_beta, "situ_linear_beta": situ_linear_beta, "swiglu_alpha": swiglu_alpha,
               "swiglu_beta": swiglu_beta, "alpha_gate": alpha_gate, "alpha_up": alpha_up, "alpha_down": alpha_down}

@@ -52,6 +52,9 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
   const int I = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
   const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
+  // weights in rows of K / 2 bytes, or fragment-tiled (MXFP4 only)
+  const bool tiled = !NV && a.tiled;
+  const int wstep = tiled ? 1024 : 64, sstep = tiled ? 64 : 4;   // bytes between K steps
   const int units = I / kFc1ColsPerWave;
   const int n_wgn = (units + 3) / 4;
   const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
@@ -77,15 +80,22 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       xrow[tt] = static_cast<const uint8_t*>(a.act) + t * xrow_bytes;
       xsrow[tt] = FP8 ? a.act_scale + t * nkb : nullptr;
     }
+    // this lane's 16 weight bytes and scale byte of each tile at K step 0
     const uint8_t* wrow[4];
     const uint8_t* srow[4];
     {
-      const int64_t ebase = (int64_t)l * (2 * I);
-      const int rows[4] = {n0 + r, n0 + 16 + r, I + n0 + r, I + n0 + 16 + r};
+      const int tiles[4] = {n0 / 16, n0 / 16 + 1, (I + n0) / 16, (I + n0) / 16 + 1};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        wrow[q] = a.w + (ebase + rows[q]) * (int64_t)(K / 2);
-        srow[q] = a.ws + (ebase + rows[q]) * (int64_t)sbr;
+        if (tiled) {
+          const int64_t t = (int64_t)l * (2 * I / 16) + tiles[q];
+          wrow[q] = a.w + t * steps * 1024 + lane * 16;
+          srow[q] = a.ws + t * steps * 64 + lane;
+        } else {
+          const int64_t row = (int64_t)l * (2 * I) + 16 * tiles[q] + r;
+          wrow[q] = a.w + row * (K / 2) + 16 * g;
+          srow[q] = a.ws + row * sbr + (NV ? 2 : 1) * g;
+        }
       }
     }
 
@@ -102,10 +112,10 @@ __global__ __launch_bounds__(kGemmThreads) void fc1_kernel(GemmArgs a) {
       uint32_t sv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        wv[q] = kin ? ld16(wrow[q] + kb * 16) : make_uint4(0, 0, 0, 0);
+        wv[q] = kin ? ld16(wrow[q] + j * wstep) : make_uint4(0, 0, 0, 0);
         // NVFP4: the two E4M3 scales of this 32-K block in one 16-bit load
-        sv[q] = NV ? (kin ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 2 * kb) : 0x3838u)
-                   : (kin ? (uint32_t)srow[q][kb] : 127u);
+        sv[q] = NV ? (kin ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 8 * j) : 0x3838u)
+                   : (kin ? (uint32_t)srow[q][j * sstep] : 127u);
       }
       if constexpr (!FP8) {
         uint4 xv[TOKT][4];
@@ -226,6 +236,8 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
   const int H = a.N, K = a.K;
   const int nkb = K / 32, steps = (nkb + 3) / 4;
   const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
+  const bool tiled = !NV && a.tiled;
+  const int wstep = tiled ? 1024 : 64, sstep = tiled ? 64 : 4;   // bytes between K steps
   const int wg_rows = 4 * kFc2RowsPerWave;
   const int n_wgn = (H + wg_rows - 1) / wg_rows;
   const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
@@ -251,13 +263,22 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
       hrow[tt] = static_cast<const uint8_t*>(a.act) + pp * hrow_bytes;
       hsrow[tt] = FP8 ? a.act_scale + pp * nkb : nullptr;
     }
+    // this lane's 16 weight bytes and scale byte of each tile at K step 0
+    // (tiles past H are clamped; their loads are skipped)
     const uint8_t* wrow[4];
     const uint8_t* srow[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t row = (int64_t)l * H + min(n0 + 16 * q + r, H - 1);
-      wrow[q] = a.w + row * (int64_t)(K / 2);
-      srow[q] = a.ws + row * (int64_t)sbr;
+      const int tile = min(n0 / 16 + q, H / 16 - 1);
+      if (tiled) {
+        const int64_t t = (int64_t)l * (H / 16) + tile;
+        wrow[q] = a.w + t * steps * 1024 + lane * 16;
+        srow[q] = a.ws + t * steps * 64 + lane;
+      } else {
+        const int64_t row = (int64_t)l * H + 16 * tile + r;
+        wrow[q] = a.w + row * (int64_t)(K / 2) + 16 * g;
+        srow[q] = a.ws + row * (int64_t)sbr + (NV ? 2 : 1) * g;
+      }
     }
 
     f32x4 acc[4][TOKT];
@@ -274,9 +295,9 @@ __global__ __launch_bounds__(kGemmThreads) void fc2_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bool ok = kin && q < ntiles;
-        wv[q] = ok ? ld16(wrow[q] + kb * 16) : make_uint4(0, 0, 0, 0);
-        sv[q] = NV ? (ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 2 * kb) : 0x3838u)
-                   : (ok ? (uint32_t)srow[q][kb] : 127u);
+        wv[q] = ok ? ld16(wrow[q] + j * wstep) : make_uint4(0, 0, 0, 0);
+        sv[q] = NV ? (ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow[q] + 8 * j) : 0x3838u)
+                   : (ok ? (uint32_t)srow[q][j * sstep] : 127u);
       }
       if constexpr (!FP8) {
         uint4 xv[TOKT][4];
@@ -403,14 +424,17 @@ __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 
 struct DecodeGeo {
   __amdgpu_buffer_rsrc_t wr, xr, xsr;
-  uint32_t w_row;          // byte offset of this lane's row of tile 0 in the expert's weights
-  uint32_t w_delta[4];     // tile q rows relative to tile 0, in weight bytes (uniform)
-  const uint8_t* s_lds;    // this unit's staged scales: [4 tiles x 16 rows][sbr]
+  uint32_t w_row;          // byte offset of this lane's 16 bytes of tile 0 at K step 0 in the expert's weights
+  uint32_t w_step;         // bytes between K steps: 64 (rows of K / 2 bytes) or 1024 (fragment-tiled)
+  uint32_t w_delta[4];     // tile q relative to tile 0, in weight bytes (uniform)
+  const uint8_t* s_lds;    // this unit's staged scales: 4 tiles x 16 sbr bytes
+  uint32_t s_lane;         // this lane's scale byte of step 0 in a staged tile
+  uint32_t s_step;         // bytes between K steps there: 4 (rows of sbr bytes) or 64 (tiled)
   uint32_t x_row;          // byte offset of this lane's activation row (kOob if none)
   uint32_t xs_row;
   const uint8_t* x_lds;    // w4a16: the m-tile's activation rows staged in LDS, or null
   uint32_t x_lds_off;      // this lane's row in them (bytes)
-  int nkb, sbr, g, r, ntiles;   // sbr: NVFP4 scale bytes per weight row (2 nkb)
+  int nkb, sbr, g, r, ntiles;   // sbr: staged scale bytes per weight row (scale_row_bytes)
 };
 
 // One K step's operands for a wave: four 16-row weight tiles (16 bytes of
@@ -438,7 +462,7 @@ __device__ __forceinline__ void load_x_lds(uint4 x[4], const DecodeGeo& d, int j
 // The four weight tiles' pieces of step j (zero past K).
 __device__ __forceinline__ void load_w(uint4 w[4], const DecodeGeo& d, int j) {
   const int kb = 4 * j + d.g;
-  const uint32_t wo = kb < d.nkb ? d.w_row + (uint32_t)kb * 16u : kOob;
+  const uint32_t wo = kb < d.nkb ? d.w_row + (uint32_t)j * d.w_step : kOob;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
@@ -510,7 +534,7 @@ __device__ __forceinline__ void compute_w4a16(const uint4 w[4], const uint4 x[4]
       fp4x8_to_bf16x8_mul(w[q].z, s1, wb + 8);
       fp4x8_to_bf16x8_mul(w[q].w, s1, wb + 12);
     } else {
-      const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u);
+      const float sc = e8m0_to_f32(kin ? (uint32_t)d.s_lds[16 * q * d.sbr + d.s_lane + j * d.s_step] : 127u);
       fp4x8_to_bf16x8(w[q].x, sc, wb + 0);
       fp4x8_to_bf16x8(w[q].y, sc, wb + 4);
       fp4x8_to_bf16x8(w[q].z, sc, wb + 8);
@@ -535,7 +559,7 @@ __device__ __forceinline__ void compute_step(const Step<FP8>& b, const DecodeGeo
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t av[4] = {b.w[q].x, b.w[q].y, b.w[q].z, b.w[q].w};
-      const uint32_t sv = kin ? (uint32_t)d.s_lds[(16 * q + d.r) * d.nkb + kb] : 127u;
+      const uint32_t sv = kin ? (uint32_t)d.s_lds[16 * q * d.sbr + d.s_lane + j * d.s_step] : 127u;
       acc[q] = mfma_scale_fp4_fp8(av, xb, sv, b.xs, acc[q]);
     }
   }
@@ -675,7 +699,8 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
   const int ks = wave % KSPLIT;
   const int uw = wave / KSPLIT;
   const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
-  const int sbr = NV ? 2 * nkb : nkb;   // scale bytes per weight row
+  const bool tiled = !NV && a.tiled;
+  const int sbr = NV ? 2 * nkb : (tiled ? 4 * steps : nkb);   // staged scale bytes per weight row
   const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
   const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
   const int n_rows = FC1 ? 2 * a.N : a.N;          // weight rows per expert
@@ -696,7 +721,8 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
   const int p = p0 + r;
   const bool valid = p < p1;
 
-  // stage the scales of the workgroup's units in LDS (16-byte loads)
+  // stage the scales of the workgroup's units in LDS (16-byte loads); the
+  // scales of 16 consecutive rows are 16 sbr contiguous bytes in either layout
   {
     const size_t sexp = (size_t)n_rows * sbr;
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.ws + (size_t)l * sexp, (uint32_t)sexp);
@@ -739,10 +765,10 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
   DecodeGeo d;
   int n0 = 0, ntiles = 4;
   if (active) {
-    const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+    const size_t wexp = expert_w_bytes(tiled, n_rows, K);
     d.wr = make_rsrc(a.w + (size_t)l * wexp, (uint32_t)wexp);
     d.nkb = nkb;
-    if constexpr (NV) d.sbr = sbr;
+    d.sbr = sbr;
     d.g = g;
     d.r = r;
     uint32_t dr[4];
@@ -755,9 +781,22 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
       dr[0] = 0; dr[1] = 16; dr[2] = 32; dr[3] = 48;
     }
     d.ntiles = ntiles;
+    if (tiled) {
+      const uint32_t tile_bytes = (uint32_t)steps * 1024u;   // a 16-row tile over all of K
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
-    d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2);
+      for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] / 16u * tile_bytes;
+      d.w_row = (uint32_t)(n0 / 16) * tile_bytes + (uint32_t)lane * 16u;
+      d.w_step = 1024u;
+      d.s_lane = (uint32_t)lane;
+      d.s_step = 64u;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] * (uint32_t)(K / 2);
+      d.w_row = (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16u * (uint32_t)g;
+      d.w_step = 64u;
+      d.s_lane = (uint32_t)(r * sbr + g);
+      d.s_step = 4u;
+    }
     d.s_lds = lds + (size_t)uw * 64 * sbr;
     d.x_lds = x_in_lds ? (FUSED ? hb : x_stage) : nullptr;
     d.x_lds_off = valid ? (uint32_t)r * arow_bytes : 0u;
@@ -936,9 +975,9 @@ struct FusedArgs {
   GemmArgs fc1, fc2;
 };
 
-__host__ __device__ constexpr uint32_t fused_h_offset(int ks1, int nkb1, int nkb2) {
-  const uint32_t s1 = decode_lds_scales(4 / ks1, nkb1) + decode_lds_red(ks1);
-  const uint32_t s2 = decode_lds_scales(4, nkb2);
+__host__ __device__ constexpr uint32_t fused_h_offset(int ks1, int sbr1, int sbr2) {
+  const uint32_t s1 = decode_lds_scales(4 / ks1, sbr1) + decode_lds_red(ks1);
+  const uint32_t s2 = decode_lds_scales(4, sbr2);
   return ((s1 > s2 ? s1 : s2) + 15u) / 16u * 16u;
 }
 __host__ __device__ constexpr uint32_t fused_h_bytes(bool fp8, int I) {
@@ -949,7 +988,7 @@ template <bool FP8, int KS1, bool GEN>
 __global__ __launch_bounds__(kGemmThreads, 4) void decode_fused_kernel(FusedArgs f) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int I = f.fc1.N, H = f.fc2.N;
-  uint8_t* hb = lds + fused_h_offset(KS1, H / 32, I / 32);
+  uint8_t* hb = lds + fused_h_offset(KS1, scale_row_bytes(false, f.fc1.tiled, H), scale_row_bytes(false, f.fc2.tiled, I));
   const int units1 = I / kFc1ColsPerWave, units2 = (H + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
   const int total = ((cptr)f.fc1.mtiles)[f.fc1.E_l];
   for (int mt = blockIdx.x; mt < total; mt += gridDim.x) {
@@ -966,7 +1005,8 @@ bool fused_decode_ok(int H, int I) {
 
 template <bool FP8, int KS1, bool GEN>
 static hipError_t launch_fused_k(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
-  const uint32_t lds = fused_h_offset(KS1, f.fc1.K / 32, f.fc2.K / 32) + fused_h_bytes(FP8, f.fc1.N);
+  const uint32_t lds = fused_h_offset(KS1, scale_row_bytes(false, f.fc1.tiled, f.fc1.K),
+                                      scale_row_bytes(false, f.fc2.tiled, f.fc2.K)) + fused_h_bytes(FP8, f.fc1.N);
   const int per_cu = resident_per_cu(reinterpret_cast<const void*>(decode_fused_kernel<FP8, KS1, GEN>), kGemmThreads, lds);
   const int64_t cap = (int64_t)cus * per_cu;
   const int grid = (int)(max_mtiles < cap ? max_mtiles : cap);
@@ -995,7 +1035,7 @@ hipError_t launch_fused_decode(const GemmArgs& fc1, const GemmArgs& fc2, bool fp
 
 template <bool FP8, bool FC1, bool NV, bool GEN>
 hipError_t launch_decode_k(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
-  const int sbr = NV ? a.K / 16 : a.K / 32;   // scale bytes per weight row
+  const int sbr = scale_row_bytes(NV, a.tiled != 0, a.K);   // staged scale bytes per weight row
   switch (decode_ksplit(a.K)) {
     case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV, GEN>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
     case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV, GEN>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));

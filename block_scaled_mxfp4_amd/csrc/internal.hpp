@@ -66,6 +66,8 @@ struct GemmArgs {
   uint16_t* lora_out;         // FC1: bf16 [T*k, I] receives h by expanded index, or null
   // weights: 0 = MXFP4 (E8M0 per 32 along K), 1 = NVFP4 (E4M3 per 16; w4a16 kernels only)
   int32_t nvfp4;
+  // MXFP4 weights in the fragment-tiled layout (tiled_w_offset / tiled_s_offset)
+  int32_t tiled;
   // outputs
   void* out;                  // FC1: h bf16 [P, I] or E4M3 [P, I]; FC2: y float [P, H] or fp16 [P, H]
   uint8_t* out_scale;         // FC1 w4a8: E8M0 [P, I/32]; FC2: null (fp32 y) or y's exponents [ceil(H/64), out_rows]
@@ -142,6 +144,27 @@ enum Tactic : int32_t {
 // offered for these sizes (hidden H, intermediate I).
 bool fused_decode_ok(int H, int I);
 hipError_t launch_fused_decode(const GemmArgs& fc1, const GemmArgs& fc2, bool fp8, int max_mtiles, int cus,
+                               hipStream_t s);
+
+// The fragment-tiled MXFP4 layout (SITU_WEIGHTS_MXFP4_TILED): an expert's
+// R x K weight matrix as (R / 16) x S blocks, S = ceil(K / 128), block
+// (rt, j) = rows 16 rt .. + 15, K 128 j .. + 127.  The E2M1 block is 1024
+// bytes in MFMA lane order (lane l's 16 bytes: row 16 rt + l % 16, K block
+// 4 j + l / 16), its E8M0 block 64 bytes (byte l, the same row and block).
+__host__ __device__ constexpr int tiled_steps(int K) { return (K / 32 + 3) / 4; }
+__host__ __device__ constexpr uint64_t tiled_w_offset(int rt, int j, int S) { return ((uint64_t)rt * S + j) * 1024u; }
+__host__ __device__ constexpr uint64_t tiled_s_offset(int rt, int j, int S) { return ((uint64_t)rt * S + j) * 64u; }
+// bytes of one expert's matrix in either layout
+__host__ __device__ constexpr uint64_t expert_w_bytes(bool tiled, int R, int K) {
+  return tiled ? (uint64_t)R * tiled_steps(K) * 64u : (uint64_t)R * (uint64_t)(K / 2);
+}
+// scale bytes per weight row as the kernels stage them: MXFP4 K / 32, NVFP4
+// K / 16, tiled 4 S (a K tail's blocks are padded to whole steps)
+__host__ __device__ constexpr int scale_row_bytes(bool nv, bool tiled, int K) {
+  return nv ? K / 16 : (tiled ? 4 * tiled_steps(K) : K / 32);
+}
+
+hipError_t launch_tile_weights(const uint8_t* w, const uint8_t* ws, uint8_t* wt, uint8_t* st, int E, int R, int K,
                                hipStream_t s);
 
 // Workgroup shapes of the grouped GEMMs (4 waves of 64 lanes).

@@ -55,8 +55,9 @@ constexpr uint32_t kOobPf = kOobOff;
 
 struct PfGeo {
   v4i wr, sr, xr, xsr;
-  uint32_t a_row[4];   // byte offset of this lane's row in each of its 4 weight tiles
-  uint32_t sa_row;     // scale row offset of weight row 64*wave + lane
+  uint32_t a_row[4];   // this lane's 16 bytes of each of its 4 weight tiles at K step 0
+  uint32_t sa_row;     // this lane's scale dword at K step 0 (weight row 64*wave + lane, or tiled: 4 bytes of tile 4*wave + l/16)
+  uint32_t a_step, sa_step;   // bytes between K steps: 64 and 4 (rows), 1024 and 64 (fragment-tiled)
   uint32_t b_row[2];   // activation row of token l/8 (+8 for the second block) of the wave's tile (kOobPf: none)
   uint32_t sb_row;     // scale row offset of token l%16 (kOobPf if none)
   int g, lane;
@@ -69,7 +70,7 @@ struct PfGeo {
 constexpr int kPfDmas = 8;
 __device__ __forceinline__ void pf_issue(uint32_t st, const PfGeo& d, int j, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(d.wr, st + (4 * wave + i) * 1024, d.a_row[i] + (uint32_t)(4 * j + d.g) * 16u);
+  for (int i = 0; i < 4; ++i) dma16(d.wr, st + (4 * wave + i) * 1024, d.a_row[i] + (uint32_t)j * d.a_step);
   // activations: lane l moves 16-byte chunk (l%8) ^ (l/8) of token 8h + l/8 (h = block),
   // so each instruction reads 8 whole 128-byte K slices and a token's chunk c
   // lands in slot c ^ (token % 8) of its row
@@ -78,7 +79,7 @@ __device__ __forceinline__ void pf_issue(uint32_t st, const PfGeo& d, int j, int
   for (int h = 0; h < 2; ++h)
     dma16(d.xr, st + kStageA + wave * kTileB + h * (1024 + 128),
           d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * j + chunk);
-  dma4(d.sr, st + kStageA + kStageB + wave * 256, d.sa_row + 4u * j);
+  dma4(d.sr, st + kStageA + kStageB + wave * 256, d.sa_row + (uint32_t)j * d.sa_step);
   if (lane < 16)
     dma4(d.xsr, st + kStageA + kStageB + kStageSA + wave * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
 }
@@ -95,8 +96,11 @@ __device__ __forceinline__ void step_barrier(int after) {
 // One K step of one wave: 8 weight tiles x 2 token tiles of MFMAs.  All of
 // the step's fragment reads are issued before the first MFMA, so each MFMA
 // pair waits only for its own weight fragment while the later reads are in
-// flight (one register set per fragment: 58 VGPRs).
-__device__ __forceinline__ void pf_compute(const uint8_t* st, bool fc1, int wn, int wm, int lane, f32x4 acc[8][2]) {
+// flight (one register set per fragment: 58 VGPRs).  The weight scales sit
+// per tile in 64 bytes, this lane's at s_rd (4 r + g from rows of scale
+// dwords, 16 g + r from tiled scales).
+__device__ __forceinline__ void pf_compute(const uint8_t* st, bool fc1, int wn, int wm, int lane, uint32_t s_rd,
+                                           f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4;
   uint4 blo[2], bhi[2];
   uint32_t sb[2];
@@ -116,7 +120,7 @@ __device__ __forceinline__ void pf_compute(const uint8_t* st, bool fc1, int wn, 
     // FC1: gate tiles 4wn..4wn+3 then the matching up tiles 8+4wn..; FC2: tiles 8wn..8wn+7
     const int tile = fc1 ? (i < 4 ? 4 * wn + i : 8 + 4 * wn + (i - 4)) : 8 * wn + i;
     av[i] = *reinterpret_cast<const uint4*>(st + tile * 1024 + lane * 16);
-    sa[i] = st[kStageA + kStageB + (16 * tile + r) * 4 + g];
+    sa[i] = st[kStageA + kStageB + tile * 64 + s_rd];
   }
   uint32_t bf[2][8];
 #pragma unroll
@@ -201,19 +205,30 @@ __device__ __forceinline__ PfGeo pf_geo(const GemmArgs& a, const PfItem& x, cons
   PfGeo d;
   d.g = g;
   d.lane = lane;
-  const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+  const bool tiled = a.tiled != 0;
+  const int S = tiled_steps(K);
+  const size_t wexp = expert_w_bytes(tiled, n_rows, K);
+  const size_t sexp = (size_t)n_rows * scale_row_bytes(false, tiled, K);
   d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
-  d.sr = rsrc4(a.ws + (size_t)x.l * n_rows * nkb, (uint32_t)(n_rows * nkb));
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
   const int n0 = FC1 ? x.nt * 128 : x.nt * kPfRows;
-  // weight rows of the 4 tiles this thread loads (tiles 4*wave .. 4*wave+3)
+  // first row of the item's weight tile t (tiles past H, in FC2, read zeros)
+  auto tile_row = [&](int t) { return FC1 ? (t < 8 ? n0 + 16 * t : a.N + n0 + 16 * (t - 8)) : n0 + 16 * t; };
+  // the 4 tiles this thread loads (tiles 4*wave .. 4*wave+3)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = 4 * wave + i;
-    const int row = FC1 ? (t < 8 ? n0 + 16 * t : a.N + n0 + 16 * (t - 8)) + r : n0 + 16 * t + r;
-    d.a_row[i] = (uint32_t)row * (uint32_t)(K / 2);       // rows past H (FC2) read zeros
+    const int row0 = tile_row(4 * wave + i);
+    d.a_row[i] = tiled ? (uint32_t)(row0 / 16) * (uint32_t)S * 1024u + (uint32_t)lane * 16u
+                       : (uint32_t)(row0 + r) * (uint32_t)(K / 2) + 16u * (uint32_t)g;
   }
-  const int srow = FC1 ? (tid < 128 ? n0 + tid : a.N + n0 + tid - 128) : n0 + tid;
-  d.sa_row = (uint32_t)srow * (uint32_t)nkb;
+  if (tiled) {
+    d.sa_row = (uint32_t)(tile_row(4 * wave + (lane >> 4)) / 16) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u;
+  } else {
+    const int srow = FC1 ? (tid < 128 ? n0 + tid : a.N + n0 + tid - 128) : n0 + tid;
+    d.sa_row = (uint32_t)srow * (uint32_t)nkb;
+  }
+  d.a_step = tiled ? 1024u : 64u;
+  d.sa_step = tiled ? 64u : 4u;
   d.xr = rsrc4(a.act, 0x7fffffff);
   d.xsr = rsrc4(a.act_scale, 0x7fffffff);
   d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
@@ -402,6 +417,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
   const int chunk = (total + 7) / 8;
   const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t s_rd = a.tiled ? (uint32_t)(16 * g + r) : (uint32_t)(4 * r + g);
 
   // The ring restarts at stage 0 for every item; the next item's first
   // kPfStages - 1 stages are requested before this item's output stores, so
@@ -440,7 +456,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu
           step_barrier(min(kPfStages - 2, steps - 1 - j));
           if (j + kPfStages - 1 < steps)
             pf_issue(lds_addr_of(stg[(u + kPfStages - 1) % kPfStages]), d, j + kPfStages - 1, wave, lane);
-          pf_compute(stg[u], FC1, wn, wm, lane, acc);
+          pf_compute(stg[u], FC1, wn, wm, lane, s_rd, acc);
         }
       }
     }
@@ -481,8 +497,12 @@ constexpr int kWDmas = 10;                                  // DMAs per wave per
 
 struct PwGeo {
   v4i wr, sr, xr, xsr;
-  uint32_t a_row[2][2];  // [tile][block]: row offset of this lane's row (kOobPf: none)
-  uint32_t sa_row;       // scale row of weight row 64*(wave&3) + lane
+  uint32_t a_row[2][2];  // [tile][block]: row offset of this lane's row (kOobPf: none); tiled:
+                         // [tile][step of the stage]: offset of this lane's 16 bytes in stage 0
+  uint32_t sa_row;       // scale row of weight row 64*(wave&3) + lane; tiled: this lane's scale
+                         // dword of tile 4*(wave&3) + l/16 at K step 0
+  uint32_t sa_step;      // scale bytes between K steps: 4 (rows) or 64 (tiled)
+  int tiled;
   uint32_t b_row[2];     // activation rows of tokens 16*wave + l/8 (+8)
   uint32_t sb_row;       // scale row of token 16*wave + l%16
   int wave, lane, K;
@@ -497,26 +517,40 @@ template <bool FC1>
 __device__ __forceinline__ PwGeo pw_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
   const int K = a.K, nkb = K / 32;
   const int n_rows = FC1 ? 2 * a.N : a.N;
+  const bool tiled = a.tiled != 0;
+  const int S = tiled_steps(K);
   PwGeo d;
   d.wave = wave;
   d.lane = lane;
   d.K = K;
-  const size_t wexp = (size_t)n_rows * (size_t)(K / 2);
+  d.tiled = tiled;
+  const size_t wexp = expert_w_bytes(tiled, n_rows, K);
+  const size_t sexp = (size_t)n_rows * scale_row_bytes(false, tiled, K);
   d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
-  d.sr = rsrc4(a.ws + (size_t)x.l * n_rows * nkb, (uint32_t)(n_rows * nkb));
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
   const int n0 = FC1 ? x.nt * 128 : x.nt * kWRows;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int row = pw_wrow<FC1>(a, n0, 2 * wave + i) + 8 * h + (lane >> 3);
-      d.a_row[i][h] = (FC1 || row < a.N) ? (uint32_t)row * (uint32_t)(K / 2) : kOobPf;
+      const int row0 = pw_wrow<FC1>(a, n0, 2 * wave + i);
+      if (tiled)
+        d.a_row[i][h] = (FC1 || row0 < a.N) ? ((uint32_t)(row0 / 16) * (uint32_t)S + (uint32_t)h) * 1024u + (uint32_t)lane * 16u
+                                            : kOobPf;
+      else {
+        const int row = row0 + 8 * h + (lane >> 3);
+        d.a_row[i][h] = (FC1 || row < a.N) ? (uint32_t)row * (uint32_t)(K / 2) : kOobPf;
+      }
     }
-  {
+  if (tiled) {
+    const int row0 = pw_wrow<FC1>(a, n0, 4 * (wave & 3) + (lane >> 4));
+    d.sa_row = (FC1 || row0 < a.N) ? (uint32_t)(row0 / 16) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u : kOobPf;
+  } else {
     const int q = wave & 3, row_in = 64 * q + lane;            // weight row 0..255 of the item
     const int row = FC1 ? (row_in < 128 ? n0 + row_in : a.N + n0 + row_in - 128) : n0 + row_in;
     d.sa_row = (FC1 || row < a.N) ? (uint32_t)row * (uint32_t)nkb : kOobPf;
   }
+  d.sa_step = tiled ? 64u : 4u;
   d.xr = rsrc4(a.act, 0x7fffffff);
   d.xsr = rsrc4(a.act_scale, 0x7fffffff);
   d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
@@ -526,6 +560,8 @@ __device__ __forceinline__ PwGeo pw_geo(const GemmArgs& a, const PfItem& x, cons
 }
 
 // This wave's kWDmas DMAs of stage J (K steps 2J and 2J + 1; a step past K reads zeros).
+// Weights in rows: tile block h = rows 8h .. 8h + 7, 128 bytes (both K steps) each,
+// swizzled; fragment-tiled: block h = K step 2J + h, 1 KB in lane order.
 __device__ __forceinline__ void pw_issue(uint32_t st, const PwGeo& d, int J) {
   const int w = d.wave, l = d.lane;
   const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
@@ -535,9 +571,12 @@ __device__ __forceinline__ void pw_issue(uint32_t st, const PwGeo& d, int J) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      const bool past = d.tiled ? 2 * J + h >= steps : ka >= half_row;
+      const uint32_t off = d.tiled ? d.a_row[i][h] + 2048u * (uint32_t)J : d.a_row[i][h] + ka;
       dma16(d.wr, st + kWStA + (2 * w + i) * kWTileSw + h * (1024 + 128),
-            (d.a_row[i][h] == kOobPf || ka >= half_row) ? kOobPf : d.a_row[i][h] + ka);
+            (d.a_row[i][h] == kOobPf || past) ? kOobPf : off);
+    }
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -547,7 +586,7 @@ __device__ __forceinline__ void pw_issue(uint32_t st, const PwGeo& d, int J) {
   {
     const int s = w >> 2;
     dma4(d.sr, st + kWStSA + s * 1024 + (w & 3) * 256,
-         (d.sa_row == kOobPf || 2 * J + s >= steps) ? kOobPf : d.sa_row + 4u * (2 * J + s));
+         (d.sa_row == kOobPf || 2 * J + s >= steps) ? kOobPf : d.sa_row + d.sa_step * (uint32_t)(2 * J + s));
   }
   if (l < 32) {
     const int s = l >> 4;
@@ -602,10 +641,27 @@ __device__ __forceinline__ int pw_active_tiles(const PfItem& x, int wm) {
   return left <= 0 ? 0 : (left <= 16 ? 1 : 2);
 }
 
+// Where this lane's weight fragment of K step s (0, 1) of a stage sits in a
+// staged tile, and its scale byte in a staged tile's 64 bytes: swizzled rows,
+// or lane order (fragment-tiled weights).
+struct PwRd {
+  uint32_t a[2], s;
+};
+__device__ __forceinline__ PwRd pw_rd(bool tiled, int lane) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  PwRd d;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    d.a[s] = tiled ? (uint32_t)(s * (1024 + 128) + 16 * lane)
+                   : (uint32_t)((r >> 3) * (1024 + 128) + rr * 128 + 16 * ((4 * s + g) ^ rr));
+  d.s = tiled ? (uint32_t)(16 * g + r) : (uint32_t)(4 * r + g);
+  return d;
+}
+
 // K step s of a stage for one wave: 8 weight tiles x NTT token tiles of MFMAs.
 template <int NTT>
 __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, int wn, int wm, int lane,
-                                           f32x4 acc[8][2]) {
+                                           const PwRd& rd, f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4, rr = r & 7;
   const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
   uint4 blo[2], bhi[2];
@@ -623,8 +679,8 @@ __device__ __forceinline__ void pw_compute(const uint8_t* st, int s, bool fc1, i
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int tile = fc1 ? (i < 4 ? 4 * wn + i : 8 + 4 * wn + (i - 4)) : 8 * wn + i;
-    av[i] = *reinterpret_cast<const uint4*>(st + kWStA + tile * kWTileSw + rowoff + 16 * ((4 * s + g) ^ rr));
-    sa[i] = st[kWStSA + s * 1024 + (16 * tile + r) * 4 + g];
+    av[i] = *reinterpret_cast<const uint4*>(st + kWStA + tile * kWTileSw + rd.a[s]);
+    sa[i] = st[kWStSA + s * 1024 + tile * 64 + rd.s];
   }
   pw_mfmas<NTT>(blo, bhi, sb, av, sa, acc);
 }
@@ -745,6 +801,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
   const int chunk = (total + 7) / 8;
   const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const PwRd rd = pw_rd(a.tiled != 0, lane);
 
   // Two stages per item: stage 0 is requested before the previous item's
   // output stores (so its latency overlaps them), stage J + 1 while stage J
@@ -795,14 +852,14 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
           }
           if (J + 1 < n_st) pw_issue(lds_addr_of(u ? st0 : st1), d, J + 1);
           const uint8_t* stc = u ? st1 : st0;
-          if (ntt == 2) pw_compute<2>(stc, 0, FC1, wn, wm, lane, acc);
-          else if (ntt == 1) pw_compute<1>(stc, 0, FC1, wn, wm, lane, acc);
+          if (ntt == 2) pw_compute<2>(stc, 0, FC1, wn, wm, lane, rd, acc);
+          else if (ntt == 1) pw_compute<1>(stc, 0, FC1, wn, wm, lane, rd, acc);
           if constexpr (!FC1) {
             if (pend && J == 0 && n_st < 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
           }
           if (2 * J + 1 < steps) {
-            if (ntt == 2) pw_compute<2>(stc, 1, FC1, wn, wm, lane, acc);
-            else if (ntt == 1) pw_compute<1>(stc, 1, FC1, wn, wm, lane, acc);
+            if (ntt == 2) pw_compute<2>(stc, 1, FC1, wn, wm, lane, rd, acc);
+            else if (ntt == 1) pw_compute<1>(stc, 1, FC1, wn, wm, lane, rd, acc);
           }
         }
       }
@@ -861,7 +918,7 @@ struct PsGeo {
   v4i wr, sr, xr, xsr;
   uint32_t b_row[2];   // activation rows of tokens 16*wave + l/8 (+8)
   uint32_t sb_row;     // scale row of token 16*wave + l%16
-  int K, steps, nkb;
+  int K, steps, nkb, tiled;
 };
 
 __device__ __forceinline__ PsGeo ps_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr) {
@@ -869,9 +926,11 @@ __device__ __forceinline__ PsGeo ps_geo(const GemmArgs& a, const PfItem& x, cons
   d.K = a.K;
   d.steps = a.K / 128;
   d.nkb = a.K / 32;
-  const size_t wexp = (size_t)a.N * (size_t)(a.K / 2);
+  d.tiled = a.tiled;
+  const size_t wexp = expert_w_bytes(a.tiled != 0, a.N, a.K);
+  const size_t sexp = (size_t)a.N * scale_row_bytes(false, a.tiled != 0, a.K);
   d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
-  d.sr = rsrc4(a.ws + (size_t)x.l * a.N * d.nkb, (uint32_t)(a.N * d.nkb));
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
   d.xr = rsrc4(a.act, 0x7fffffff);
   d.xsr = rsrc4(a.act_scale, 0x7fffffff);
   d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)a.K : kOobPf;
@@ -897,28 +956,37 @@ __device__ __forceinline__ void ps_issue_act(uint8_t* lds, const PsGeo& d, int w
          d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * (uint32_t)(l >> 4));
 }
 
-// This wave's two 16-row weight tiles of n-tile rows n0.. for every K step
-// (16 rows x 64 B per request, stored in lane order), and a share of the
-// n-tile's scale dwords.
+// This wave's two 16-row weight tiles of n-tile rows n0.. for every K step,
+// stored in lane order (from rows: 16 rows x 64 B per request; fragment-tiled:
+// 1 KB contiguous), and a share of the n-tile's scales: per step 256 rows x
+// one dword (from rows) or 16 tiles x 64 bytes in lane order (tiled).
 __device__ __forceinline__ void ps_issue_w(uint8_t* wb, const PsGeo& d, int N, int n0, int w, int l) {
   const int r = l & 15, g = l >> 4;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = n0 + 16 * (2 * w + i) + r;
-    const uint32_t ar = row < N ? (uint32_t)row * (uint32_t)(d.K / 2) : kOobPf;
+    const int row0 = n0 + 16 * (2 * w + i);
+    const uint32_t ar = row0 >= N ? kOobPf
+                        : d.tiled ? (uint32_t)(row0 / 16) * (uint32_t)d.steps * 1024u + (uint32_t)l * 16u
+                                  : (uint32_t)(row0 + r) * (uint32_t)(d.K / 2) + 16u * (uint32_t)g;
+    const uint32_t astep = d.tiled ? 1024u : 64u;
 #pragma unroll
     for (int s = 0; s < kSMaxSteps; ++s)
       if (s < d.steps)
-        dma16(d.wr, lds_addr_of(wb + (16 * s + 2 * w + i) * 1024),
-              ar == kOobPf ? kOobPf : ar + (uint32_t)(4 * s + g) * 16u);
+        dma16(d.wr, lds_addr_of(wb + (16 * s + 2 * w + i) * 1024), ar == kOobPf ? kOobPf : ar + (uint32_t)s * astep);
   }
 #pragma unroll
-  for (int q = w; q < 4 * kSMaxSteps; q += 8) {   // per step four blocks of 64 rows
+  for (int q = w; q < 4 * kSMaxSteps; q += 8) {   // per step four blocks of 64 rows (4 tiles)
     const int s = q >> 2, blk = q & 3;
     if (s < d.steps) {
-      const int row = n0 + 64 * blk + l;
-      dma4(d.sr, lds_addr_of(wb + kSWScales + s * 1024 + blk * 256),
-           row < N ? (uint32_t)row * (uint32_t)d.nkb + 4u * (uint32_t)s : kOobPf);
+      uint32_t so;
+      if (d.tiled) {
+        const int row0 = n0 + 64 * blk + 16 * (l >> 4);
+        so = row0 < N ? ((uint32_t)(row0 / 16) * (uint32_t)d.steps + (uint32_t)s) * 64u + (uint32_t)(l & 15) * 4u : kOobPf;
+      } else {
+        const int row = n0 + 64 * blk + l;
+        so = row < N ? (uint32_t)row * (uint32_t)d.nkb + 4u * (uint32_t)s : kOobPf;
+      }
+      dma4(d.sr, lds_addr_of(wb + kSWScales + s * 1024 + blk * 256), so);
     }
   }
 }
@@ -927,7 +995,7 @@ __device__ __forceinline__ void ps_issue_w(uint8_t* wb, const PsGeo& d, int N, i
 // and MFMAs interleaved as in the wide kernel.
 template <int NTT>
 __device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb, int s, int wn, int wm, int lane,
-                                           f32x4 acc[8][2]) {
+                                           uint32_t s_rd, f32x4 acc[8][2]) {
   const int r = lane & 15, g = lane >> 4, rr = r & 7;
   const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
   uint4 blo[2], bhi[2];
@@ -946,7 +1014,7 @@ __device__ __forceinline__ void ps_compute(const uint8_t* lds, const uint8_t* wb
   for (int i = 0; i < 8; ++i) {
     const int tile = 8 * wn + i;
     av[i] = *reinterpret_cast<const uint4*>(wb + (16 * s + tile) * 1024 + lane * 16);
-    sa[i] = wb[kSWScales + s * 1024 + (16 * tile + r) * 4 + g];
+    sa[i] = wb[kSWScales + s * 1024 + tile * 64 + s_rd];
   }
   pw_mfmas<NTT>(blo, bhi, sb, av, sa, acc);
 }
@@ -960,6 +1028,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
   const int wn = wave & 1, wm = wave >> 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int steps = a.K / 128;
+  const uint32_t s_rd = a.tiled ? (uint32_t)(16 * (lane >> 4) + (lane & 15)) : (uint32_t)(4 * (lane & 15) + (lane >> 4));
   const int n_tiles = (a.N + kWRows - 1) / kWRows;
   const int groups = (n_tiles + kSNtPerItem - 1) / kSNtPerItem;   // work items per m-tile
   const cptr te = (cptr)a.tile_expert, tr = (cptr)a.tile_rows;
@@ -1002,8 +1071,8 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
             if (s == min(1, steps - 1)) pw_y16_store<1>(a, px, yp, wn, wm, lane);
             if (s == min(2, steps - 1)) pw_y16_store<2>(a, px, yp, wn, wm, lane);
           }
-          if (ntt == 2) ps_compute<2>(lds, wb, s, wn, wm, lane, acc);
-          else if (ntt == 1) ps_compute<1>(lds, wb, s, wn, wm, lane, acc);
+          if (ntt == 2) ps_compute<2>(lds, wb, s, wn, wm, lane, s_rd, acc);
+          else if (ntt == 1) ps_compute<1>(lds, wb, s, wn, wm, lane, s_rd, acc);
         }
       }
       lds_barrier();                    // every wave is done reading wb: it holds the y transpose now

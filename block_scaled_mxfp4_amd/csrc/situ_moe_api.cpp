@@ -123,12 +123,20 @@ situ_status validate(const situ_moe_problem* p) {
   if (p->activation != SITU_ACTIVATION_SITU && p->activation != SITU_ACTIVATION_SWIGLU &&
       p->activation != SITU_ACTIVATION_SWIGLU_BIAS)
     return fail(SITU_E_UNSUPPORTED, "activation %d", p->activation);
-  if (p->weight_format != SITU_WEIGHTS_MXFP4 && p->weight_format != SITU_WEIGHTS_NVFP4)
+  if (p->weight_format != SITU_WEIGHTS_MXFP4 && p->weight_format != SITU_WEIGHTS_NVFP4 &&
+      p->weight_format != SITU_WEIGHTS_MXFP4_TILED)
     return fail(SITU_E_UNSUPPORTED, "weight_format %d", p->weight_format);
   if (p->weight_format == SITU_WEIGHTS_NVFP4 && p->act_mode != SITU_ACT_W4A16)
     return fail(SITU_E_UNSUPPORTED, "NVFP4 weights are served with bf16 activations (w4a16) only");
   const int64_t tk = (int64_t)p->num_tokens * p->top_k;
   if (tk >= (int64_t)1 << 31) return fail(SITU_E_UNSUPPORTED, "num_tokens * top_k = %lld exceeds int32", (long long)tk);
+  // one expert's weights are addressed with 32-bit offsets from one buffer resource
+  const bool tiled = p->weight_format == SITU_WEIGHTS_MXFP4_TILED;
+  const uint64_t w1e = situ::expert_w_bytes(tiled, 2 * p->intermediate_size, p->hidden_size);
+  const uint64_t w2e = situ::expert_w_bytes(tiled, p->hidden_size, p->intermediate_size);
+  if (w1e >= (uint64_t)1 << 31 || w2e >= (uint64_t)1 << 31)
+    return fail(SITU_E_UNSUPPORTED, "one expert's weights (%llu, %llu bytes) exceed 2 GiB", (unsigned long long)w1e,
+                (unsigned long long)w2e);
   // activation rows are addressed with 32-bit offsets from one buffer resource
   if ((int64_t)p->num_tokens * p->hidden_size * 2 >= (int64_t)1 << 31)
     return fail(SITU_E_UNSUPPORTED, "hidden states of %lld bytes exceed 2 GiB",
@@ -150,7 +158,7 @@ int valid_pairs(const situ_moe_problem* p, int32_t* fc1, int32_t* fc2, int cap) 
   // the fused decode pair (both GEMMs in one launch, h kept on chip)
   const int32_t fused[2] = {w4a8 ? situ::FC1_FUSED_W4A8_M16 : situ::FC1_FUSED_W4A16_M16,
                             w4a8 ? situ::FC2_FUSED_W4A8_M16 : situ::FC2_FUSED_W4A16_M16};
-  const bool fuse = p->weight_format == SITU_WEIGHTS_MXFP4 && situ::fused_decode_ok(p->hidden_size, p->intermediate_size);
+  const bool fuse = p->weight_format != SITU_WEIGHTS_NVFP4 && situ::fused_decode_ok(p->hidden_size, p->intermediate_size);
   const int64_t TK = (int64_t)p->num_tokens * p->top_k;
   const int64_t mt128 = (TK + 127) / 128 + p->local_num_experts;
   const bool wide = w4a8 && p->hidden_size % 128 == 0 && p->intermediate_size % 128 == 0 &&
@@ -424,6 +432,7 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   g.alpha_g = t->alpha_gate;
   g.alpha_u = t->alpha_up;
   g.nvfp4 = p.weight_format == SITU_WEIGHTS_NVFP4 ? 1 : 0;
+  g.tiled = p.weight_format == SITU_WEIGHTS_MXFP4_TILED ? 1 : 0;
 
   // FC1 + SiTU
   g.act = act;
@@ -498,6 +507,22 @@ situ_status situ_moe_run_profiled(const situ_moe_plan_t* plan, const situ_moe_te
   for (int i = 0; i < 6; ++i)
     if (!hip_events[i]) return fail(SITU_E_NULL_ARG, "hip_events[%d] is NULL", i);
   return run_impl(plan, t, ws, ws_bytes, hip_stream, hip_events);
+}
+
+situ_status situ_moe_tile_weights(const uint8_t* w, const uint8_t* w_scale, int32_t experts, int32_t rows, int32_t k,
+                                  uint8_t* w_tiled, uint8_t* scale_tiled, void* hip_stream) {
+  if (experts <= 0 || rows <= 0 || rows % 16 || k <= 0 || k % 32)
+    return fail(SITU_E_BAD_SHAPE, "experts %d, rows %d (multiple of 16), k %d (multiple of 32)", experts, rows, k);
+  if (situ::expert_w_bytes(true, rows, k) >= (uint64_t)1 << 31)
+    return fail(SITU_E_BAD_SHAPE, "one expert's tiled weights exceed 2 GiB");
+  if (!w || !w_scale || !w_tiled || !scale_tiled) return fail(SITU_E_NULL_ARG, "a pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(w) % 16 || reinterpret_cast<uintptr_t>(w_tiled) % 16)
+    return fail(SITU_E_BAD_SHAPE, "w and w_tiled must be 16-byte aligned");
+  int cus = 0;
+  situ_status st = device_check(&cus);
+  if (st != SITU_OK) return st;
+  return launch_status(situ::launch_tile_weights(w, w_scale, w_tiled, scale_tiled, experts, rows, k,
+                                                 static_cast<hipStream_t>(hip_stream)), "tile weights");
 }
 
 situ_status situ_moe_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int32_t cols, uint8_t* codes,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SITU_MOE_ABI_VERSION 2
+#define SITU_MOE_ABI_VERSION 3
 
 typedef enum situ_status {
   SITU_OK = 0,
@@ -80,8 +80,11 @@ enum { SITU_OUT_F32 = 0, SITU_OUT_BF16 = 1 };
  *  SwigluBias  g * sigmoid(g * swiglu_alpha) * (u + swiglu_beta)          */
 enum { SITU_ACTIVATION_SITU = 0, SITU_ACTIVATION_SWIGLU = 1, SITU_ACTIVATION_SWIGLU_BIAS = 2 };
 /* Expert weight format: MXFP4 = E2M1 + E8M0 scale per 32 along K;
- * NVFP4 = E2M1 + E4M3 scale per 16 along K (w4a16 only). */
-enum { SITU_WEIGHTS_MXFP4 = 0, SITU_WEIGHTS_NVFP4 = 1 };
+ * NVFP4 = E2M1 + E4M3 scale per 16 along K (w4a16 only);
+ * MXFP4_TILED = the same MXFP4 values in the fragment-tiled layout made by
+ * situ_moe_tile_weights (ABI 3; see there).  The layer computes the same
+ * result bit for bit from MXFP4 and MXFP4_TILED weights. */
+enum { SITU_WEIGHTS_MXFP4 = 0, SITU_WEIGHTS_NVFP4 = 1, SITU_WEIGHTS_MXFP4_TILED = 2 };
 
 /* The runtime shape of one shard (host POD). */
 typedef struct situ_moe_problem {
@@ -143,9 +146,10 @@ typedef struct situ_moe_tensors {
   const int32_t* topk_ids;            /* (device) int32 [T, k], GLOBAL ids; any id outside the shard is skipped */
   const uint16_t* topk_weights;       /* (device) bf16 [T, k] routing weights, applied in the combine */
   const int32_t* topk_packed;         /* (device) int32 [T, k] = (bf16 weight bits << 16) | (id & 0xFFFF); topk_packed only */
-  const uint8_t* w1;                  /* (device) E2M1 [E_l, 2I, H/2]: rows [0,I) gate, [I,2I) up; low nibble = even k */
+  const uint8_t* w1;                  /* (device) E2M1 [E_l, 2I, H/2]: rows [0,I) gate, [I,2I) up; low nibble = even k
+                                         (MXFP4_TILED: situ_moe_tile_weights of it, rows = 2I, k = H) */
   const uint8_t* w1_scale;            /* (device) MXFP4: E8M0 [E_l, 2I, H/32]; NVFP4: E4M3 [E_l, 2I, H/16] */
-  const uint8_t* w2;                  /* (device) E2M1 [E_l, H, I/2] */
+  const uint8_t* w2;                  /* (device) E2M1 [E_l, H, I/2] (MXFP4_TILED: tiled with rows = H, k = I) */
   const uint8_t* w2_scale;            /* (device) MXFP4: E8M0 [E_l, H, I/32]; NVFP4: E4M3 [E_l, H, I/16] */
   const float* situ_beta;             /* (device) float [E_l]; required with SiTU, else ignored */
   const float* situ_linear_beta;      /* (device) float [E_l]; required with SiTU, else ignored */
@@ -215,6 +219,32 @@ situ_status situ_moe_run_static(const situ_moe_plan_t* plan, const situ_moe_tens
  * the workspace (offsets in the plan).  Reads only the top-k tensors. */
 situ_status situ_moe_route(const situ_moe_plan_t* plan, const situ_moe_tensors* tensors,
                            void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* MXFP4 expert weights in the fragment-tiled layout (SITU_WEIGHTS_MXFP4_TILED).
+ * Callers that cannot allocate it themselves call this once per weight
+ * tensor when the weights are loaded (the layout is this library's own: the
+ * pages leave the arrangement of expert weights to each MoE backend, "bring
+ * up Kimi K3 NVFP4 with CUTLASS and cuteDSL MegaMoE SiTU", the note on the
+ * expert loader).  The values are unchanged; only their order differs, and
+ * every GEMM kernel then reads a weight fragment as one contiguous 1 KB.
+ *
+ * Input: w E2M1 [experts, rows, k/2] and w_scale E8M0 [experts, rows, k/32]
+ * (device, row-major as in situ_moe_tensors).  With S = ceil(k / 128), each
+ * expert's matrix becomes rows/16 x S blocks, row tile rt major and K step j
+ * fastest:
+ *   w_tiled     (device) [experts, rows/16, S, 1024] bytes: byte 16*l + b of
+ *               block (rt, j) is byte b of row 16*rt + l%16, K block
+ *               4*j + l/16 (the 16 bytes row-major holds at
+ *               row*(k/2) + 16*(4*j + l/16)); zero for K blocks >= k/32
+ *   scale_tiled (device) [experts, rows/16, S, 64] bytes: byte l of block
+ *               (rt, j) is the E8M0 scale of that row and K block; 127 for K
+ *               blocks >= k/32
+ * rows a positive multiple of 16, k a positive multiple of 32, one expert's
+ * tiled matrix below 2 GiB (rows * S * 64 bytes); w, w_tiled 16-byte
+ * aligned.  The outputs must not overlap the inputs.  Asynchronous on
+ * hip_stream.  SITU_E_BAD_SHAPE / SITU_E_NULL_ARG on bad arguments. */
+situ_status situ_moe_tile_weights(const uint8_t* w, const uint8_t* w_scale, int32_t experts, int32_t rows, int32_t k,
+                                  uint8_t* w_tiled, uint8_t* scale_tiled, void* hip_stream);
 
 /* MXFP8 quantization of a bf16 matrix [rows, cols] (cols multiple of 32),
  * per row per 32 consecutive columns, by the OCP MX v1.0 rule: scale code =

@@ -32,19 +32,25 @@ def config_inputs(cfg):
 
 
 def run_layer(inp, spec, *, mode=None, out_dtype="f32", tactic=(-1, -1), prequantized=False,
-              keep=False, workspace=None, lora_out=False):
+              keep=False, workspace=None, lora_out=False, tiled=False):
     """Run the layer on the GPU; returns (out numpy, plan, workspace, device tensors).
     The activation and weight format come from spec ("activation",
     "weight_format"); lora_out=True also asks for the down-LoRA input rows
-    (device tensor d["activation_lora_input"])."""
+    (device tensor d["activation_lora_input"]); tiled=True hands the layer
+    the MXFP4 weights in the fragment-tiled layout, made from the row-major
+    ones by situ_moe_tile_weights."""
     mode = mode or spec.get("mode", "w4a16")
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
     packed = inp.get("topk_packed") is not None
+    wf = spec.get("weight_format", "mxfp4")
+    if tiled:
+        assert wf == "mxfp4"
+        wf = "mxfp4_tiled"
     prob = B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
                           local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
                           act_mode=mode, act_prequantized=prequantized, topk_packed=packed,
                           out_dtype=out_dtype, tactic=tactic, activation=spec.get("activation", "situ"),
-                          weight_format=spec.get("weight_format", "mxfp4"))
+                          weight_format=wf)
     plan = B.situ_moe_plan(prob)
     d = {}
     if prequantized:
@@ -62,6 +68,9 @@ def run_layer(inp, spec, *, mode=None, out_dtype="f32", tactic=(-1, -1), prequan
                 "swiglu_alpha", "swiglu_beta", "alpha_down"):
         if inp.get(key) is not None:
             d[key] = dev(inp[key])
+    if tiled:
+        d["w1"], d["w1_scale"] = B.situ_moe_tile_weights(d["w1"], d["w1_scale"])
+        d["w2"], d["w2_scale"] = B.situ_moe_tile_weights(d["w2"], d["w2_scale"])
     if inp.get("gate_up_lora_delta") is not None:
         d["gate_up_lora_delta"] = dev(np.asarray(inp["gate_up_lora_delta"]).reshape(T * k, 2 * I))
     if lora_out:   # filled with a pattern the layer must overwrite everywhere

@@ -30,9 +30,9 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert B.situ_moe_abi_version() == B.ABI_VERSION == 2
+    assert B.situ_moe_abi_version() == B.ABI_VERSION == 3
     info = B.situ_moe_build_info()
-    assert "gfx950" in info and "abi 2" in info
+    assert "gfx950" in info and "abi 3" in info
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -110,7 +110,9 @@ def _status(fn):
     (dict(activation=3), "SITU_E_UNSUPPORTED"),
     (dict(weight_format="nvfp4"), "SITU_OK"),
     (dict(weight_format="nvfp4", act_mode="w4a8"), "SITU_E_UNSUPPORTED"),   # NVFP4 with bf16 activations only
-    (dict(weight_format=2), "SITU_E_UNSUPPORTED"),
+    (dict(weight_format="mxfp4_tiled"), "SITU_OK"),
+    (dict(weight_format="mxfp4_tiled", act_mode="w4a8"), "SITU_OK"),
+    (dict(weight_format=3), "SITU_E_UNSUPPORTED"),
 ])
 def test_plan_validation(kw, want):
     assert _status(lambda: B.situ_moe_plan(_prob(**kw))) == want
@@ -215,3 +217,23 @@ def test_no_device_reports_device_error():
                           plan.workspace_bytes, None)
     assert st == 5, B.situ_moe_last_error()
     assert B.situ_moe_status_string(5) == "SITU_E_DEVICE"
+
+
+def test_tile_weights_argument_errors_before_any_device_work():
+    lib = B.load()
+    fake = 1 << 20   # never dereferenced: every case fails on the host first
+
+    def tile(E=2, R=32, K=256, w=fake, s=fake, wt=fake + (1 << 24), st=fake + (1 << 25)):
+        return lib.situ_moe_tile_weights(ctypes.c_void_p(w), ctypes.c_void_p(s), E, R, K, ctypes.c_void_p(wt),
+                                         ctypes.c_void_p(st), None)
+
+    assert tile(R=24) == 2                      # rows a multiple of 16
+    assert tile(K=48) == 2                      # k a multiple of 32
+    assert tile(E=0) == 2
+    assert tile(R=1 << 20, K=1 << 14) == 2      # one expert's tiled matrix beyond 2 GiB
+    assert tile(w=0) == 1
+    assert tile(st=0) == 1
+    assert tile(w=fake + 8) == 2                # 16-byte alignment
+    assert tile(wt=fake + (1 << 24) + 4) == 2
+    assert B.tiled_shapes(3, 48, 96) == ((3, 3, 1, 1024), (3, 3, 1, 64))
+    assert B.tiled_shapes(1, 6144, 3584) == ((1, 384, 28, 1024), (1, 384, 28, 64))
