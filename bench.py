@@ -186,12 +186,13 @@ def _percentiles(ms):
             "p90": round(float(np.quantile(a, 0.9)), 5)}
 
 
-def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled"):
+def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled", rows_beside=True):
     """Time one workload; returns the result fields of its line.  weights:
     "tiled" hands the layer its MXFP4 weights in the fragment-tiled layout
     (made once by situ_moe_tile_weights before timing; the same values, so
     the same output bit for bit) and times the row-major weights beside it;
-    "rows" times the row-major weights only."""
+    "rows" times the row-major weights only (rows_beside=False: tiled
+    only, so that a profiler sees one layout's launches)."""
     import torch
     import block_scaled_mxfp4_amd as B
     import synthetic as S
@@ -320,7 +321,7 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
         graph_error = f"{type(e).__name__}: {e}"
 
     rows_ms = None
-    if tiled:   # the same step from the row-major weights
+    if tiled and rows_beside:   # the same step from the row-major weights
         plan_r = B.situ_moe_plan(problem(w4a8, "mxfp4"))
         assert plan_r.workspace_bytes <= plan.workspace_bytes
         out_r = torch.empty_like(tens["out"])
@@ -620,6 +621,8 @@ def main(argv=None):
     ap.add_argument("--decode-tactic", default="-1,-1", help="FC1,FC2 tactic ids of the workload beside it")
     ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
                     help="MXFP4 weight layout handed to the layer (tiled: the row-major step is timed beside it)")
+    ap.add_argument("--no-row-major", action="store_true",
+                    help="with tiled weights, skip the row-major step (profiling runs: one layout's launches)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -652,7 +655,8 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     tac = tuple(int(v) for v in args.tactic.split(","))
     dtac = tuple(int(v) for v in args.decode_tactic.split(","))
-    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac, weights=args.weights)
+    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac, weights=args.weights,
+                   rows_beside=not args.no_row_major)
     res = {
         "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
         "value": head.pop("value"),
@@ -670,7 +674,8 @@ def main(argv=None):
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_decode and args.decode_config >= 0 and args.decode_config != args.config:
-        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac, weights=args.weights)
+        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac, weights=args.weights,
+                      rows_beside=not args.no_row_major)
         res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)
