@@ -892,6 +892,228 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// FC1 with 512 weight rows per work item, for fragment-tiled weights and an
+// intermediate size that is a multiple of 256 (the EP shards, I = 3072).  A
+// work item is 256 gate columns with their 256 up rows x 128 tokens of one
+// expert: per 128-wide K step 32 KB of E2M1 weights and 16 KB of E4M3
+// activations, 25 % fewer staged bytes per MFMA than the 256-row kernel.
+// From tiled weights each weight request is 1 KB of contiguous memory and
+// each scale request 4 tiles x 64 contiguous bytes; from rows the same
+// stages cost the address unit a cache-line lookup per row (16 per weight
+// request, 64 per scale request), and the 512-row item then ran no faster
+// than the 256-row one.  8 waves, each 64 gate + 64 up rows x 64 tokens =
+// 8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4.  Stages hold one K step
+// (52.5 KB), three in a ring, so two steps are in flight while one is
+// multiplied.  The ring restarts with every work item: its first two stages
+// are requested once every wave is past the previous item's last step
+// (before that item's epilogue), and every DMA a wave issues is waited for
+// before the stage it fills is read, so no DMA is outstanding when a
+// workgroup leaves an item or exits.  Weights land as they are stored (lane
+// l's 16 bytes at 16 l of a tile), activations in the 256-row kernel's
+// swizzled tiles.  Same MFMA operands per 16 x 16 tile and K order as the
+// 256-row kernel, so the same h bit for bit.
+namespace {
+
+constexpr int kBRows = 512, kBTok = 128, kBThreads = 512;
+constexpr int kBStA = 0;                              // 32 weight tiles of 1 KB, lane order
+constexpr int kBStB = kBStA + 32 * 1024;              // 8 token tiles (swizzled, kWTileSw each)
+constexpr int kBStSA = kBStB + 8 * kWTileSw;          // 32 weight tiles x 64 E8M0 bytes, lane order
+constexpr int kBStSB = kBStSA + kBRows * 4;           // 128 tokens x 4 bytes
+constexpr int kBStage = kBStSB + kBTok * 4;           // 53760 bytes
+constexpr int kBStages = 3;
+constexpr int kBDmas = 8;                             // DMAs per wave per stage
+static_assert(kBStages * kBStage <= 160 * 1024, "stage ring fits the LDS");
+
+struct PbGeo {
+  v4i wr, sr, xr, xsr;
+  uint32_t a_row[4];   // this lane's 16 bytes of each of the wave's 4 weight tiles at K step 0
+  uint32_t sa_row;     // this lane's scale dword at K step 0 (tile 4 wave + l/16)
+  uint32_t b_row[2];   // activation rows of tokens l/8 and 8 + l/8 of the wave's token tile (kOobPf: none)
+  uint32_t sb_row;     // scale row offset of token l%16 of the tile (kOobPf: none)
+  int wave, lane, K;
+};
+
+// Item row t (0..511) -> weight row: t < 256 gate column n0 + t, else up row I + n0 + t - 256.
+__device__ __forceinline__ int pb_wrow(const GemmArgs& a, int n0, int t) {
+  return t < 256 ? n0 + t : a.N + n0 + (t - 256);
+}
+
+__device__ __forceinline__ PbGeo pb_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
+  const int K = a.K, nkb = K / 32, S = tiled_steps(K);
+  const int n_rows = 2 * a.N;
+  PbGeo d;
+  d.wave = wave;
+  d.lane = lane;
+  d.K = K;
+  const size_t wexp = expert_w_bytes(true, n_rows, K);
+  const size_t sexp = (size_t)n_rows * scale_row_bytes(false, true, K);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
+  const int n0 = x.nt * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d.a_row[i] = (uint32_t)(pb_wrow(a, n0, 16 * (4 * wave + i)) / 16) * (uint32_t)S * 1024u + (uint32_t)lane * 16u;
+  d.sa_row = (uint32_t)(pb_wrow(a, n0, 16 * (4 * wave + (lane >> 4))) / 16) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u;
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)K : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)nkb : kOobPf;
+  return d;
+}
+
+// This wave's kBDmas DMAs of K step j into stage `st`: weight tiles 4w..4w+3
+// (1 KB each), the two 8-token halves of token tile w, the scales of weight
+// tiles 4w..4w+3 (64 bytes each) and of the tile's 16 tokens (lanes 0..15).
+__device__ __forceinline__ void pb_issue(uint32_t st, const PbGeo& d, int j) {
+  const int w = d.wave, l = d.lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(d.wr, st + kBStA + (4 * w + i) * 1024, d.a_row[i] + 1024u * (uint32_t)j);
+  const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    dma16(d.xr, st + kBStB + w * kWTileSw + h * (1024 + 128),
+          d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * j + chunk);
+  dma4(d.sr, st + kBStSA + w * 256, d.sa_row + 64u * (uint32_t)j);
+  if (l < 16) dma4(d.xsr, st + kBStSB + w * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
+}
+
+// One K step of one wave from stage `st`: weight tiles (gate 4wn..4wn+3, up
+// 16+4wn..), token tiles 4wm..4wm+NTT-1; the reads are interleaved with the
+// MFMAs so only the first ones' latency precedes them.
+template <int NTT>
+__device__ __forceinline__ void pb_compute(const uint8_t* st, int wn, int wm, int lane, f32x4 acc[8][4]) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
+  uint32_t bf[NTT][8];
+  uint32_t sb[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int tile = 4 * wm + tt;
+    const uint8_t* row = st + kBStB + tile * kWTileSw + rowoff;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ rr));
+    bf[tt][0] = lo.x; bf[tt][1] = lo.y; bf[tt][2] = lo.z; bf[tt][3] = lo.w;
+    bf[tt][4] = hi.x; bf[tt][5] = hi.y; bf[tt][6] = hi.z; bf[tt][7] = hi.w;
+    sb[tt] = st[kBStSB + (16 * tile + r) * 4 + g];
+  }
+  // weight tiles stream through a window of three register sets: tile i + 2
+  // is read while tile i's MFMAs run
+  auto a_tile = [&](int i) { return i < 4 ? 4 * wn + i : 16 + 4 * wn + (i - 4); };
+  uint4 av[3];
+  uint32_t sa[3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    av[i] = *reinterpret_cast<const uint4*>(st + kBStA + a_tile(i) * 1024 + 16 * lane);
+    sa[i] = st[kBStSA + a_tile(i) * 64 + 16 * g + r];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 2 < 8) {
+      av[(i + 2) % 3] = *reinterpret_cast<const uint4*>(st + kBStA + a_tile(i + 2) * 1024 + 16 * lane);
+      sa[(i + 2) % 3] = st[kBStSA + a_tile(i + 2) * 64 + 16 * g + r];
+    }
+    const uint32_t a4[4] = {av[i % 3].x, av[i % 3].y, av[i % 3].z, av[i % 3].w};
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i % 3], sb[tt], acc[i][tt]);
+  }
+  // token fragments and the first two weight tiles' reads, then the MFMAs of
+  // each weight tile behind the reads of the tile two ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 3 * NTT + 4, 0);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NTT, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTT, 0);
+}
+
+// Token tiles of a wave's 64 rows that hold any row of the group (0 to 4).
+__device__ __forceinline__ int pb_active_tiles(const PfItem& x, int wm) {
+  const int left = x.p1 - (x.p0 + 64 * wm);
+  return left <= 0 ? 0 : (left >= 64 ? 4 : (left + 15) / 16);
+}
+
+}  // namespace
+
+template <bool GEN>
+__global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t sg0[kBStage];
+  __shared__ __align__(16) uint8_t sg1[kBStage];
+  __shared__ __align__(16) uint8_t sg2[kBStage];
+  const int tid = threadIdx.x;
+  // the wave index made visibly uniform, so that per-wave choices (its
+  // active token tiles) are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int wn = wave & 3, wm = wave >> 2;
+  const int K = a.K, steps = K / 128;
+  const int n_tiles = a.N / 256;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_tiles;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
+  const int chunk = (total + 7) / 8;
+  const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int it = i_begin + slot;
+  PfItem cur{0, 0, 0, 0};
+  PbGeo d{};
+  if (it < i_end) {
+    cur = pw_item(a, it, n_tiles);
+    d = pb_geo(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
+    lds_barrier();
+    pb_issue(lds_addr_of(sg0), d, 0);
+    if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+  }
+  for (; it < i_end; it += per_xcd_wgs) {
+    const int it_next = it + per_xcd_wgs;
+    PfItem nxt{0, 0, 0, 0};
+    PfRows trow2{-1, -1, -1};
+    if (it_next < i_end) {
+      nxt = pw_item(a, it_next, n_tiles);
+      trow2 = pf_act_rows<true>(a, nxt, wave_u, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ntt = pb_active_tiles(cur, wm);     // uniform per wave
+    for (int j0 = 0; j0 < steps; j0 += kBStages) {
+#pragma unroll
+      for (int u = 0; u < kBStages; ++u) {
+        const int j = j0 + u;
+        if (j < steps) {
+          // step j has landed (the only DMAs this wave issued after it are
+          // step j + 1's) and every wave is done reading step j - 1
+          if (j + 1 < steps) dma_barrier<kBDmas>();
+          else dma_barrier<0>();
+          if (j + 2 < steps) pb_issue(lds_addr_of(u == 0 ? sg2 : (u == 1 ? sg0 : sg1)), d, j + 2);
+          const uint8_t* stc = u == 0 ? sg0 : (u == 1 ? sg1 : sg2);
+          if (ntt > 0) pb_compute<4>(stc, wn, wm, lane, acc);
+        }
+      }
+    }
+
+    // every wave is done with the stages: request the next item's first two
+    lds_barrier();
+    if (it_next < i_end) {
+      d = pb_geo(a, nxt, trow2, wave, lane);
+      pb_issue(lds_addr_of(sg0), d, 0);
+      if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int nh = min(2, max(0, ntt - 2 * half));   // uniform
+      if (nh > 0) pf_epilogue<true, kBTok, 256, 4, GEN>(a, cur, acc, wn, 2 * wm + half, wave, lane, nullptr, nh, 2 * half);
+    }
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // FC2 at short K (at most three 128-wide K steps, as at I = 384): a work item
 // is one 128-row m-tile x two 256-row n-tiles.  The m-tile's activations for
 // the whole of K are requested once per item and stay in LDS, and the second
@@ -1098,6 +1320,19 @@ hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipSt
       if (grid > work) grid = (work + 7) / 8 * 8;
       if (grid <= 0) return hipSuccess;
       hipLaunchKernelGGL(prefill_fc2_short_kernel, dim3((unsigned)grid), dim3(kWThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (FC1) {
+    if (a.tiled && a.N % 256 == 0) {   // 512 weight rows per item (tiled weights only)
+      const int64_t work = (int64_t)max_mtiles * (a.N / 256);
+      int64_t grid = cus;                                    // one workgroup per CU
+      if (grid > work) grid = (work + 7) / 8 * 8;
+      if (grid <= 0) return hipSuccess;
+      if (general_epilogue(a))
+        hipLaunchKernelGGL(prefill_fc1_512_kernel<true>, dim3((unsigned)grid), dim3(kBThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL(prefill_fc1_512_kernel<false>, dim3((unsigned)grid), dim3(kBThreads), 0, s, a);
       return hipGetLastError();
     }
   }
