@@ -709,7 +709,9 @@ struct YPend {
   u32x4 rows[8];     // [2 * block + k]
   uint32_t e[4];     // exponent of token r's row segment, per block
 };
-__device__ __forceinline__ void pw_y16_prepare(f32x4 acc[8][2], int lane, uint8_t* scratch, YPend& yp) {
+// TT, TT0: token tiles TT0, TT0 + 1 of an [8][TT] accumulator set.
+template <int TT = 2, int TT0 = 0>
+__device__ __forceinline__ void pw_y16_prepare(f32x4 (&acc)[8][TT], int lane, uint8_t* scratch, YPend& yp) {
   const int r = lane & 15, g = lane >> 4;
   const int t8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
@@ -720,7 +722,7 @@ __device__ __forceinline__ void pw_y16_prepare(f32x4 acc[8][2], int lane, uint8_
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[4 * half + i][tt][e]));
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[4 * half + i][TT0 + tt][e]));
       m = fmaxf(m, __shfl_xor(m, 16, kWave));       // columns past H hold zeros
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
       const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 127;   // floor(log2 m)
@@ -728,7 +730,7 @@ __device__ __forceinline__ void pw_y16_prepare(f32x4 acc[8][2], int lane, uint8_
       const float inv = __builtin_bit_cast(float, (uint32_t)(254 - E) << 23);        // 2^(127 - E)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 v = acc[4 * half + i][tt];
+        const f32x4 v = acc[4 * half + i][TT0 + tt];
         const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(v[0] * inv));
         const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(v[1] * inv));
         const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(v[2] * inv));
@@ -743,12 +745,14 @@ __device__ __forceinline__ void pw_y16_prepare(f32x4 acc[8][2], int lane, uint8_
     }
 }
 // Stores 4 PART .. 4 PART + 3 of the 12: per block, two row stores (8 tokens
-// each) and the exponent store.
-template <int PART>
-__device__ __forceinline__ void pw_y16_store(const GemmArgs& a, const PfItem& x, const YPend& yp, int wn, int wm, int lane) {
+// each) and the exponent store.  NROWS: weight rows (y columns) of a work
+// item; tok0: the first of the 32 tokens (within the m-tile) held in yp.
+template <int PART, int NROWS = kWRows>
+__device__ __forceinline__ void pw_y16_store(const GemmArgs& a, const PfItem& x, const YPend& yp, int wn, int tok0,
+                                             int lane) {
   const int r = lane & 15, g = lane >> 4;
   const int t8 = lane >> 3, c8 = lane & 7;
-  const int H = a.N, n0 = x.nt * kWRows;
+  const int H = a.N, n0 = x.nt * NROWS;
   const int nb64 = (H + 63) / 64;
   const v4i yr = rsrc4(static_cast<uint16_t*>(a.out) + (size_t)x.p0 * H, (uint32_t)(kWTok * H * 2));
   const v4i er = rsrc4(a.out_scale, (uint32_t)nb64 * (uint32_t)a.out_rows);
@@ -757,12 +761,12 @@ __device__ __forceinline__ void pw_y16_store(const GemmArgs& a, const PfItem& x,
     const int blk = j / 3, kind = j % 3, tt = blk >> 1, half = blk & 1;
     const int col0 = n0 + 128 * wn + 64 * half;
     if (kind < 2) {
-      const int pr = 32 * wm + 16 * tt + 8 * kind + t8;
+      const int pr = tok0 + 16 * tt + 8 * kind + t8;
       const int col = col0 + 8 * c8;
       const bool ok = x.p0 + pr < x.p1 && col < H;
       st16u(yr, ok ? (uint32_t)(pr * H + col) * 2u : kOobPf, yp.rows[2 * blk + kind]);
     } else {
-      const int pe = 32 * wm + 16 * tt + r;
+      const int pe = tok0 + 16 * tt + r;
       const bool oke = g == 0 && x.p0 + pe < x.p1 && col0 < H;
       st1(er, oke ? (uint32_t)(x.p0 + pe) * (uint32_t)nb64 + (uint32_t)(col0 / 64) : kOobPf, yp.e[blk]);
     }
@@ -842,12 +846,12 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
           dma_barrier<0>();                                  // stage J has landed everywhere
           if constexpr (!FC1) {
             if (pend) {
-              if (J == 0) pw_y16_store<0>(a, px, yp, wn, wm, lane);
+              if (J == 0) pw_y16_store<0>(a, px, yp, wn, 32 * wm, lane);
               else if (J == 1) {
-                if (n_st >= 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
-                else pw_y16_store<2>(a, px, yp, wn, wm, lane);
+                if (n_st >= 3) pw_y16_store<1>(a, px, yp, wn, 32 * wm, lane);
+                else pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
               }
-              else if (J == 2) pw_y16_store<2>(a, px, yp, wn, wm, lane);
+              else if (J == 2) pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
             }
           }
           if (J + 1 < n_st) pw_issue(lds_addr_of(u ? st0 : st1), d, J + 1);
@@ -855,7 +859,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
           if (ntt == 2) pw_compute<2>(stc, 0, FC1, wn, wm, lane, rd, acc);
           else if (ntt == 1) pw_compute<1>(stc, 0, FC1, wn, wm, lane, rd, acc);
           if constexpr (!FC1) {
-            if (pend && J == 0 && n_st < 3) pw_y16_store<1>(a, px, yp, wn, wm, lane);
+            if (pend && J == 0 && n_st < 3) pw_y16_store<1>(a, px, yp, wn, 32 * wm, lane);
           }
           if (2 * J + 1 < steps) {
             if (ntt == 2) pw_compute<2>(stc, 1, FC1, wn, wm, lane, rd, acc);
@@ -865,7 +869,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
       }
     }
     if constexpr (!FC1) {
-      if (pend && n_st < 2) pw_y16_store<2>(a, px, yp, wn, wm, lane);
+      if (pend && n_st < 2) pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
     }
 
     // every wave is done with the stages: request the next item's first one
@@ -882,9 +886,9 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
       px = cur;
       pend = true;
       if (it_next >= i_end) {        // the last item: nothing to hide the stores behind
-        pw_y16_store<0>(a, px, yp, wn, wm, lane);
-        pw_y16_store<1>(a, px, yp, wn, wm, lane);
-        pw_y16_store<2>(a, px, yp, wn, wm, lane);
+        pw_y16_store<0>(a, px, yp, wn, 32 * wm, lane);
+        pw_y16_store<1>(a, px, yp, wn, 32 * wm, lane);
+        pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
       }
     }
     cur = nxt;
@@ -933,14 +937,17 @@ struct PbGeo {
   int wave, lane, K;
 };
 
-// Item row t (0..511) -> weight row: t < 256 gate column n0 + t, else up row I + n0 + t - 256.
+// Item row t (0..511) -> weight row.  FC1: t < 256 gate column n0 + t, else
+// up row I + n0 + t - 256; FC2: row n0 + t (rows past H read zeros).
+template <bool FC1>
 __device__ __forceinline__ int pb_wrow(const GemmArgs& a, int n0, int t) {
-  return t < 256 ? n0 + t : a.N + n0 + (t - 256);
+  return FC1 ? (t < 256 ? n0 + t : a.N + n0 + (t - 256)) : n0 + t;
 }
 
+template <bool FC1>
 __device__ __forceinline__ PbGeo pb_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
   const int K = a.K, nkb = K / 32, S = tiled_steps(K);
-  const int n_rows = 2 * a.N;
+  const int n_rows = FC1 ? 2 * a.N : a.N;
   PbGeo d;
   d.wave = wave;
   d.lane = lane;
@@ -949,11 +956,14 @@ __device__ __forceinline__ PbGeo pb_geo(const GemmArgs& a, const PfItem& x, cons
   const size_t sexp = (size_t)n_rows * scale_row_bytes(false, true, K);
   d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
   d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
-  const int n0 = x.nt * 256;
+  const int n0 = x.nt * (FC1 ? 256 : kBRows);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    d.a_row[i] = (uint32_t)(pb_wrow(a, n0, 16 * (4 * wave + i)) / 16) * (uint32_t)S * 1024u + (uint32_t)lane * 16u;
-  d.sa_row = (uint32_t)(pb_wrow(a, n0, 16 * (4 * wave + (lane >> 4))) / 16) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u;
+  for (int i = 0; i < 4; ++i) {
+    const int row0 = pb_wrow<FC1>(a, n0, 16 * (4 * wave + i));
+    d.a_row[i] = row0 < n_rows ? (uint32_t)(row0 / 16) * (uint32_t)S * 1024u + (uint32_t)lane * 16u : kOobPf;
+  }
+  const int srow0 = pb_wrow<FC1>(a, n0, 16 * (4 * wave + (lane >> 4)));
+  d.sa_row = srow0 < n_rows ? (uint32_t)(srow0 / 16) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u : kOobPf;
   d.xr = rsrc4(a.act, 0x7fffffff);
   d.xsr = rsrc4(a.act_scale, 0x7fffffff);
   d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
@@ -968,20 +978,21 @@ __device__ __forceinline__ PbGeo pb_geo(const GemmArgs& a, const PfItem& x, cons
 __device__ __forceinline__ void pb_issue(uint32_t st, const PbGeo& d, int j) {
   const int w = d.wave, l = d.lane;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(d.wr, st + kBStA + (4 * w + i) * 1024, d.a_row[i] + 1024u * (uint32_t)j);
+  for (int i = 0; i < 4; ++i)
+    dma16(d.wr, st + kBStA + (4 * w + i) * 1024, d.a_row[i] == kOobPf ? kOobPf : d.a_row[i] + 1024u * (uint32_t)j);
   const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
     dma16(d.xr, st + kBStB + w * kWTileSw + h * (1024 + 128),
           d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * j + chunk);
-  dma4(d.sr, st + kBStSA + w * 256, d.sa_row + 64u * (uint32_t)j);
+  dma4(d.sr, st + kBStSA + w * 256, d.sa_row == kOobPf ? kOobPf : d.sa_row + 64u * (uint32_t)j);
   if (l < 16) dma4(d.xsr, st + kBStSB + w * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
 }
 
-// One K step of one wave from stage `st`: weight tiles (gate 4wn..4wn+3, up
-// 16+4wn..), token tiles 4wm..4wm+NTT-1; the reads are interleaved with the
-// MFMAs so only the first ones' latency precedes them.
-template <int NTT>
+// One K step of one wave from stage `st`: weight tiles (FC1: gate 4wn..4wn+3,
+// up 16+4wn..; FC2: 8wn..8wn+7), token tiles 4wm..4wm+NTT-1; the reads are
+// interleaved with the MFMAs so only the first ones' latency precedes them.
+template <bool FC1, int NTT>
 __device__ __forceinline__ void pb_compute(const uint8_t* st, int wn, int wm, int lane, f32x4 acc[8][4]) {
   const int r = lane & 15, g = lane >> 4, rr = r & 7;
   const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
@@ -999,7 +1010,7 @@ __device__ __forceinline__ void pb_compute(const uint8_t* st, int wn, int wm, in
   }
   // weight tiles stream through a window of three register sets: tile i + 2
   // is read while tile i's MFMAs run
-  auto a_tile = [&](int i) { return i < 4 ? 4 * wn + i : 16 + 4 * wn + (i - 4); };
+  auto a_tile = [&](int i) { return FC1 ? (i < 4 ? 4 * wn + i : 16 + 4 * wn + (i - 4)) : 8 * wn + i; };
   uint4 av[3];
   uint32_t sa[3];
 #pragma unroll
@@ -1060,7 +1071,7 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
   PbGeo d{};
   if (it < i_end) {
     cur = pw_item(a, it, n_tiles);
-    d = pb_geo(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
+    d = pb_geo<true>(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
     lds_barrier();
     pb_issue(lds_addr_of(sg0), d, 0);
     if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
@@ -1092,7 +1103,7 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
           else dma_barrier<0>();
           if (j + 2 < steps) pb_issue(lds_addr_of(u == 0 ? sg2 : (u == 1 ? sg0 : sg1)), d, j + 2);
           const uint8_t* stc = u == 0 ? sg0 : (u == 1 ? sg1 : sg2);
-          if (ntt > 0) pb_compute<4>(stc, wn, wm, lane, acc);
+          if (ntt > 0) pb_compute<true, 4>(stc, wn, wm, lane, acc);
         }
       }
     }
@@ -1100,7 +1111,7 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
     // every wave is done with the stages: request the next item's first two
     lds_barrier();
     if (it_next < i_end) {
-      d = pb_geo(a, nxt, trow2, wave, lane);
+      d = pb_geo<true>(a, nxt, trow2, wave, lane);
       pb_issue(lds_addr_of(sg0), d, 0);
       if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
     }
@@ -1108,6 +1119,98 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
     for (int half = 0; half < 2; ++half) {
       const int nh = min(2, max(0, ntt - 2 * half));   // uniform
       if (nh > 0) pf_epilogue<true, kBTok, 256, 4, GEN>(a, cur, acc, wn, 2 * wm + half, wave, lane, nullptr, nh, 2 * half);
+    }
+    cur = nxt;
+  }
+}
+
+// FC2 with 512 weight rows (y columns) per work item, for fragment-tiled
+// weights and K > 384 (the EP shards, K = I = 3072): the FC1 kernel's stages
+// and wave tiles (128 rows x 64 tokens per wave), y written fp16 with one
+// exponent per 64 columns as in the 256-row kernel.  The y tile of a wave is
+// made and stored in two 32-token halves at the item's end, through the
+// third stage buffer (free from the last step's reads, which the barrier
+// after the K loop closes, to the next item's first barrier).  Same MFMA
+// operands per 16 x 16 tile, K order and y arithmetic as the 256-row kernel,
+// so the same y bit for bit.
+__global__ __launch_bounds__(kBThreads, 1) void prefill_fc2_512_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t sg0[kBStage];
+  __shared__ __align__(16) uint8_t sg1[kBStage];
+  __shared__ __align__(16) uint8_t sg2[kBStage];
+  static_assert(8 * kWYScratch <= kBStage, "the y transpose fits a stage");
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int wn = wave & 3, wm = wave >> 2;
+  const int K = a.K, steps = K / 128;
+  const int n_tiles = (a.N + kBRows - 1) / kBRows;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_tiles;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
+  const int chunk = (total + 7) / 8;
+  const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int it = i_begin + slot;
+  PfItem cur{0, 0, 0, 0};
+  PbGeo d{};
+  if (it < i_end) {
+    cur = pw_item(a, it, n_tiles);
+    d = pb_geo<false>(a, cur, pf_act_rows<false>(a, cur, wave_u, lane), wave, lane);
+    lds_barrier();
+    pb_issue(lds_addr_of(sg0), d, 0);
+    if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+  }
+  for (; it < i_end; it += per_xcd_wgs) {
+    const int it_next = it + per_xcd_wgs;
+    PfItem nxt{0, 0, 0, 0};
+    PfRows trow2{-1, -1, -1};
+    if (it_next < i_end) {
+      nxt = pw_item(a, it_next, n_tiles);
+      trow2 = pf_act_rows<false>(a, nxt, wave_u, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ntt = pb_active_tiles(cur, wm);     // uniform per wave
+    for (int j0 = 0; j0 < steps; j0 += kBStages) {
+#pragma unroll
+      for (int u = 0; u < kBStages; ++u) {
+        const int j = j0 + u;
+        if (j < steps) {
+          if (j + 1 < steps) dma_barrier<kBDmas>();
+          else dma_barrier<0>();
+          if (j + 2 < steps) pb_issue(lds_addr_of(u == 0 ? sg2 : (u == 1 ? sg0 : sg1)), d, j + 2);
+          const uint8_t* stc = u == 0 ? sg0 : (u == 1 ? sg1 : sg2);
+          if (ntt > 0) pb_compute<false, 4>(stc, wn, wm, lane, acc);
+        }
+      }
+    }
+
+    // every wave is done with the stages: request the next item's first two
+    // (into sg0 and sg1; sg2 holds the y transposes until the next barrier)
+    lds_barrier();
+    if (it_next < i_end) {
+      d = pb_geo<false>(a, nxt, trow2, wave, lane);
+      pb_issue(lds_addr_of(sg0), d, 0);
+      if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+    }
+    uint8_t* scratch = sg2 + wave * kWYScratch;
+    YPend yp;
+    if (ntt > 0) {
+      pw_y16_prepare<4, 0>(acc, lane, scratch, yp);
+      pw_y16_store<0, kBRows>(a, cur, yp, wn, 64 * wm, lane);
+      pw_y16_store<1, kBRows>(a, cur, yp, wn, 64 * wm, lane);
+      pw_y16_store<2, kBRows>(a, cur, yp, wn, 64 * wm, lane);
+    }
+    if (ntt > 2) {
+      pw_y16_prepare<4, 2>(acc, lane, scratch, yp);
+      pw_y16_store<0, kBRows>(a, cur, yp, wn, 64 * wm + 32, lane);
+      pw_y16_store<1, kBRows>(a, cur, yp, wn, 64 * wm + 32, lane);
+      pw_y16_store<2, kBRows>(a, cur, yp, wn, 64 * wm + 32, lane);
     }
     cur = nxt;
   }
@@ -1289,9 +1392,9 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
       for (int s = 0; s < kSMaxSteps; ++s) {
         if (s < steps) {
           if (pend) {                   // parts 0, 1, 2 at steps 0, 1, 2 (the last step takes the rest)
-            if (s == 0) pw_y16_store<0>(a, px, yp, wn, wm, lane);
-            if (s == min(1, steps - 1)) pw_y16_store<1>(a, px, yp, wn, wm, lane);
-            if (s == min(2, steps - 1)) pw_y16_store<2>(a, px, yp, wn, wm, lane);
+            if (s == 0) pw_y16_store<0>(a, px, yp, wn, 32 * wm, lane);
+            if (s == min(1, steps - 1)) pw_y16_store<1>(a, px, yp, wn, 32 * wm, lane);
+            if (s == min(2, steps - 1)) pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
           }
           if (ntt == 2) ps_compute<2>(lds, wb, s, wn, wm, lane, s_rd, acc);
           else if (ntt == 1) ps_compute<1>(lds, wb, s, wn, wm, lane, s_rd, acc);
@@ -1305,15 +1408,23 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
     }
   }
   if (pend) {
-    pw_y16_store<0>(a, px, yp, wn, wm, lane);
-    pw_y16_store<1>(a, px, yp, wn, wm, lane);
-    pw_y16_store<2>(a, px, yp, wn, wm, lane);
+    pw_y16_store<0>(a, px, yp, wn, 32 * wm, lane);
+    pw_y16_store<1>(a, px, yp, wn, 32 * wm, lane);
+    pw_y16_store<2>(a, px, yp, wn, 32 * wm, lane);
   }
 }
 
 template <bool FC1>
 hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
   if constexpr (!FC1) {
+    if (a.tiled && a.K % 128 == 0 && a.K > 128 * kSMaxSteps) {   // 512 y columns per item (tiled weights only)
+      const int64_t work = (int64_t)max_mtiles * ((a.N + kBRows - 1) / kBRows);
+      int64_t grid = cus;                                    // one workgroup per CU
+      if (grid > work) grid = (work + 7) / 8 * 8;
+      if (grid <= 0) return hipSuccess;
+      hipLaunchKernelGGL(prefill_fc2_512_kernel, dim3((unsigned)grid), dim3(kBThreads), 0, s, a);
+      return hipGetLastError();
+    }
     if (a.K % 128 == 0 && a.K <= 128 * kSMaxSteps) {     // the m-tile's activations fit beside two n-tiles
       const int64_t work = (int64_t)max_mtiles * ((a.N + kWRows - 1) / kWRows + kSNtPerItem - 1) / kSNtPerItem;
       int64_t grid = cus;                                    // one workgroup per CU
