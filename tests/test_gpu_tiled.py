@@ -7,7 +7,8 @@ numpy.  The kernels compute the same products and sums in the same order
 from either layout, so the layer's output from tiled weights must equal its
 output from the row-major weights bit for bit, in every tactic (the 16-row
 decode kernels, the fused decode kernel, the 64-row kernels of both
-activation modes, the 128-row wide kernel and the short-K FC2 kernel), with
+activation modes, the 128-row kernels with 256- and 512-row work items and
+the short-K FC2 kernel), with
 K tails, the general epilogue with LoRA bridges, and at full size; the
 row-major runs are the ones the layer parity tests hold to the oracle, and
 one tiled run is held to the oracle here as well.
@@ -83,8 +84,11 @@ SHAPES = {
     # kernel's last two-step stage is half empty), FC2 at K = I = 512 takes
     # the wide kernel
     "prefill": dict(T=900, H=384, I=512, E_g=6, E_l=4, off=1, k=3, seed=94, skew=True),
-    # FC2 at K = I = 384 takes the short-K kernel
+    # FC2 at K = I = 384 takes the short-K kernel, FC1 the 256-row kernel
+    # (I not a multiple of 256)
     "short": dict(T=700, H=640, I=384, E_g=6, E_l=4, off=1, k=3, seed=95, skew=True),
+    # I = 128: one 256-row FC1 n-tile per m-tile; FC2 at K = 128
+    "narrow": dict(T=300, H=256, I=128, E_g=4, E_l=4, off=0, k=2, seed=96, skew=True),
 }
 TACTICS = {"w4a16": [(0, 16), (1, 17), (5, 21)], "w4a8": [(2, 18), (3, 19), (4, 20), (6, 22)]}
 
@@ -117,10 +121,11 @@ def test_tiled_equals_row_major_bitwise(name, mode, tactic):
     assert np.array_equal(_bits(rows), _bits(tiled))
 
 
-@pytest.mark.parametrize("mode,tactic", [("w4a16", (0, 16)), ("w4a16", (1, 17)), ("w4a8", (3, 19)),
-                                         ("w4a8", (4, 20))])
-def test_tiled_general_epilogue_and_lora_bridges(mode, tactic):
-    spec = S.spec_of(dict(SHAPES["prefill"], activation="swiglu_bias", lora=True))
+@pytest.mark.parametrize("shape,mode,tactic", [("prefill", "w4a16", (0, 16)), ("prefill", "w4a16", (1, 17)),
+                                               ("prefill", "w4a8", (3, 19)), ("prefill", "w4a8", (4, 20)),
+                                               ("short", "w4a8", (4, 20))])
+def test_tiled_general_epilogue_and_lora_bridges(shape, mode, tactic):
+    spec = S.spec_of(dict(SHAPES[shape], activation="swiglu_bias", lora=True))
     inp = S.generate(spec)
     rows, _, _, dr = run_layer(inp, spec, mode=mode, tactic=tactic, lora_out=True)
     tiled, _, _, dt = run_layer(inp, spec, mode=mode, tactic=tactic, lora_out=True, tiled=True)
