@@ -468,13 +468,48 @@ __device__ __forceinline__ void load_w(uint4 w[4], const DecodeGeo& d, int j) {
     w[q] = q < d.ntiles ? bload16(d.wr, wo, d.w_delta[q]) : make_uint4(0, 0, 0, 0);   // q < ntiles: uniform
 }
 
-// w4a16: this lane's activation piece of step j from memory (zero past the
-// group or past K).
+// w4a16: the activation pieces of step j from memory (zero past the group or
+// past K).  A lane computes with K block g of its token's 256-byte step
+// (64 bytes, four 16-byte pieces), but the four lanes of a token load
+// request c together as the token's bytes 64 c .. 64 c + 63, so that each
+// request touches one 64-byte piece of a cache line per token instead of
+// four pieces spread over two lines (the address unit's cost is per line,
+// and from memory these loads were as many lookups as the weights);
+// x_transpose then gives each lane its own block.
 __device__ __forceinline__ void load_x_mem(uint4 x[4], const DecodeGeo& d, int j) {
-  const int kb = 4 * j + d.g;
-  const uint32_t xo = (kb < d.nkb && d.x_row != kOob) ? d.x_row + (uint32_t)kb * 64u : kOob;
+  const uint32_t base = d.x_row != kOob ? d.x_row + 256u * (uint32_t)j + 16u * (uint32_t)d.g : kOob;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) x[c] = bload16(d.xr, xo + 16u * c);
+  for (int c = 0; c < 4; ++c) x[c] = bload16(d.xr, (base != kOob && 4 * j + c < d.nkb) ? base + 64u * c : kOob);
+}
+
+// After load_x_mem, lane group g (lanes 16 g .. 16 g + 15) holds piece g of
+// block c in x[c]; this turns it into piece c of block g (a 4 x 4 transpose
+// between the register index and the lane group, per 32-bit word): swap the
+// upper half of x[0] (x[1]) with the lower half of x[2] (x[3]), then the odd
+// lane groups of x[0] (x[2]) with the even ones of x[1] (x[3]).
+__device__ __forceinline__ void x_transpose(uint4 x[4]) {
+  uint32_t w[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w[c][0] = x[c].x; w[c][1] = x[c].y; w[c][2] = x[c].z; w[c][3] = x[c].w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const auto s32 = __builtin_amdgcn_permlane32_swap(w[c][e], w[c + 2][e], false, false);
+      w[c][e] = s32[0];
+      w[c + 2][e] = s32[1];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(w[c][e], w[c + 1][e], false, false);
+      w[c][e] = s16[0];
+      w[c + 1][e] = s16[1];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x[c] = make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]);
 }
 
 // Step j's weights and this lane's activation piece, both from memory.
@@ -844,6 +879,7 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
               else load_x_mem(xr[(u + 1) % 2].x, d, jstep(s + 1));
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (!x_in_lds) x_transpose(xr[u % 2].x);   // uniform
             compute_w4a16<NV>(wr[u % NW].w, xr[u % 2].x, d, jstep(s), acc);
             __builtin_amdgcn_sched_barrier(0);
           }
