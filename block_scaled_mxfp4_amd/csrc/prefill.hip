@@ -262,12 +262,13 @@ static_assert(4 * 4352 <= kStage, "FC2 transpose scratch fits one stage");
 
 // FC1: alpha, SiTU and the MXFP8 rounding of h (32 columns per block);
 // FC2: the fp32 rows of y.  acc[i][tt] holds weight tile i x token tile tt.
-// NCOL: gate columns of an FC1 work item;
-// the token tiles used are acc[.][tt0 .. tt0 + 1] of an [8][TT] accumulator set.
+// NCOL: gate columns of an FC1 work item; NG: gate tiles per wave (its up
+// tiles follow them in acc), two per 32-column MXFP8 block;
+// the token tiles used are acc[.][tt0 .. tt0 + 1] of a [2 NG][TT] accumulator set.
 // GEN: the general FC1 epilogue (every activation kind, LoRA bridges); else
 // SiTU only, with the fewest registers.
-template <bool FC1, int TOK = kPfTok, int NCOL = 128, int TT = 2, bool GEN = false>
-__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 (&acc)[8][TT], int wn, int wm,
+template <bool FC1, int TOK = kPfTok, int NCOL = 128, int TT = 2, bool GEN = false, int NG = 4>
+__device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, f32x4 (&acc)[2 * NG][TT], int wn, int wm,
                                             int wave, int lane, uint8_t* scratch, int ntt = 2, int tt0 = 0) {
   const int r = lane & 15, g = lane >> 4;
   const int n0 = FC1 ? x.nt * NCOL : x.nt * kPfRows;
@@ -289,21 +290,21 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
       // the pair's expanded index: the row of its LoRA delta and down-LoRA input
       const int64_t j = (bridges && valid) ? (int64_t)a.perm[x.p0 + pr] : 0;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {          // two 32-column MXFP8 blocks per wave
+      for (int blk = 0; blk < NG / 2; ++blk) {     // NG / 2 32-column MXFP8 blocks per wave
         // h = q * blb with q = act_q (SiTU: blb = b*lb, else 1): the block
         // maximum of |h| is blb times that of |q| (rounding is monotone), and
         // h * 2^sh is q * (blb * 2^sh) in one product, exact whenever the
         // block's scale leaves the elements that get a nonzero E4M3 code in
         // fp32's normal range (sh <= 108); other blocks (all zero, or below
         // 2^-100) take h and then 2^sh
-        const int col0 = n0 + 64 * wn + 32 * blk;   // first gate column of this block
+        const int col0 = n0 + 16 * NG * wn + 32 * blk;   // first gate column of this block
         float qv[2][4];
         float amax = 0.0f;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int i = 2 * blk + h2;
           const f32x4& gv = acc[i][tt0 + tt];
-          const f32x4& uv = acc[4 + i][tt0 + tt];
+          const f32x4& uv = acc[NG + i][tt0 + tt];
           if constexpr (GEN) {
             float xg[4], xu[4];
             const float ag4[4] = {gv[0], gv[1], gv[2], gv[3]};
@@ -1124,6 +1125,204 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
   }
 }
 
+// FC1 with 384 weight rows per work item, for fragment-tiled weights and an
+// intermediate size that is a multiple of 192 but not of 256 (the TP8
+// shard, I = 384: two items per m-tile where the 256-row kernel takes three):
+// 192 gate columns with their 192 up rows x 128 tokens of one expert, per
+// 128-wide K step 24 KB of weights and 16 KB of activations, 17 % fewer
+// staged bytes per MFMA than the 256-row item.  8 waves, each 96 gate + 96
+// up rows x 32 tokens = 12 x 2 MFMA tiles (three 32-column MXFP8 blocks of h
+// per wave); stages of one K step (44 KB), three in a ring, the same
+// protocol as the 512-row kernel.  Same MFMA operands per 16 x 16 tile and
+// K order as the 256-row kernel, so the same h bit for bit.
+namespace {
+
+constexpr int kCTok = 128, kCThreads = 512;
+constexpr int kCStA = 0;                              // 24 weight tiles of 1 KB, lane order
+constexpr int kCStB = kCStA + 24 * 1024;              // 8 token tiles (swizzled, kWTileSw each)
+constexpr int kCStSA = kCStB + 8 * kWTileSw;          // 24 weight tiles x 64 E8M0 bytes, lane order
+constexpr int kCStSB = kCStSA + 24 * 64;              // 128 tokens x 4 bytes
+constexpr int kCStage = kCStSB + kCTok * 4;           // 45056 bytes
+constexpr int kCStages = 3;
+constexpr int kCDmas = 7;                             // DMAs per wave per stage
+static_assert(kCStages * kCStage <= 160 * 1024, "stage ring fits the LDS");
+
+struct PcGeo {
+  v4i wr, sr, xr, xsr;
+  uint32_t a_row[3];   // this lane's 16 bytes of each of the wave's 3 weight tiles at K step 0
+  uint32_t sa_row;     // lanes 0..47: this lane's scale dword at K step 0 (tile 3 wave + l/16)
+  uint32_t b_row[2];   // activation rows of tokens l/8 and 8 + l/8 of the wave's token tile (kOobPf: none)
+  uint32_t sb_row;     // scale row offset of token l%16 of the tile (kOobPf: none)
+  int wave, lane;
+};
+
+// Item tile t (0..23) -> first weight row: t < 12 gate columns n0 + 16 t, else up rows I + n0 + 16 (t - 12).
+__device__ __forceinline__ int pc_wrow(const GemmArgs& a, int n0, int t) {
+  return t < 12 ? n0 + 16 * t : a.N + n0 + 16 * (t - 12);
+}
+
+__device__ __forceinline__ PcGeo pc_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
+  const int K = a.K, nkb = K / 32, S = tiled_steps(K);
+  const int n_rows = 2 * a.N;
+  PcGeo d;
+  d.wave = wave;
+  d.lane = lane;
+  const size_t wexp = expert_w_bytes(true, n_rows, K);
+  const size_t sexp = (size_t)n_rows * scale_row_bytes(false, true, K);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
+  const int n0 = x.nt * 192;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    d.a_row[i] = (uint32_t)(pc_wrow(a, n0, 3 * wave + i) / 16) * (uint32_t)S * 1024u + (uint32_t)lane * 16u;
+  d.sa_row = lane < 48 ? (uint32_t)(pc_wrow(a, n0, 3 * wave + (lane >> 4)) / 16) * (uint32_t)S * 64u +
+                             (uint32_t)(lane & 15) * 4u
+                       : kOobPf;
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)K : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)nkb : kOobPf;
+  return d;
+}
+
+// This wave's kCDmas DMAs of K step j into stage `st`: weight tiles 3w..3w+2
+// (1 KB each), the two 8-token halves of token tile w, the scales of weight
+// tiles 3w..3w+2 (64 bytes each, lanes 0..47) and of the tile's 16 tokens
+// (lanes 0..15).  The lane-masked requests write only their lanes' bytes.
+__device__ __forceinline__ void pc_issue(uint32_t st, const PcGeo& d, int j) {
+  const int w = d.wave, l = d.lane;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) dma16(d.wr, st + kCStA + (3 * w + i) * 1024, d.a_row[i] + 1024u * (uint32_t)j);
+  const uint32_t chunk = (uint32_t)(((l & 7) ^ (l >> 3)) * 16);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    dma16(d.xr, st + kCStB + w * kWTileSw + h * (1024 + 128),
+          d.b_row[h] == kOobPf ? kOobPf : d.b_row[h] + 128u * j + chunk);
+  if (l < 48) dma4(d.sr, st + kCStSA + 3 * w * 64, d.sa_row + 64u * (uint32_t)j);
+  if (l < 16) dma4(d.xsr, st + kCStSB + w * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
+}
+
+// One K step of one wave from stage `st`: weight tiles gate 6wn..6wn+5, up
+// 12+6wn.., token tiles 2wm..2wm+NTT-1; the weight tiles stream through a
+// window of three register sets, read two ahead of their MFMAs.
+template <int NTT>
+__device__ __forceinline__ void pc_compute(const uint8_t* st, int wn, int wm, int lane, f32x4 acc[12][2]) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  const int rowoff = (r >> 3) * (1024 + 128) + rr * 128;
+  uint32_t bf[NTT][8];
+  uint32_t sb[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int tile = 2 * wm + tt;
+    const uint8_t* row = st + kCStB + tile * kWTileSw + rowoff;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (g ^ rr));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ rr));
+    bf[tt][0] = lo.x; bf[tt][1] = lo.y; bf[tt][2] = lo.z; bf[tt][3] = lo.w;
+    bf[tt][4] = hi.x; bf[tt][5] = hi.y; bf[tt][6] = hi.z; bf[tt][7] = hi.w;
+    sb[tt] = st[kCStSB + (16 * tile + r) * 4 + g];
+  }
+  auto a_tile = [&](int i) { return i < 6 ? 6 * wn + i : 12 + 6 * wn + (i - 6); };
+  uint4 av[3];
+  uint32_t sa[3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    av[i] = *reinterpret_cast<const uint4*>(st + kCStA + a_tile(i) * 1024 + 16 * lane);
+    sa[i] = st[kCStSA + a_tile(i) * 64 + 16 * g + r];
+  }
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    if (i + 2 < 12) {
+      av[(i + 2) % 3] = *reinterpret_cast<const uint4*>(st + kCStA + a_tile(i + 2) * 1024 + 16 * lane);
+      sa[(i + 2) % 3] = st[kCStSA + a_tile(i + 2) * 64 + 16 * g + r];
+    }
+    const uint32_t a4[4] = {av[i % 3].x, av[i % 3].y, av[i % 3].z, av[i % 3].w};
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[i][tt] = mfma_scale_fp4_fp8(a4, bf[tt], sa[i % 3], sb[tt], acc[i][tt]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 3 * NTT + 4, 0);
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NTT, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTT, 0);
+}
+
+}  // namespace
+
+template <bool GEN>
+__global__ __launch_bounds__(kCThreads, 1) void prefill_fc1_384_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint8_t sg0[kCStage];
+  __shared__ __align__(16) uint8_t sg1[kCStage];
+  __shared__ __align__(16) uint8_t sg2[kCStage];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int K = a.K, steps = K / 128;
+  const int n_tiles = a.N / 192;
+  const int total = ((cptr)a.mtiles)[a.E_l] * n_tiles;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd_wgs = (gridDim.x + 7 - xcd) / 8;
+  const int chunk = (total + 7) / 8;
+  const int i_begin = xcd * chunk, i_end = min(total, i_begin + chunk);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int it = i_begin + slot;
+  PfItem cur{0, 0, 0, 0};
+  PcGeo d{};
+  if (it < i_end) {
+    cur = pw_item(a, it, n_tiles);
+    d = pc_geo(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
+    lds_barrier();
+    pc_issue(lds_addr_of(sg0), d, 0);
+    if (steps > 1) pc_issue(lds_addr_of(sg1), d, 1);
+  }
+  for (; it < i_end; it += per_xcd_wgs) {
+    const int it_next = it + per_xcd_wgs;
+    PfItem nxt{0, 0, 0, 0};
+    PfRows trow2{-1, -1, -1};
+    if (it_next < i_end) {
+      nxt = pw_item(a, it_next, n_tiles);
+      trow2 = pf_act_rows<true>(a, nxt, wave_u, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc[12][2];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ntt = pw_active_tiles(cur, wm);     // uniform per wave
+    for (int j0 = 0; j0 < steps; j0 += kCStages) {
+#pragma unroll
+      for (int u = 0; u < kCStages; ++u) {
+        const int j = j0 + u;
+        if (j < steps) {
+          // step j has landed (the only DMAs this wave issued after it are
+          // step j + 1's) and every wave is done reading step j - 1
+          if (j + 1 < steps) dma_barrier<kCDmas>();
+          else dma_barrier<0>();
+          if (j + 2 < steps) pc_issue(lds_addr_of(u == 0 ? sg2 : (u == 1 ? sg0 : sg1)), d, j + 2);
+          const uint8_t* stc = u == 0 ? sg0 : (u == 1 ? sg1 : sg2);
+          // a wave with one token tile of the group also multiplies the other
+          // (zero rows): a second instance of the step, for one tile, would
+          // double the registers the kernel needs
+          if (ntt > 0) pc_compute<2>(stc, wn, wm, lane, acc);
+        }
+      }
+    }
+
+    // every wave is done with the stages: request the next item's first two
+    lds_barrier();
+    if (it_next < i_end) {
+      d = pc_geo(a, nxt, trow2, wave, lane);
+      pc_issue(lds_addr_of(sg0), d, 0);
+      if (steps > 1) pc_issue(lds_addr_of(sg1), d, 1);
+    }
+    pf_epilogue<true, kCTok, 192, 2, GEN, 6>(a, cur, acc, wn, wm, wave, lane, nullptr, ntt);
+    cur = nxt;
+  }
+}
+
 // FC2 with 512 weight rows (y columns) per work item, for fragment-tiled
 // weights and K > 384 (the EP shards, K = I = 3072): the FC1 kernel's stages
 // and wave tiles (128 rows x 64 tokens per wave), y written fp16 with one
@@ -1435,6 +1634,17 @@ hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipSt
     }
   }
   if constexpr (FC1) {
+    if (a.tiled && a.N % 256 != 0 && a.N % 192 == 0) {   // 384 weight rows per item (tiled weights only)
+      const int64_t work = (int64_t)max_mtiles * (a.N / 192);
+      int64_t grid = cus;                                    // one workgroup per CU
+      if (grid > work) grid = (work + 7) / 8 * 8;
+      if (grid <= 0) return hipSuccess;
+      if (general_epilogue(a))
+        hipLaunchKernelGGL(prefill_fc1_384_kernel<true>, dim3((unsigned)grid), dim3(kCThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL(prefill_fc1_384_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, s, a);
+      return hipGetLastError();
+    }
     if (a.tiled && a.N % 256 == 0) {   // 512 weight rows per item (tiled weights only)
       const int64_t work = (int64_t)max_mtiles * (a.N / 256);
       int64_t grid = cus;                                    // one workgroup per CU
