@@ -1324,7 +1324,8 @@ __global__ __launch_bounds__(kCThreads, 1) void prefill_fc1_384_kernel(GemmArgs 
 }
 
 // FC2 with 512 weight rows (y columns) per work item, for fragment-tiled
-// weights and K > 384 (the EP shards, K = I = 3072): the FC1 kernel's stages
+// weights (the EP shards at K = I = 3072; at K = 384, the TP8 shard, it
+// also beats the short-K kernel: 0.745 against 0.80 ms): the FC1 kernel's stages
 // and wave tiles (128 rows x 64 tokens per wave), y written fp16 with one
 // exponent per 64 columns as in the 256-row kernel.  The y tile of a wave is
 // made and stored in two 32-token halves at the item's end, through the
@@ -1616,7 +1617,7 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_fc2_short_kernel(GemmArg
 template <bool FC1>
 hipError_t launch_prefill_wide(const GemmArgs& a, int max_mtiles, int cus, hipStream_t s) {
   if constexpr (!FC1) {
-    if (a.tiled && a.K % 128 == 0 && a.K > 128 * kSMaxSteps) {   // 512 y columns per item (tiled weights only)
+    if (a.tiled && a.K % 128 == 0) {   // 512 y columns per item (fragment-tiled weights)
       const int64_t work = (int64_t)max_mtiles * ((a.N + kBRows - 1) / kBRows);
       int64_t grid = cus;                                    // one workgroup per CU
       if (grid > work) grid = (work + 7) / 8 * 8;
