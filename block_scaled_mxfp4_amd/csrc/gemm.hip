@@ -720,10 +720,13 @@ __device__ __forceinline__ void decode_epilogue(const GemmArgs& a, const f32x4 a
 // row groups) starting at unit0 for m-tile mt.  FUSED: a pass of the fused
 // decode kernel, whose m-tile rows of h live in LDS at hb: FC1 writes them
 // there (and stages no activation rows), FC2 reads them there.
-template <bool FP8, bool FC1, int KSPLIT, bool NV, bool GEN, bool FUSED>
+// TL: the weights are fragment-tiled (a compile-time choice: runtime strides
+// cost the decode kernels a few dozen more scalar registers, spilled).
+template <bool FP8, bool FC1, int KSPLIT, bool NV, bool GEN, bool FUSED, bool TL>
 __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int mt, int unit0, uint8_t* hb) {
   static_assert(!(NV && FP8), "NVFP4 weights are served with bf16 activations");
   static_assert(!(FUSED && NV), "the fused decode kernel takes MXFP4 weights");
+  static_assert(!(NV && TL), "NVFP4 weights are row-major");
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
   // wave-uniform values are made visibly uniform (readfirstlane, scalar
   // loads of the routing tables) so buffer resources stay in SGPRs
@@ -734,7 +737,7 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
   const int ks = wave % KSPLIT;
   const int uw = wave / KSPLIT;
   const int K = a.K, nkb = K / 32, steps = (nkb + 3) / 4;
-  const bool tiled = !NV && a.tiled;
+  constexpr bool tiled = TL;
   const int sbr = NV ? 2 * nkb : (tiled ? 4 * steps : nkb);   // staged scale bytes per weight row
   const int units = FC1 ? a.N / kFc1ColsPerWave : (a.N + kFc2RowsPerWave - 1) / kFc2RowsPerWave;
   const uint32_t arow_bytes = FP8 ? (uint32_t)K : (uint32_t)K * 2u;
@@ -816,7 +819,7 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
       dr[0] = 0; dr[1] = 16; dr[2] = 32; dr[3] = 48;
     }
     d.ntiles = ntiles;
-    if (tiled) {
+    if constexpr (tiled) {
       const uint32_t tile_bytes = (uint32_t)steps * 1024u;   // a 16-row tile over all of K
 #pragma unroll
       for (int q = 0; q < 4; ++q) d.w_delta[q] = dr[q] / 16u * tile_bytes;
@@ -944,7 +947,7 @@ __device__ __forceinline__ void decode_pass(const GemmArgs& a, uint8_t* lds, int
   __syncthreads();   // staged scales and partial sums are reused by the next work item
 }
 
-template <bool FP8, bool FC1, int KSPLIT, bool NV = false, bool GEN = false>
+template <bool FP8, bool FC1, int KSPLIT, bool NV = false, bool GEN = false, bool TL = false>
 __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void decode_gemm_kernel(GemmArgs a) {
   constexpr int UNITS_PER_WG = 4 / KSPLIT;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -952,7 +955,7 @@ __global__ __launch_bounds__(kGemmThreads, decode_waves(FP8, FC1, KSPLIT)) void 
   const int n_wgn = (units + UNITS_PER_WG - 1) / UNITS_PER_WG;
   const int total = ((cptr)a.mtiles)[a.E_l] * n_wgn;
   for (int w = blockIdx.x; w < total; w += gridDim.x)
-    decode_pass<FP8, FC1, KSPLIT, NV, GEN, false>(a, lds, w / n_wgn, (w % n_wgn) * UNITS_PER_WG, nullptr);
+    decode_pass<FP8, FC1, KSPLIT, NV, GEN, false, TL>(a, lds, w / n_wgn, (w % n_wgn) * UNITS_PER_WG, nullptr);
 }
 
 // K split for the decode kernels: long K loops are shared by the four waves.
@@ -1020,7 +1023,7 @@ __host__ __device__ constexpr uint32_t fused_h_bytes(bool fp8, int I) {
   return fp8 ? 16u * (uint32_t)I + 16u * (uint32_t)(I / 32) : 32u * (uint32_t)I;
 }
 
-template <bool FP8, int KS1, bool GEN>
+template <bool FP8, int KS1, bool GEN, bool TL>
 __global__ __launch_bounds__(kGemmThreads, 4) void decode_fused_kernel(FusedArgs f) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int I = f.fc1.N, H = f.fc2.N;
@@ -1030,8 +1033,8 @@ __global__ __launch_bounds__(kGemmThreads, 4) void decode_fused_kernel(FusedArgs
   for (int mt = blockIdx.x; mt < total; mt += gridDim.x) {
     // every pass ends with a workgroup barrier: FC2 starts on complete rows
     // of h, and the next m-tile's FC1 overwrites them only after FC2
-    for (int u0 = 0; u0 < units1; u0 += 4 / KS1) decode_pass<FP8, true, KS1, false, GEN, true>(f.fc1, lds, mt, u0, hb);
-    for (int u0 = 0; u0 < units2; u0 += 4) decode_pass<FP8, false, 1, false, false, true>(f.fc2, lds, mt, u0, hb);
+    for (int u0 = 0; u0 < units1; u0 += 4 / KS1) decode_pass<FP8, true, KS1, false, GEN, true, TL>(f.fc1, lds, mt, u0, hb);
+    for (int u0 = 0; u0 < units2; u0 += 4) decode_pass<FP8, false, 1, false, false, true, TL>(f.fc2, lds, mt, u0, hb);
   }
 }
 
@@ -1039,16 +1042,21 @@ bool fused_decode_ok(int H, int I) {
   return I % kFc1ColsPerWave == 0 && I <= 768 && (I / 32 + 3) / 4 < 16 && H % 32 == 0;
 }
 
-template <bool FP8, int KS1, bool GEN>
-static hipError_t launch_fused_k(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
-  const uint32_t lds = fused_h_offset(KS1, scale_row_bytes(false, f.fc1.tiled, f.fc1.K),
-                                      scale_row_bytes(false, f.fc2.tiled, f.fc2.K)) + fused_h_bytes(FP8, f.fc1.N);
-  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(decode_fused_kernel<FP8, KS1, GEN>), kGemmThreads, lds);
+template <bool FP8, int KS1, bool GEN, bool TL>
+static hipError_t launch_fused_kt(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
+  const uint32_t lds = fused_h_offset(KS1, scale_row_bytes(false, TL, f.fc1.K),
+                                      scale_row_bytes(false, TL, f.fc2.K)) + fused_h_bytes(FP8, f.fc1.N);
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(decode_fused_kernel<FP8, KS1, GEN, TL>), kGemmThreads, lds);
   const int64_t cap = (int64_t)cus * per_cu;
   const int grid = (int)(max_mtiles < cap ? max_mtiles : cap);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_fused_kernel<FP8, KS1, GEN>), dim3(grid), dim3(kGemmThreads), lds, s, f);
+  hipLaunchKernelGGL((decode_fused_kernel<FP8, KS1, GEN, TL>), dim3(grid), dim3(kGemmThreads), lds, s, f);
   return hipGetLastError();
+}
+template <bool FP8, int KS1, bool GEN>
+static hipError_t launch_fused_k(const FusedArgs& f, int max_mtiles, int cus, hipStream_t s) {
+  return f.fc1.tiled ? launch_fused_kt<FP8, KS1, GEN, true>(f, max_mtiles, cus, s)
+                     : launch_fused_kt<FP8, KS1, GEN, false>(f, max_mtiles, cus, s);
 }
 
 template <bool FP8, bool GEN>
@@ -1069,14 +1077,21 @@ hipError_t launch_fused_decode(const GemmArgs& fc1, const GemmArgs& fc2, bool fp
   return gen ? launch_fused_g<false, true>(f, max_mtiles, cus, s) : launch_fused_g<false, false>(f, max_mtiles, cus, s);
 }
 
+template <bool FP8, bool FC1, bool NV, bool GEN, bool TL>
+hipError_t launch_decode_kt(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
+  const int sbr = scale_row_bytes(NV, TL, a.K);   // staged scale bytes per weight row
+  switch (decode_ksplit(a.K)) {
+    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV, GEN, TL>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
+    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV, GEN, TL>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));
+    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1, NV, GEN, TL>>(a, work, cus, s, decode_lds_bytes(1, sbr, decode_lds_x(FP8, FC1, 1, a.K, sbr)));
+  }
+}
 template <bool FP8, bool FC1, bool NV, bool GEN>
 hipError_t launch_decode_k(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
-  const int sbr = scale_row_bytes(NV, a.tiled != 0, a.K);   // staged scale bytes per weight row
-  switch (decode_ksplit(a.K)) {
-    case 4: return launch_persistent<decode_gemm_kernel<FP8, FC1, 4, NV, GEN>>(a, work, cus, s, decode_lds_bytes(4, sbr, decode_lds_x(FP8, FC1, 4, a.K, sbr)));
-    case 2: return launch_persistent<decode_gemm_kernel<FP8, FC1, 2, NV, GEN>>(a, work, cus, s, decode_lds_bytes(2, sbr, decode_lds_x(FP8, FC1, 2, a.K, sbr)));
-    default: return launch_persistent<decode_gemm_kernel<FP8, FC1, 1, NV, GEN>>(a, work, cus, s, decode_lds_bytes(1, sbr, decode_lds_x(FP8, FC1, 1, a.K, sbr)));
+  if constexpr (!NV) {
+    if (a.tiled) return launch_decode_kt<FP8, FC1, NV, GEN, true>(a, work, cus, s);
   }
+  return launch_decode_kt<FP8, FC1, NV, GEN, false>(a, work, cus, s);
 }
 template <bool FP8, bool FC1>
 hipError_t launch_decode(const GemmArgs& a, int64_t work, int cus, hipStream_t s) {
