@@ -498,7 +498,8 @@ def _per_kernel(rows, counter):
 
 
 STAGE_KERNELS = {"fc1": ("decode_gemm_kernel<false, true", "decode_gemm_kernel<true, true", "fc1_kernel",
-                         "prefill_wide_kernel<true", "prefill_gemm_kernel<true", "prefill_fc1_512_kernel"),
+                         "prefill_wide_kernel<true", "prefill_gemm_kernel<true", "prefill_fc1_512_kernel",
+                         "prefill_fc1_384_kernel"),
                  "fc2": ("decode_gemm_kernel<false, false", "decode_gemm_kernel<true, false", "fc2_kernel",
                          "prefill_wide_kernel<false", "prefill_gemm_kernel<false", "prefill_fc2_short_kernel",
                          "prefill_fc2_512_kernel")}
