@@ -50,6 +50,23 @@ __device__ __forceinline__ void dma4(const v4i& r, uint32_t lds_addr, uint32_t v
                ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r) : "memory", "m0");
 }
 
+// The same with a wave-uniform byte offset added in the instruction's scalar
+// offset field, so that a lane's vector offset can be shared by requests
+// that differ only by uniform amounts.  A vector offset of kOobOff keeps the
+// request past its buffer (it reads zeros) whether or not the range check
+// counts the scalar offset: the scalar offsets used are below 2^31, so the
+// sum cannot wrap.
+__device__ __forceinline__ void dma16s(const v4i& r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const v4i& r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+
 // Workgroup barrier once this wave's DMAs up to the one N instructions back
 // have landed and its LDS reads are done.
 template <int N>

@@ -908,12 +908,16 @@ __global__ __launch_bounds__(kWThreads, 1) void prefill_wide_kernel(GemmArgs a) 
 // request, 64 per scale request), and the 512-row item then ran no faster
 // than the 256-row one.  8 waves, each 64 gate + 64 up rows x 64 tokens =
 // 8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4.  Stages hold one K step
-// (52.5 KB), three in a ring, so two steps are in flight while one is
-// multiplied.  The ring restarts with every work item: its first two stages
-// are requested once every wave is past the previous item's last step
-// (before that item's epilogue), and every DMA a wave issues is waited for
-// before the stage it fills is read, so no DMA is outstanding when a
-// workgroup leaves an item or exits.  Weights land as they are stored (lane
+// (52.5 KB), three in a ring.  FC1 runs the pipelined K loop below (the
+// barrier in mid-step, the next step's fragments read behind the current
+// step's MFMAs, the stage requests spread between them); the ring restarts
+// with every work item: its first three stages are requested once every
+// wave is past the previous item's last step (before that item's epilogue),
+// every wave issues 8 requests per stage (out of range past the item's last
+// stage), each stage is certified before it is read, and the kernel waits
+// for all of its requests before it exits.  FC2 keeps the simpler loop (its
+// y transpose needs the third buffer after the last step): two stages ahead,
+// the barrier at each step's start.  Weights land as they are stored (lane
 // l's 16 bytes at 16 l of a tile), activations in the 256-row kernel's
 // swizzled tiles.  Same MFMA operands per 16 x 16 tile and K order as the
 // 256-row kernel, so the same h bit for bit.
@@ -990,6 +994,83 @@ __device__ __forceinline__ void pb_issue(uint32_t st, const PbGeo& d, int j) {
   if (l < 16) dma4(d.xsr, st + kBStSB + w * 64, d.sb_row == kOobPf ? kOobPf : d.sb_row + 4u * j);
 }
 
+// The DMAs of the pipelined FC1 loop.  A wave's four weight tiles are one
+// contiguous run of rows, so their requests share one vector offset (16 per
+// lane) and differ by a scalar offset, as do its scale requests; only the
+// token rows (routed, per lane) need vector offsets of their own.
+struct PbDma {
+  v4i wr, sr, xr, xsr;
+  uint32_t w_soff;     // the wave's first weight tile at K step 0 (uniform)
+  uint32_t tile_b;     // bytes of one 16-row tile's E2M1 over all K steps (uniform)
+  uint32_t sa_soff;    // its scale block at K step 0 (uniform)
+  uint32_t w_lane;     // 16 lane
+  uint32_t sa_lane;    // (lane / 16) row tiles + 4 (lane % 16) bytes into a scale block
+  uint32_t b_row[2];   // token rows l/8 and 8 + l/8 of the wave's token tile, plus the lane's swizzled chunk (kOobPf: none)
+  uint32_t sb_row;     // scale row of token l%16 of the tile (kOobPf: none)
+  int wave, lane;
+};
+
+__device__ __forceinline__ PbDma pb_dma_geo(const GemmArgs& a, const PfItem& x, const PfRows& tr, int wave, int lane) {
+  const int K = a.K, nkb = K / 32, S = tiled_steps(K);
+  const int n_rows = 2 * a.N;
+  PbDma d;
+  d.wave = wave;
+  d.lane = lane;
+  const size_t wexp = expert_w_bytes(true, n_rows, K);
+  const size_t sexp = (size_t)n_rows * scale_row_bytes(false, true, K);
+  d.wr = rsrc4(a.w + (size_t)x.l * wexp, (uint32_t)wexp);
+  d.sr = rsrc4(a.ws + (size_t)x.l * sexp, (uint32_t)sexp);
+  // item rows 64 w .. 64 w + 63: gate columns (w < 4) or up rows, all within the matrix
+  const int rt0 = pb_wrow<true>(a, x.nt * 256, 64 * wave) / 16;
+  d.tile_b = (uint32_t)S * 1024u;
+  d.w_soff = (uint32_t)rt0 * d.tile_b;
+  d.sa_soff = (uint32_t)rt0 * (uint32_t)S * 64u;
+  d.w_lane = (uint32_t)lane * 16u;
+  d.sa_lane = (uint32_t)(lane >> 4) * (uint32_t)S * 64u + (uint32_t)(lane & 15) * 4u;
+  d.xr = rsrc4(a.act, 0x7fffffff);
+  d.xsr = rsrc4(a.act_scale, 0x7fffffff);
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  d.b_row[0] = tr.t_a >= 0 ? (uint32_t)tr.t_a * (uint32_t)K + chunk : kOobPf;
+  d.b_row[1] = tr.t_b >= 0 ? (uint32_t)tr.t_b * (uint32_t)K + chunk : kOobPf;
+  d.sb_row = tr.t_s >= 0 ? (uint32_t)tr.t_s * (uint32_t)nkb : kOobPf;
+  return d;
+}
+
+// This wave's DMAs of K step j into the stage at LDS address st, one at a
+// time: q = 0..3 weight tiles 4w..4w+3 (1 KB each), 4 and 5 the two 8-token
+// halves of token tile w, 6 the weight tiles' scales (64 bytes each); the
+// token tile's scales (lanes 0..15) by pb_dma_xs.  Same destinations and
+// bytes as pb_issue.  With live false the requests are out of range: they
+// write zeros to the same destinations and count like the others (a stage
+// past the item's last keeps every wave's request count, so its waits, the
+// same at every step).
+template <int Q>
+__device__ __forceinline__ void pb_dma(uint32_t st, const PbDma& d, int j, bool live) {
+  const int w = d.wave;
+  if constexpr (Q < 4) {
+    dma16s(d.wr, st + kBStA + (4 * w + Q) * 1024, live ? d.w_lane : kOobPf,
+           d.w_soff + (uint32_t)Q * d.tile_b + 1024u * (uint32_t)j);
+  } else if constexpr (Q < 6) {
+    dma16s(d.xr, st + kBStB + w * kWTileSw + (Q - 4) * (1024 + 128), live ? d.b_row[Q - 4] : kOobPf,
+           128u * (uint32_t)j);
+  } else {
+    dma4s(d.sr, st + kBStSA + w * 256, live ? d.sa_lane : kOobPf, d.sa_soff + 64u * (uint32_t)j);
+  }
+}
+__device__ __forceinline__ void pb_dma_xs(uint32_t st, const PbDma& d, int j, bool live) {
+  if (d.lane < 16) dma4s(d.xsr, st + kBStSB + d.wave * 64, live ? d.sb_row : kOobPf, 4u * (uint32_t)j);
+}
+__device__ __forceinline__ void pb_dma_all(uint32_t st, const PbDma& d, int j, bool live) {
+  pb_dma<0>(st, d, j, live);
+  pb_dma<1>(st, d, j, live);
+  pb_dma<2>(st, d, j, live);
+  pb_dma<3>(st, d, j, live);
+  pb_dma<4>(st, d, j, live);
+  pb_dma<5>(st, d, j, live);
+  pb_dma<6>(st, d, j, live);
+  pb_dma_xs(st, d, j, live);
+}
+
 // One K step of one wave from stage `st`: weight tiles (FC1: gate 4wn..4wn+3,
 // up 16+4wn..; FC2: 8wn..8wn+7), token tiles 4wm..4wm+NTT-1; the reads are
 // interleaved with the MFMAs so only the first ones' latency precedes them.
@@ -1040,6 +1121,188 @@ __device__ __forceinline__ void pb_compute(const uint8_t* st, int wn, int wm, in
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTT, 0);
 }
 
+// The pipelined K loop of the 512-row FC1 kernel.  A wave keeps all 8 of its
+// weight tiles and its 4 token tiles of a K step in registers and runs the
+// step in two halves: the MFMAs of token tiles 0 and 1 with every weight
+// tile (while token tiles 2 and 3 are read), then, after the workgroup
+// barrier, those of token tiles 2 and 3, each weight tile's registers being
+// refilled with the next step's tile right after their last MFMA, and token
+// tiles 0 and 1 with the next step's at the half's start.  The barrier sits
+// where every read of stage j is done (its buffer is then free for stage
+// j + 3) and, once this wave's DMAs of stage j + 1 have landed, certifies
+// that stage for the reads that follow it.  The matrix cores so have 16
+// MFMAs a wave ready across every barrier (where a barrier at the step's
+// start left them idle until the first fragments had arrived), and two
+// stages stay in flight.  Measured on the EP8 shard: 0.77 ms without the
+// stage requests against 0.89 for the step-start barrier, 1.073 ms with
+// them against 1.092.
+struct PbTok {
+  uint32_t bf[8];
+  uint32_t sb;
+};
+struct PbW {
+  uint32_t a[4];
+  uint32_t sa;
+};
+
+// A lane's fragment offsets within a stage (fixed for the kernel): weight
+// tile 0 of its wave column and that tile's scale byte, the low and high
+// 16 bytes of its row of token tile 4 wm and that row's scale byte.  Tile
+// i of the column is then a constant offset away, and a read is one base
+// register plus an immediate.
+struct PbLane {
+  uint32_t w, sa, tlo, thi, sb;
+};
+
+template <bool FC1>
+__device__ __forceinline__ PbLane pb_lane(int wn, int wm, int lane) {
+  const int r = lane & 15, g = lane >> 4, rr = r & 7;
+  const int t0 = FC1 ? 4 * wn : 8 * wn;
+  const int row = kBStB + 4 * wm * kWTileSw + (r >> 3) * (1024 + 128) + rr * 128;
+  return PbLane{(uint32_t)(kBStA + t0 * 1024 + 16 * lane), (uint32_t)(kBStSA + t0 * 64 + 16 * g + r),
+                (uint32_t)(row + 16 * (g ^ rr)), (uint32_t)(row + 16 * ((4 + g) ^ rr)),
+                (uint32_t)(kBStSB + (64 * wm + r) * 4 + g)};
+}
+
+// Weight tile i (0..7) of a wave column, relative to its tile 0: FC1 gate
+// tiles 4wn.. then up tiles 16 + 4wn..; FC2 tiles 8wn..
+template <bool FC1>
+__device__ __forceinline__ constexpr int pb_a_rel(int i) {
+  return FC1 ? (i < 4 ? i : 12 + i) : i;
+}
+
+// token tile tt (0..3) of the wave from the stage at `st`
+__device__ __forceinline__ void pb_read_tok(const uint8_t* st, const PbLane& o, int tt, PbTok& t) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(st + o.tlo + tt * kWTileSw);
+  const uint4 hi = *reinterpret_cast<const uint4*>(st + o.thi + tt * kWTileSw);
+  t.bf[0] = lo.x; t.bf[1] = lo.y; t.bf[2] = lo.z; t.bf[3] = lo.w;
+  t.bf[4] = hi.x; t.bf[5] = hi.y; t.bf[6] = hi.z; t.bf[7] = hi.w;
+  t.sb = st[o.sb + tt * 64];
+}
+
+template <bool FC1>
+__device__ __forceinline__ void pb_read_w(const uint8_t* st, const PbLane& o, int i, PbW& w) {
+  const uint4 v = *reinterpret_cast<const uint4*>(st + o.w + pb_a_rel<FC1>(i) * 1024);
+  w.a[0] = v.x; w.a[1] = v.y; w.a[2] = v.z; w.a[3] = v.w;
+  w.sa = st[o.sa + pb_a_rel<FC1>(i) * 64];
+}
+
+__device__ __forceinline__ f32x4 pb_mfma(const PbW& w, const PbTok& t, f32x4 acc) {
+  return mfma_scale_fp4_fp8(w.a, t.bf, w.sa, t.sb, acc);
+}
+
+// The barrier in step j (a step follows): stage j + 1 has landed (the only
+// requests this wave issued after it are the 8 for stage j + 2, real or
+// past the item's end, besides, at step 0, the previous item's epilogue
+// stores, which only lengthen the wait) and every wave is done reading stage
+// j, whose buffer then takes stage j + 3.
+__device__ __forceinline__ void pb_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  dma_barrier<kBDmas>();
+}
+
+// The first half of a step: token tiles 2 and 3 read, the MFMAs of tiles 0
+// and 1 with every weight tile.
+__device__ __forceinline__ void pb_half0(const uint8_t* stc, const PbLane& o, PbTok (&tok)[4], const PbW (&w)[8],
+                                         f32x4 (&acc)[8][4]) {
+  pb_read_tok(stc, o, 2, tok[2]);
+  pb_read_tok(stc, o, 3, tok[3]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i][0] = pb_mfma(w[i], tok[0], acc[i][0]);
+    acc[i][1] = pb_mfma(w[i], tok[1], acc[i][1]);
+  }
+  // the six reads first, then the sixteen MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+}
+
+// The second half of a step that another follows: the MFMAs of token tiles
+// 2 and 3, each weight tile's registers refilled from the next stage (stn)
+// after its last MFMA, and between them this wave's DMAs 0..6 of stage
+// j + 3 (live when it exists) into st_free, one per weight tile, so that the
+// address unit takes them while the matrix cores run (issued back to back
+// they filled its queue, and a wave waiting to issue one could issue no
+// MFMA).
+template <bool FC1>
+__device__ __forceinline__ void pb_half1(const uint8_t* stn, const PbLane& o, const PbTok (&tok)[4], PbW (&w)[8],
+                                         f32x4 (&acc)[8][4], uint32_t st_free, const PbDma& d, int j3, bool live) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i][2] = pb_mfma(w[i], tok[2], acc[i][2]);
+    acc[i][3] = pb_mfma(w[i], tok[3], acc[i][3]);
+    pb_read_w<FC1>(stn, o, i, w[i]);
+    if (i == 0) pb_dma<0>(st_free, d, j3, live);
+    if (i == 1) pb_dma<1>(st_free, d, j3, live);
+    if (i == 2) pb_dma<2>(st_free, d, j3, live);
+    if (i == 3) pb_dma<3>(st_free, d, j3, live);
+    if (i == 4) pb_dma<4>(st_free, d, j3, live);
+    if (i == 5) pb_dma<5>(st_free, d, j3, live);
+    if (i == 6) pb_dma<6>(st_free, d, j3, live);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
+// The item's stages 0..2 (live where they exist), requested into stage
+// buffers 0..2 of the ring at `ring` once every wave is done with the
+// previous item's stages.
+__device__ __forceinline__ void pb_issue_first(uint32_t ring, const PbDma& d, int steps) {
+  pb_dma_all(ring, d, 0, true);
+  pb_dma_all(ring + kBStage, d, 1, steps > 1);
+  pb_dma_all(ring + 2 * kBStage, d, 2, steps > 2);
+}
+
+// The K loop of one item over the ring of three stages at `ring` (stage j
+// in buffer j mod 3).  First stage 0 is certified (the requests of stages 1
+// and 2 are newer than its own, besides the previous item's epilogue
+// stores, which only lengthen the wait) and its weight tiles and token tiles
+// 0 and 1 are read.  Every wave takes the same barriers and issues the same
+// requests, active or not.
+template <bool FC1>
+__device__ __forceinline__ void pb_k_loop(uint8_t* ring, const PbDma& d, const PbLane& o, int steps, bool active,
+                                          f32x4 (&acc)[8][4]) {
+  dma_barrier<2 * kBDmas>();
+  const uint32_t ring_addr = lds_addr_of(ring);
+  if (!active) {   // a wave with no token rows in the group: its barriers and DMAs only
+    for (int j = 0, bc = 0; j + 1 < steps; ++j, bc = bc == 2 ? 0 : bc + 1) {
+      pb_barrier();
+      pb_dma_all(ring_addr + bc * kBStage, d, j + 3, j + 3 < steps);
+    }
+    return;
+  }
+  PbTok tok[4];
+  PbW w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pb_read_w<FC1>(ring, o, i, w[i]);
+  pb_read_tok(ring, o, 0, tok[0]);
+  pb_read_tok(ring, o, 1, tok[1]);
+  int bc = 0;   // stage j's buffer
+  for (int j = 0; j + 1 < steps; ++j) {
+    const int bn = bc == 2 ? 0 : bc + 1;
+    const uint8_t* stn = ring + bn * kBStage;
+    const uint32_t st_free = ring_addr + bc * kBStage;
+    const bool live = j + 3 < steps;
+    pb_half0(ring + bc * kBStage, o, tok, w, acc);
+    pb_barrier();
+    pb_read_tok(stn, o, 0, tok[0]);
+    pb_read_tok(stn, o, 1, tok[1]);
+    pb_dma_xs(st_free, d, j + 3, live);
+    pb_half1<FC1>(stn, o, tok, w, acc, st_free, d, j + 3, live);
+    bc = bn;
+  }
+  // the last step
+  pb_half0(ring + bc * kBStage, o, tok, w, acc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i][2] = pb_mfma(w[i], tok[2], acc[i][2]);
+    acc[i][3] = pb_mfma(w[i], tok[3], acc[i][3]);
+  }
+}
+
 // Token tiles of a wave's 64 rows that hold any row of the group (0 to 4).
 __device__ __forceinline__ int pb_active_tiles(const PfItem& x, int wm) {
   const int left = x.p1 - (x.p0 + 64 * wm);
@@ -1050,9 +1313,7 @@ __device__ __forceinline__ int pb_active_tiles(const PfItem& x, int wm) {
 
 template <bool GEN>
 __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint8_t sg0[kBStage];
-  __shared__ __align__(16) uint8_t sg1[kBStage];
-  __shared__ __align__(16) uint8_t sg2[kBStage];
+  __shared__ __align__(16) uint8_t ring[kBStages * kBStage];
   const int tid = threadIdx.x;
   // the wave index made visibly uniform, so that per-wave choices (its
   // active token tiles) are scalar branches
@@ -1069,14 +1330,14 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
 
   int it = i_begin + slot;
   PfItem cur{0, 0, 0, 0};
-  PbGeo d{};
+  PbDma d{};
   if (it < i_end) {
     cur = pw_item(a, it, n_tiles);
-    d = pb_geo<true>(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
+    d = pb_dma_geo(a, cur, pf_act_rows<true>(a, cur, wave_u, lane), wave, lane);
     lds_barrier();
-    pb_issue(lds_addr_of(sg0), d, 0);
-    if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+    pb_issue_first(lds_addr_of(ring), d, steps);
   }
+  const PbLane o = pb_lane<true>(wn, wm, lane);
   for (; it < i_end; it += per_xcd_wgs) {
     const int it_next = it + per_xcd_wgs;
     PfItem nxt{0, 0, 0, 0};
@@ -1093,28 +1354,13 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ntt = pb_active_tiles(cur, wm);     // uniform per wave
-    for (int j0 = 0; j0 < steps; j0 += kBStages) {
-#pragma unroll
-      for (int u = 0; u < kBStages; ++u) {
-        const int j = j0 + u;
-        if (j < steps) {
-          // step j has landed (the only DMAs this wave issued after it are
-          // step j + 1's) and every wave is done reading step j - 1
-          if (j + 1 < steps) dma_barrier<kBDmas>();
-          else dma_barrier<0>();
-          if (j + 2 < steps) pb_issue(lds_addr_of(u == 0 ? sg2 : (u == 1 ? sg0 : sg1)), d, j + 2);
-          const uint8_t* stc = u == 0 ? sg0 : (u == 1 ? sg1 : sg2);
-          if (ntt > 0) pb_compute<true, 4>(stc, wn, wm, lane, acc);
-        }
-      }
-    }
+    pb_k_loop<true>(ring, d, o, steps, ntt > 0, acc);
 
-    // every wave is done with the stages: request the next item's first two
+    // every wave is done with the stages: request the next item's first three
     lds_barrier();
     if (it_next < i_end) {
-      d = pb_geo<true>(a, nxt, trow2, wave, lane);
-      pb_issue(lds_addr_of(sg0), d, 0);
-      if (steps > 1) pb_issue(lds_addr_of(sg1), d, 1);
+      d = pb_dma_geo(a, nxt, trow2, wave, lane);
+      pb_issue_first(lds_addr_of(ring), d, steps);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1123,6 +1369,8 @@ __global__ __launch_bounds__(kBThreads, 1) void prefill_fc1_512_kernel(GemmArgs 
     }
     cur = nxt;
   }
+  // the last item's out-of-range requests land before the workgroup leaves
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // FC1 with 384 weight rows per work item, for fragment-tiled weights and an

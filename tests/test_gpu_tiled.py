@@ -89,6 +89,12 @@ SHAPES = {
     "short": dict(T=700, H=640, I=384, E_g=6, E_l=4, off=1, k=3, seed=95, skew=True),
     # I = 128: one 256-row FC1 n-tile per m-tile; FC2 at K = 128
     "narrow": dict(T=300, H=256, I=128, E_g=4, E_l=4, off=0, k=2, seed=96, skew=True),
+    # the 512-row FC1 kernel's pipelined K loop at 1, 2 and 5 K steps (its
+    # ring of three stages: no step after the first, no stage beyond the
+    # first three, and a rotation that does not end on the ring's start)
+    "k1": dict(T=600, H=128, I=256, E_g=4, E_l=4, off=0, k=2, seed=97, skew=True),
+    "k2": dict(T=640, H=256, I=256, E_g=5, E_l=3, off=1, k=2, seed=98, skew=True),
+    "k5": dict(T=700, H=640, I=512, E_g=5, E_l=4, off=0, k=3, seed=99, skew=True),
 }
 TACTICS = {"w4a16": [(0, 16), (1, 17), (5, 21)], "w4a8": [(2, 18), (3, 19), (4, 20), (6, 22)]}
 
