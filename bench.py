@@ -21,11 +21,14 @@ value comes from K plain (eager) calls between two synchronizations.  A
 second pass times every call on its own (HIP events on the stream) for the
 median, p10 and p90; a third records six events per call at the stage
 boundaries (situ_moe_run_profiled) for each kernel's average duration on the
-stream it runs on.  For the decode workload a fourth pass writes a 512 MiB
-buffer before every call (outside the timed events) so that no weight is
-left in the 256 MiB MALL.  The step is also captured into a HIP graph and
+stream it runs on.  A fourth pass writes a 512 MiB buffer before every call
+(outside the timed events) so that nothing is left in the 256 MiB MALL
+(median, p10, p90).  The step is also captured into a HIP graph and
 replayed; its time and whether its output equals the eager one bit for bit
-are reported.
+are reported.  Each roofline also carries the achieved rate against a
+measured ceiling: the device's plain copy bandwidth (HBM-bound kernels) or
+the sustained rate of the block-scaled FP4 x FP8 MFMA (the w4a8 GEMMs),
+both measured at the start of the run.
 
 Prints one JSON line: tokens/s, ms per step, the roofline of the dominant
 kernel (algorithmic bytes or flops per launch over its average duration),
@@ -140,6 +143,46 @@ def copy_probe(mib, reps):
     _log(f"copy probe: {reps} x {mib} MiB device-to-device")
 
 
+def reference_rates(dev):
+    """Measured ceilings beside the published ones: the device's plain copy
+    bandwidth (1 GiB device-to-device, read + written bytes, best of five)
+    and the sustained rate of the block-scaled FP4 x FP8 MFMA (the library's
+    measurement aid, best of three)."""
+    import torch
+    import block_scaled_mxfp4_amd as B
+    n = 2**30 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * 2**30 / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    peak = max(B.situ_moe_measure_mfma_peak(2000) for _ in range(3))
+    return {"copy_gbs": round(best, 1), "mfma_scale_fp4_fp8_tflops": round(peak, 1)}
+
+
+def with_measured(roof, refs):
+    """A roofline dict with its achieved rate also set against the measured
+    ceiling of its kind (copy bandwidth for HBM-bound kernels, the sustained
+    block-scaled MFMA rate for the w4a8 matrix-core-bound ones)."""
+    if refs is None or roof.get("achieved") is None:
+        return roof
+    if roof["bound"] == "hbm":
+        ref, what = refs["copy_gbs"], "device-to-device copy, GB/s"
+    elif roof["bound"] == "mfma" and roof["peak"] == MFMA_PEAK_TFLOPS["mxfp8"]:
+        ref, what = refs["mfma_scale_fp4_fp8_tflops"], "v_mfma_scale_f32_16x16x128_f8f6f4 E2M1 x E4M3, TFLOP/s"
+    else:
+        return roof
+    return dict(roof, measured_peak=ref, measured_peak_kind=what, frac_of_measured_peak=round(roof["achieved"] / ref, 4))
+
+
 def _first_tokens(inp, n):
     """The same batch cut to its first n tokens (the layer is independent per
     token: each kept token's output row is unchanged)."""
@@ -150,7 +193,7 @@ def _first_tokens(inp, n):
     return sub
 
 
-def cpu_baseline(inp, spec, budget_s=15.0):
+def cpu_baseline(inp, spec, budget_s=30.0):
     """The oracle (float32 mode, as it stands) on a bounded sample: the first n
     tokens of the same batch, n chosen for about budget_s seconds of CPU work
     (w4a8: including the oracle's own MXFP8 quantization of those tokens)."""
@@ -186,7 +229,8 @@ def _percentiles(ms):
             "p90": round(float(np.quantile(a, 0.9)), 5)}
 
 
-def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled", rows_beside=True):
+def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled", rows_beside=True,
+            refs=None):
     """Time one workload; returns the result fields of its line.  weights:
     "tiled" hands the layer its MXFP4 weights in the fragment-tiled layout
     (made once by situ_moe_tile_weights before timing; the same values, so
@@ -401,7 +445,7 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
         stage_ms["fused"] = stage_ms["fc1"] + stage_ms["fc2"]
         roof = roofline("fused")
         roof["traffic"] = None
-        other = {"kernel": "none (FC1 and FC2 in one launch)", "bound": None, "achieved": None,
+        other = {"kernel": "none (FC1 and FC2 in one launch)", "bound": None, "achieved": None, "peak": None,
                  "unit": None, "frac": None, "traffic": None}
     else:
         # the dominant kernel: the GEMM that takes longer
@@ -427,8 +471,9 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
                    "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic),
                    "weights": "MXFP4, fragment-tiled once by situ_moe_tile_weights before timing" if tiled
                               else "MXFP4, row-major"},
-        "roofline": roof,
-        "roofline_other_gemm": {kk: other[kk] for kk in ("kernel", "bound", "achieved", "unit", "frac", "traffic")},
+        "roofline": with_measured(roof, refs),
+        "roofline_other_gemm": with_measured({kk: other[kk] for kk in ("kernel", "bound", "achieved", "peak", "unit",
+                                                                       "frac", "traffic")}, refs),
         "stage_ms": {kk: round(v, 5) for kk, v in stage_ms.items()},
         "layer_hbm_gbs": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
@@ -657,8 +702,10 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     tac = tuple(int(v) for v in args.tactic.split(","))
     dtac = tuple(int(v) for v in args.decode_tactic.split(","))
-    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=False, tactic=tac, weights=args.weights,
-                   rows_beside=not args.no_row_major)
+    refs = reference_rates(dev)
+    _log(f"measured ceilings: {refs}")
+    head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=True, tactic=tac,
+                   weights=args.weights, rows_beside=not args.no_row_major, refs=refs)
     res = {
         "metric": "MoE-layer tokens/s at 1 GPU + % of HBM roofline (decode) / MFMA peak (prefill)",
         "value": head.pop("value"),
@@ -673,11 +720,12 @@ def main(argv=None):
     }
     cpu = head.pop("cpu_baseline", None)
     res.update(head)
+    res["measured_ceilings"] = refs
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_decode and args.decode_config >= 0 and args.decode_config != args.config:
-        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac, weights=args.weights,
-                      rows_beside=not args.no_row_major)
+        dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac,
+                      weights=args.weights, rows_beside=not args.no_row_major, refs=refs)
         res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)

@@ -12,7 +12,8 @@ Names mirror the C entry points: situ_moe_plan, situ_moe_valid_tactics,
 situ_moe_run, situ_moe_run_profiled, situ_moe_run_static, situ_moe_route, situ_moe_quantize_mxfp8,
 situ_moe_tile_weights, situ_moe_status_string,
 situ_moe_last_error, situ_moe_build_info, situ_moe_tactic_name,
-situ_moe_abi_version.  situ_moe(...) is the keyword-only one-call form.
+situ_moe_abi_version, and the measurement aid situ_moe_measure_mfma_peak.
+situ_moe(...) is the keyword-only one-call form.
 """
 
 import ctypes
@@ -22,7 +23,8 @@ __all__ = [
     "SituMoeError", "SituMoeProblem", "SituMoePlan", "SituMoeTensors", "library_path", "load",
     "situ_moe_plan", "situ_moe_valid_tactics", "situ_moe_run", "situ_moe_run_profiled", "situ_moe_run_static",
     "situ_moe_route",
-    "situ_moe_quantize_mxfp8", "situ_moe_tile_weights", "situ_moe_status_string", "situ_moe_last_error",
+    "situ_moe_quantize_mxfp8", "situ_moe_tile_weights", "situ_moe_measure_mfma_peak", "situ_moe_status_string",
+    "situ_moe_last_error",
     "situ_moe_build_info", "situ_moe_tactic_name", "situ_moe_abi_version", "situ_moe",
     "make_problem", "make_tensors", "new_workspace", "workspace_view", "ACT_W4A16", "ACT_W4A8", "OUT_F32", "OUT_BF16",
 ]
@@ -105,6 +107,7 @@ def load():
         "situ_moe_run_static": (c_int, [P(SituMoePlan), P(SituMoeTensors), vp]),
         "situ_moe_quantize_mxfp8": (c_int, [vp, c_i64, c_int, vp, vp, vp]),
         "situ_moe_tile_weights": (c_int, [vp, vp, c_int, c_int, c_int, vp, vp, vp]),
+        "situ_moe_measure_mfma_peak": (c_int, [c_int, P(ctypes.c_double)]),
         "situ_moe_status_string": (ctypes.c_char_p, [c_int]),
         "situ_moe_last_error": (ctypes.c_char_p, []),
         "situ_moe_build_info": (ctypes.c_char_p, []),
@@ -221,6 +224,14 @@ def tiled_shapes(experts, rows, k):
     """Shapes of the fragment-tiled weights and scales of an [experts, rows, k] MXFP4 matrix."""
     steps = (k // 32 + 3) // 4
     return (experts, rows // 16, steps, 1024), (experts, rows // 16, steps, 64)
+
+
+def situ_moe_measure_mfma_peak(iters=2000):
+    """TFLOP/s the current device sustains on the block-scaled FP4 x FP8 MFMA
+    of the w4a8 GEMMs (a measurement aid; synchronous)."""
+    out = ctypes.c_double(0.0)
+    _check(load().situ_moe_measure_mfma_peak(int(iters), ctypes.byref(out)))
+    return out.value
 
 
 def situ_moe_tile_weights(w, w_scale, w_tiled=None, scale_tiled=None, stream=None):

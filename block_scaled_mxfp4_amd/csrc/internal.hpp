@@ -167,6 +167,10 @@ __host__ __device__ constexpr int scale_row_bytes(bool nv, bool tiled, int K) {
 hipError_t launch_tile_weights(const uint8_t* w, const uint8_t* ws, uint8_t* wt, uint8_t* st, int E, int R, int K,
                                hipStream_t s);
 
+// `blocks` workgroups of 4 waves, each running `iters` rounds of 8 block-scaled
+// FP4 x FP8 MFMAs on registers (the matrix-core peak measurement).
+hipError_t launch_mfma_peak(int iters, int blocks, hipStream_t s);
+
 // Workgroup shapes of the grouped GEMMs (4 waves of 64 lanes).
 constexpr int kGemmThreads = 256;
 constexpr int kFc1ColsPerWave = 32;    // gate columns per wave (with the matching up columns)

@@ -538,6 +538,34 @@ situ_status situ_moe_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int32_
   return launch_status(situ::launch_quant_mxfp8(q, static_cast<hipStream_t>(hip_stream)), "quantize");
 }
 
+situ_status situ_moe_measure_mfma_peak(int32_t iters, double* tflops) {
+  if (!tflops) return fail(SITU_E_NULL_ARG, "tflops is NULL");
+  if (iters < 1 || iters > (1 << 20)) return fail(SITU_E_BAD_SHAPE, "iters %d not in [1, 2^20]", iters);
+  int cus = 0;
+  situ_status st = device_check(&cus);
+  if (st != SITU_OK) return st;
+  const int blocks = 4 * cus;   // 16 waves per CU: 4 per SIMD
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipStreamCreate(&s);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = situ::launch_mfma_peak(iters, blocks, s);   // warm-up (clocks, code load)
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  if (e == hipSuccess) e = situ::launch_mfma_peak(iters, blocks, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (s) (void)hipStreamDestroy(s);
+  if (e != hipSuccess) return launch_status(e, "MFMA peak measurement");
+  const double flops = (double)blocks * 4.0 * (double)iters * 8.0 * 65536.0;
+  *tflops = ms > 0.f ? flops / (ms * 1e-3) / 1e12 : 0.0;
+  return SITU_OK;
+}
+
 const char* situ_moe_status_string(situ_status s) {
   switch (s) {
     case SITU_OK: return "SITU_OK";

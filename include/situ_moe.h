@@ -255,6 +255,17 @@ situ_status situ_moe_tile_weights(const uint8_t* w, const uint8_t* w_scale, int3
 situ_status situ_moe_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int32_t cols,
                                     uint8_t* codes, uint8_t* scales, void* hip_stream);
 
+/* Measurement aid for the roofline of the w4a8 GEMMs (not part of the
+ * layer): the sustained rate of v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 x
+ * E4M3 operands (the instruction the w4a8 FC1 kernels issue; 65536 flops
+ * each) on the current device, every SIMD running 4 waves of 8 independent
+ * accumulators for `iters` rounds on register operands.  Writes TFLOP/s to
+ * *tflops.  Synchronous (one warm-up launch, then one timed launch on a
+ * stream of its own); allocates no device memory.  iters in [1, 1 << 20]
+ * (SITU_E_BAD_SHAPE otherwise); SITU_E_NULL_ARG if tflops is NULL;
+ * SITU_E_DEVICE without a gfx950 device; SITU_E_LAUNCH on a runtime error. */
+situ_status situ_moe_measure_mfma_peak(int32_t iters, double* tflops);
+
 const char* situ_moe_status_string(situ_status status);
 const char* situ_moe_last_error(void);
 /* Human-readable build description: ABI version, gfx target, tactic family. */

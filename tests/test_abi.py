@@ -237,3 +237,12 @@ def test_tile_weights_argument_errors_before_any_device_work():
     assert tile(wt=fake + (1 << 24) + 4) == 2
     assert B.tiled_shapes(3, 48, 96) == ((3, 3, 1, 1024), (3, 3, 1, 64))
     assert B.tiled_shapes(1, 6144, 3584) == ((1, 384, 28, 1024), (1, 384, 28, 64))
+
+
+def test_measure_mfma_peak_argument_errors_before_any_device_work():
+    lib = B.load()
+    out = ctypes.c_double(-1.0)
+    assert lib.situ_moe_measure_mfma_peak(0, ctypes.byref(out)) == 2          # iters >= 1
+    assert lib.situ_moe_measure_mfma_peak((1 << 20) + 1, ctypes.byref(out)) == 2
+    assert lib.situ_moe_measure_mfma_peak(100, None) == 1
+    assert out.value == -1.0

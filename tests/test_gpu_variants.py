@@ -270,3 +270,11 @@ def test_hidden_not_multiple_of_1024_in_child_process(H, mode):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
     print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
     assert r.returncode == 0 and "CHILD_OK" in r.stdout
+
+
+def test_measured_mfma_peak_is_plausible():
+    """The measurement aid returns a rate between a fifth of the published FP8
+    peak (5.0 PFLOP/s, the rate E2M1 x E4M3 issues at) and that peak plus 10 %."""
+    tf = B.situ_moe_measure_mfma_peak(500)
+    print(f"block-scaled FP4 x FP8 MFMA: {tf:.0f} TFLOP/s", flush=True)
+    assert 1000.0 < tf < 5500.0
