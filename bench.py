@@ -21,9 +21,9 @@ value comes from K plain (eager) calls between two synchronizations.  A
 second pass times every call on its own (HIP events on the stream) for the
 median, p10 and p90; a third records six events per call at the stage
 boundaries (situ_moe_run_profiled) for each kernel's average duration on the
-stream it runs on.  A fourth pass writes a 512 MiB buffer before every call
-(outside the timed events) so that nothing is left in the 256 MiB MALL
-(median, p10, p90).  The step is also captured into a HIP graph and
+stream it runs on.  A fourth pass reads a 512 MiB buffer before every call
+(outside the timed events) so that nothing of the previous call is left in
+the 256 MiB MALL (median, p10, p90).  The step is also captured into a HIP graph and
 replayed; its time and whether its output equals the eager one bit for bit
 are reported.  Each roofline also carries the achieved rate against a
 measured ceiling: the device's plain copy bandwidth (HBM-bound kernels) or
@@ -324,18 +324,21 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
     per_call = [a_.elapsed_time(b_) for a_, b_ in evs]
 
     flushed = None
-    if mall_flush:   # a 512 MiB write before every call, outside its events
-        junk = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    if mall_flush:   # a 512 MiB read before every call, outside its events
+        # (a read leaves clean lines behind; a write would leave 256 MiB of
+        # dirty ones whose write-back then competes with the timed call)
+        junk = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         fevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         for a_, b_ in fevs:
-            junk.fill_(1.0)
+            torch.sum(junk, dim=0, out=sink)
             a_.record(stream)
             B.situ_moe_run(plan, ts, ws)
             b_.record(stream)
         torch.cuda.synchronize()
         flushed = _percentiles([a_.elapsed_time(b_) for a_, b_ in fevs])
-        flushed["note"] = "each call preceded by a 512 MiB device write (the MALL holds 256 MiB)"
-        del junk
+        flushed["note"] = "each call preceded by a 512 MiB device read (the MALL holds 256 MiB)"
+        del junk, sink
 
     # The same step captured once into a HIP graph, replayed K times.
     graph_ms = graph_same = graph_error = None
