@@ -11,6 +11,14 @@ namespace situ {
 
 constexpr int kMaxLocalExperts = 1024;
 
+struct QuantArgs {
+  const uint16_t* x;       // bf16 [rows, cols]
+  uint8_t* codes;          // [rows, cols]
+  uint8_t* scales;         // [rows, cols/32]
+  int64_t rows;
+  int32_t cols;
+};
+
 struct RouteArgs {
   const int32_t* ids;      // [T*k] or null when packed
   const int32_t* packed;   // [T*k] or null
@@ -26,15 +34,18 @@ struct RouteArgs {
   int32_t* hist;           // [nblocks, E_l] (multi-block routing only)
   int64_t chunk;           // pairs per block
   int32_t nblocks;         // 1 = single-workgroup routing
+  // w4a8 with bf16 input: the activations' MXFP8 quantization runs in the
+  // same launch as the router (single-workgroup routing) or as its count
+  // step, in quant_blocks further workgroups of kRouteThreads pieces (0: none)
+  QuantArgs quant;
+  int32_t quant_blocks;
 };
 
-struct QuantArgs {
-  const uint16_t* x;       // bf16 [rows, cols]
-  uint8_t* codes;          // [rows, cols]
-  uint8_t* scales;         // [rows, cols/32]
-  int64_t rows;
-  int32_t cols;
-};
+constexpr int kRouteThreads = 1024;   // the routing kernels' workgroup (16 waves)
+// 8-element pieces of a quantization (one thread each)
+__host__ __device__ inline int64_t quant_pieces(const QuantArgs& a) { return a.rows * (int64_t)(a.cols / 8); }
+
+
 
 // Grouped GEMM arguments shared by FC1 and FC2.  Rows of the A side (the
 // token-expert pairs) are found through the tile list built by the router.

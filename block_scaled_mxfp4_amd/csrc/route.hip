@@ -20,14 +20,18 @@
 // Large batches split the pairs into contiguous blocks: per-block histograms,
 // one scan workgroup (prefix over blocks, then over experts), and a scatter
 // in which every block repeats A and C on its own pairs from its own bases.
+// With bf16 activations in w4a8, further workgroups of the first launch
+// (the router's, or the histograms') quantize them to MXFP8 meanwhile: the
+// quantization moves into the permute step's launch.
 // Every position depends only on the input, never on timing.
 #include "common.hpp"
 #include "internal.hpp"
+#include "quant.hpp"
 
 namespace situ {
 
 constexpr int kRouteWaves = 16;
-constexpr int kRouteThreads = kRouteWaves * kWave;
+static_assert(kRouteThreads == kRouteWaves * kWave, "the routing workgroup is 16 waves");
 
 __device__ __forceinline__ int local_expert_of(const RouteArgs& a, int64_t j) {
   int id = a.packed ? (a.packed[j] & 0xFFFF) : a.ids[j];
@@ -144,11 +148,27 @@ __device__ int scan_experts(const RouteArgs& a, int total_of_tid, int (*wave_sum
   return excl_a;
 }
 
+// Workgroups past the router's (blockIdx.x >= first) quantize the bf16
+// activations to MXFP8, 8-element pieces in a grid-stride loop: the
+// quantization overlaps the routing and needs no launch of its own.
+__device__ __forceinline__ bool quant_block(const RouteArgs& a, int first) {
+  if ((int)blockIdx.x < first) return false;
+  // grid-stride over the pieces: a block's lanes stay in whole 32-element
+  // blocks (the stride is a multiple of 4 and cols / 8 is a multiple of 4),
+  // so the four lanes of a block always leave the loop together
+  const int64_t n8 = quant_pieces(a.quant);
+  const int64_t stride = (int64_t)(gridDim.x - first) * kRouteThreads;
+  for (int64_t c = (int64_t)(blockIdx.x - first) * kRouteThreads + threadIdx.x; c < n8; c += stride)
+    quant_mxfp8_piece(a.quant, c);
+  return true;
+}
+
 // Small batches: one workgroup does everything in LDS.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int cnt[kRouteWaves][kMaxLocalExperts];
   __shared__ int offs[kMaxLocalExperts];
   __shared__ int wave_sums[2][kRouteWaves];
+  if (quant_block(a, 1)) return;   // uniform per workgroup
   const int tid = threadIdx.x;
   int lv[kRouteKept];
   count_waves(a, 0, a.TK, cnt, lv);
@@ -176,6 +196,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 // 1. per-block histograms -> hist[b][l]
 __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a) {
   __shared__ int h[kMaxLocalExperts];
+  if (quant_block(a, a.nblocks)) return;   // uniform per workgroup
   const int tid = threadIdx.x;
   for (int l = tid; l < kMaxLocalExperts; l += kRouteThreads) h[l] = 0;
   __syncthreads();
@@ -239,11 +260,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  const unsigned qb = a.quant_blocks > 0 ? (unsigned)a.quant_blocks : 0u;
   if (a.nblocks <= 1) {
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+    hipLaunchKernelGGL(route_kernel, dim3(1 + qb), dim3(kRouteThreads), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(route_count_kernel, dim3(a.nblocks), dim3(kRouteThreads), 0, s, a);
+  hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)a.nblocks + qb), dim3(kRouteThreads), 0, s, a);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(a.nblocks), dim3(kRouteThreads), 0, s, a);
   return hipGetLastError();

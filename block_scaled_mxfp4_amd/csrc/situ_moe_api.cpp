@@ -278,6 +278,8 @@ situ::RouteArgs route_args(const situ_moe_plan_t* plan, const situ_moe_tensors* 
   r.hist = at<int32_t>(ws, plan->off_route_hist);
   r.chunk = plan->route_chunk;
   r.nblocks = plan->route_blocks;
+  r.quant = situ::QuantArgs{};
+  r.quant_blocks = 0;
   return r;
 }
 
@@ -404,18 +406,19 @@ situ_status run_impl(const situ_moe_plan_t* plan, const situ_moe_tensors* t, voi
   };
   if ((st = mark(0)) != SITU_OK) return st;
   situ::RouteArgs ra = route_args(plan, t, ws);
-  if ((st = launch_status(situ::launch_route(ra, s), "route")) != SITU_OK) return st;
-  if ((st = mark(1)) != SITU_OK) return st;
-
   const void* act = t->hidden_states;
   const uint8_t* act_scale = t->hidden_states_scale;
-  if (w4a8 && !p.act_prequantized) {
-    situ::QuantArgs q{static_cast<const uint16_t*>(t->hidden_states), at<uint8_t>(ws, plan->off_xq),
-                      at<uint8_t>(ws, plan->off_xs), T, (int32_t)H};
-    if ((st = launch_status(situ::launch_quant_mxfp8(q, s), "quantize")) != SITU_OK) return st;
-    act = q.codes;
-    act_scale = q.scales;
+  if (w4a8 && !p.act_prequantized) {   // quantized in the routing launch, beside the router
+    ra.quant = situ::QuantArgs{static_cast<const uint16_t*>(t->hidden_states), at<uint8_t>(ws, plan->off_xq),
+                               at<uint8_t>(ws, plan->off_xs), T, (int32_t)H};
+    const int64_t need = (situ::quant_pieces(ra.quant) + situ::kRouteThreads - 1) / situ::kRouteThreads;
+    ra.quant_blocks = (int32_t)(need < 4 * (int64_t)cus ? need : 4 * (int64_t)cus);   // at most 4 per CU
+    act = ra.quant.codes;
+    act_scale = ra.quant.scales;
   }
+  if ((st = launch_status(situ::launch_route(ra, s), "route")) != SITU_OK) return st;
+  if ((st = mark(1)) != SITU_OK) return st;
+  // (the quantization's stage is part of the routing launch's)
   if ((st = mark(2)) != SITU_OK) return st;
 
   situ::GemmArgs g{};

@@ -291,6 +291,25 @@ def test_w4a8_prequantized_equals_library_quantized(name):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,k,tactic", [(4096, 16, (-1, -1)), (4096, 16, (4, 20)), (40, 4, (2, 18)), (40, 4, (6, 22))])
+def test_quantization_in_the_routing_launch(T, k, tactic):
+    """w4a8 with bf16 input: the MXFP8 quantization runs in the routing launch
+    (beside the multi-block router at 65536 pairs, beside the one-workgroup
+    router at 160); its codes and scales in the workspace equal the oracle's
+    quantization byte for byte, and the layer's output equals the output from
+    the oracle-prequantized input bit for bit."""
+    spec = S.spec_of(dict(T=T, H=256, I=128, E_g=32, E_l=24, off=4, k=k, seed=41 + T, skew=True, mode="w4a8"))
+    inp = S.generate(spec)
+    a, *_ = run_layer(inp, spec, mode="w4a8", prequantized=True, tactic=tactic)
+    b, plan, ws, _ = run_layer(inp, spec, mode="w4a8", prequantized=False, tactic=tactic)
+    assert (plan.route_blocks > 1) == (T * k > 32768)
+    codes, scales = F.mx_quantize(F.bf16_to_f64(inp["hidden_states"]), "e4m3")
+    xq = B.workspace_view(plan, ws, "xq", torch.uint8, (T, 256)).cpu().numpy()
+    xs = B.workspace_view(plan, ws, "xs", torch.uint8, (T, 256 // 32)).cpu().numpy()
+    assert np.array_equal(xq, codes) and np.array_equal(xs, scales)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 @pytest.mark.parametrize("mode,name,tactic", [("w4a16", "wide", (-1, -1)), ("w4a8", "wide", (-1, -1)),
                                                ("w4a8", "prefill_c", (3, 19)), ("w4a8", "prefill_c", (4, 20))])
 def test_intermediate_h_matches_oracle(mode, name, tactic):
