@@ -163,7 +163,10 @@ int valid_pairs(const situ_moe_problem* p, int32_t* fc1, int32_t* fc2, int cap) 
   const int64_t mt128 = (TK + 127) / 128 + p->local_num_experts;
   const bool wide = w4a8 && p->hidden_size % 128 == 0 && p->intermediate_size % 128 == 0 &&
                     mt128 * 128 * p->intermediate_size < ((int64_t)1 << 31);
-  const double rows_per_expert = (double)TK / p->local_num_experts;
+  // the expected group size: the plan is made without the routing, so the
+  // batch's T*k pairs are taken as spread evenly over all E_g experts (in an
+  // EP shard only about E_l / E_g of them are local)
+  const double rows_per_expert = (double)TK / p->num_experts;
   const int32_t* order[4] = {m16, m64, m128, fused};
   int n_order = wide ? 3 : 2;
   if (wide && rows_per_expert > kWideRowsPerExpert) {

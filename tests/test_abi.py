@@ -158,6 +158,11 @@ def test_plan_layout_and_tactics():
     assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a16")).block_m == 64
     assert B.situ_moe_plan(_prob(num_tokens=16384, act_mode="w4a8")).block_m == 128
     assert B.situ_moe_valid_tactics(_prob(num_tokens=16384, act_mode="w4a8"))[:2] == [(4, 20), (3, 19)]
+    # an EP shard's groups are sized by the whole batch over all E_g experts:
+    # 256 decode tokens over 56 of 896 experts average ~4.6 local rows each
+    ep16 = dict(num_tokens=256, intermediate_size=3072, local_num_experts=56, local_expert_offset=280)
+    assert B.situ_moe_plan(_prob(**ep16)).block_m == 16
+    assert B.situ_moe_plan(_prob(**dict(ep16, num_tokens=32768, act_mode="w4a8"))).block_m == 128
     # the 128-row kernel needs sizes that are multiples of 128
     assert (4, 20) not in B.situ_moe_valid_tactics(_prob(num_tokens=16384, act_mode="w4a8", intermediate_size=416))
 
