@@ -69,24 +69,28 @@ def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_work(spec, counts, tokens_used, y_format=0):
+def algorithmic_work(spec, counts, tokens_used, y_format=0, lora=False):
     """Bytes and flops the layer must move / compute, per stage: every active
-    expert's packed E2M1 weights with their E8M0 scales, each used token's
-    input row as the kernel reads it, h and y once each, and 2 flops per
-    multiply-add of the two contractions.  y_format 1: y is fp16 with one
-    exponent byte per 64 columns."""
+    expert's packed E2M1 weights with their scales (E8M0 per 32, or E4M3 per
+    16 for NVFP4), each used token's input row as the kernel reads it, h and
+    y once each, and 2 flops per multiply-add of the two contractions.
+    y_format 1: y is fp16 with one exponent byte per 64 columns.  lora: FC1
+    also reads each local pair's bf16 gate_up delta row and writes the bf16
+    down-LoRA input, every one of its T*k rows (zeros outside the shard)."""
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
     counts = np.asarray(counts, np.int64)
     A = int(np.count_nonzero(counts))
     P = int(counts.sum())
     w4a8 = spec["mode"] == "w4a8"
-    fc1_w = 2 * I * (H // 2 + H // 32)              # packed E2M1 + E8M0 per expert
-    fc2_w = H * (I // 2 + I // 32)
+    blk = 16 if spec.get("weight_format") == "nvfp4" else 32   # K elements per weight scale byte
+    fc1_w = 2 * I * (H // 2 + H // blk)             # packed E2M1 + scales per expert
+    fc2_w = H * (I // 2 + I // blk)
     x_row = H + H // 32 if w4a8 else 2 * H          # the FC1 input row as the kernel reads it
     h_row = I + I // 32 if w4a8 else 2 * I
+    lora_bytes = P * 2 * I * 2 + T * k * I * 2 if lora else 0
     work = {
         "A": A, "P": P,
-        "fc1_bytes": A * fc1_w + tokens_used * x_row + P * h_row,
+        "fc1_bytes": A * fc1_w + tokens_used * x_row + P * h_row + lora_bytes,
         "fc2_bytes": A * fc2_w + P * h_row + (P * (2 * H + (H + 63) // 64) if y_format else P * H * 4),
         "fc1_flops": 2.0 * P * H * 2 * I,
         "fc2_flops": 2.0 * P * I * H,
@@ -193,10 +197,12 @@ def _first_tokens(inp, n):
     return sub
 
 
-def cpu_baseline(inp, spec, budget_s=30.0):
+def cpu_baseline(inp, spec, budget_s=30.0, lora=False):
     """The oracle (float32 mode, as it stands) on a bounded sample: the first n
     tokens of the same batch, n chosen for about budget_s seconds of CPU work
-    (w4a8: including the oracle's own MXFP8 quantization of those tokens)."""
+    (w4a8: including the oracle's own MXFP8 quantization of those tokens).
+    lora: the sample's pairs get gate_up delta rows ~ N(0, 0.05) of their own
+    (the device draws the full batch's rows)."""
     from oracle import moe as M
     try:
         from threadpoolctl import threadpool_info
@@ -208,9 +214,15 @@ def cpu_baseline(inp, spec, budget_s=30.0):
     T = spec["T"]
 
     def run(n):
+        sub = _first_tokens(inp, n)
+        if lora:
+            rng = np.random.default_rng(spec["seed"])
+            d = (rng.standard_normal((n * spec["k"], 2 * spec["I"])) * 0.05).astype(np.float32)
+            sub["gate_up_lora_delta"] = (d.view(np.uint32) >> 16).astype(np.uint16)
         t0 = time.perf_counter()
-        M.moe_forward(_first_tokens(inp, n), local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
-                      act_mode=spec["mode"], precision="f32")
+        M.moe_forward(sub, local_expert_offset=spec["off"], local_num_experts=spec["E_l"],
+                      act_mode=spec["mode"], precision="f32", activation=spec["activation"],
+                      weight_format=spec["weight_format"])
         return time.perf_counter() - t0
 
     n = min(T, 4)
@@ -230,18 +242,25 @@ def _percentiles(ms):
 
 
 def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weights="tiled", rows_beside=True,
-            refs=None):
+            refs=None, overrides=None, lora=False, lean=False, cpu_budget=30.0):
     """Time one workload; returns the result fields of its line.  weights:
     "tiled" hands the layer its MXFP4 weights in the fragment-tiled layout
     (made once by situ_moe_tile_weights before timing; the same values, so
     the same output bit for bit) and times the row-major weights beside it;
     "rows" times the row-major weights only (rows_beside=False: tiled
-    only, so that a profiler sees one layout's launches)."""
+    only, so that a profiler sees one layout's launches).  overrides: spec
+    fields replaced (activation, weight_format; NVFP4 weights stay
+    row-major); lora: the layer also takes a bf16 gate_up delta per pair
+    (drawn on the device, seeded) and writes the down-LoRA input; lean:
+    only the eager, per-call and per-stage passes (no graph replay and no
+    bf16-input step)."""
     import torch
     import block_scaled_mxfp4_amd as B
     import synthetic as S
 
     spec = S.spec_of(cfg)
+    if overrides:
+        spec = S.spec_of(dict(spec, **overrides))
     _log(f"generating inputs for config {cfg} ({spec['name']})")
     t0 = time.perf_counter()
     inp = S.generate(spec)
@@ -256,14 +275,16 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
     T, H, I, k = spec["T"], spec["H"], spec["I"], spec["k"]
     w4a8 = spec["mode"] == "w4a8"
 
-    tiled = weights == "tiled"
-    wf = "mxfp4_tiled" if tiled else "mxfp4"
+    nv = spec["weight_format"] == "nvfp4"
+    tiled = weights == "tiled" and not nv
+    wf = "nvfp4" if nv else ("mxfp4_tiled" if tiled else "mxfp4")
 
     def problem(prequantized, weight_format=wf):
         return B.make_problem(num_tokens=T, hidden_size=H, intermediate_size=I, num_experts=spec["E_g"],
                               local_expert_offset=spec["off"], local_num_experts=spec["E_l"], top_k=k,
                               act_mode=spec["mode"], act_prequantized=prequantized, topk_packed=packed,
-                              out_dtype="f32", tactic=tactic, weight_format=weight_format)
+                              out_dtype="f32", tactic=tactic, activation=spec["activation"],
+                              weight_format=weight_format)
 
     x_bf16 = d(inp["hidden_states"])
     prob = problem(w4a8)
@@ -279,6 +300,19 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
                 alpha_up=d(inp["alpha_up"]), out=torch.empty((T, H), dtype=torch.float32, device=dev))
     if w4a8:
         tens["hidden_states_scale"] = x_scales
+    for key in ("swiglu_alpha", "swiglu_beta", "alpha_down"):
+        if inp.get(key) is not None:
+            tens[key] = d(inp[key])
+    if lora:   # a LoRA adapter's FC1 contribution per pair, N(0, 0.05) as bf16
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7000 + spec["seed"])
+        delta = torch.empty((T * k, 2 * I), dtype=torch.bfloat16, device=dev)
+        for r0 in range(0, T * k, 65536):
+            r1 = min(T * k, r0 + 65536)
+            delta[r0:r1] = (torch.randn((r1 - r0, 2 * I), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        tens["gate_up_lora_delta"] = delta
+        tens["activation_lora_input"] = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
     if packed:
         tens["topk_packed"] = d(inp["topk_packed"])
     else:
@@ -343,6 +377,8 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
     # The same step captured once into a HIP graph, replayed K times.
     graph_ms = graph_same = graph_error = None
     try:
+        if lean:
+            raise RuntimeError("not measured for this workload")
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -387,7 +423,7 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
         del out_r
 
     bf16_input_ms = None
-    if w4a8:   # bf16 activations, quantized by the library inside the step
+    if w4a8 and not lean:   # bf16 activations, quantized by the library inside the step
         prob16 = problem(False)
         plan16 = B.situ_moe_plan(prob16)
         t16 = dict(tens, hidden_states=x_bf16)
@@ -420,9 +456,12 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
     counts = B.workspace_view(plan, ws, "counts", torch.int32, (spec["E_l"],)).cpu().numpy()
     inv = B.workspace_view(plan, ws, "inv", torch.int32, (T * k,)).cpu().numpy().reshape(T, k)
     tokens_used = int(np.count_nonzero((inv >= 0).any(axis=1)))
-    work = algorithmic_work(spec, counts, tokens_used, plan.y_format)
+    work = algorithmic_work(spec, counts, tokens_used, plan.y_format, lora)
 
     workload = f"{spec['name']}_{spec['mode']}"
+    variant = [v for v in (spec["activation"] != "situ" and spec["activation"], nv and "nvfp4", lora and "lora") if v]
+    if variant:
+        workload += "_" + "_".join(variant)
     peak_tf = MFMA_PEAK_TFLOPS["mxfp8"] if w4a8 else MFMA_PEAK_TFLOPS["bf16"]
 
     def roofline(stage):
@@ -472,7 +511,9 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
                    "active_local_experts": work["A"], "local_pairs": work["P"],
                    "fc1_tactic": B.situ_moe_tactic_name(plan.fc1_tactic),
                    "fc2_tactic": B.situ_moe_tactic_name(plan.fc2_tactic),
-                   "weights": "MXFP4, fragment-tiled once by situ_moe_tile_weights before timing" if tiled
+                   "activation": spec["activation"], "lora_bridges": bool(lora),
+                   "weights": "NVFP4 (E4M3 scale per 16), row-major" if nv else
+                              "MXFP4, fragment-tiled once by situ_moe_tile_weights before timing" if tiled
                               else "MXFP4, row-major"},
         "roofline": with_measured(roof, refs),
         "roofline_other_gemm": with_measured({kk: other[kk] for kk in ("kernel", "bound", "achieved", "peak", "unit",
@@ -499,10 +540,50 @@ def measure(cfg, steps, warmup, dev, want_cpu, mall_flush, tactic=(-1, -1), weig
                              "note": "the same step with bf16 activations quantized by the library (eager)"}
     if want_cpu:
         _log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(inp, spec)
+        res["cpu_baseline"] = cpu_baseline(inp, spec, cpu_budget, lora)
     del ws
     torch.cuda.empty_cache()
     return res
+
+
+# The layer's variants at full size, each timed like the workloads above
+# (lean: eager, per-call and per-stage passes), its dominant kernel against
+# its roofline and the oracle on a small sample of the same batch beside it:
+# the fused decode kernel, NVFP4 weights, the LoRA bridges, the SwiGLU and
+# SwigluBias activations, the EP16 shard (56 of 896 experts) and an uneven
+# EP shard (896 experts over 6 ranks: 150, 150, 149, 149, 149, 149; rank 4).
+# name -> (config id or spec, spec overrides, measure() options)
+_EP16 = dict(H=3584, I=3072, E_g=896, E_l=56, off=5 * 56, k=16, skew=True)
+_EP6 = dict(H=3584, I=3072, E_g=896, E_l=149, off=150 + 150 + 149 + 149, k=16, skew=True)
+VARIANTS = {
+    "tp8_decode_fused": (1, {}, dict(tactic=(5, 21))),
+    "tp8_decode_nvfp4": (1, {"weight_format": "nvfp4"}, {}),
+    "ep8_decode_nvfp4": (2, {"weight_format": "nvfp4"}, {}),
+    "tp8_decode_lora": (1, {}, dict(lora=True)),
+    "tp8_prefill_lora": (3, {}, dict(lora=True)),
+    "ep8_prefill_lora": (4, {}, dict(lora=True)),
+    "tp8_decode_swiglu_bias": (1, {"activation": "swiglu_bias"}, {}),
+    "ep8_prefill_swiglu": (4, {"activation": "swiglu"}, {}),
+    "ep8_prefill_swiglu_bias": (4, {"activation": "swiglu_bias"}, {}),
+    "ep16_decode": (dict(_EP16, name="ep16_decode", T=256, mode="w4a16", seed=161), {}, {}),
+    "ep16_prefill": (dict(_EP16, name="ep16_prefill", T=32768, mode="w4a8", packed=True, seed=162), {}, {}),
+    "uneven_ep6_decode": (dict(_EP6, name="uneven_ep6_decode", T=256, mode="w4a16", seed=163), {}, {}),
+    "uneven_ep6_prefill": (dict(_EP6, name="uneven_ep6_prefill", T=32768, mode="w4a8", packed=True, seed=164),
+                           {}, {}),
+}
+
+
+def measure_variants(names, steps, warmup, dev, refs, want_cpu):
+    out = {}
+    for name in names:
+        cfg, overrides, opts = VARIANTS[name]
+        _log(f"variant {name}")
+        r = measure(cfg, steps, warmup, dev, want_cpu, mall_flush=False, rows_beside=False, refs=refs,
+                    overrides=overrides, lean=True, cpu_budget=6.0, **opts)
+        for key in ("graph_replay", "wall_s_timed_region", "activations"):
+            r.pop(key, None)
+        out[name] = {"tokens_per_s": r.pop("value"), **r}
+    return out
 
 
 # ---------------------------------------------------------------- rocprofv3 summaries
@@ -673,6 +754,11 @@ def main(argv=None):
                     help="MXFP4 weight layout handed to the layer (tiled: the row-major step is timed beside it)")
     ap.add_argument("--no-row-major", action="store_true",
                     help="with tiled weights, skip the row-major step (profiling runs: one layout's launches)")
+    ap.add_argument("--variants", default="",
+                    help="comma-separated variant workloads measured after the others, or 'all': "
+                         + ", ".join(VARIANTS))
+    ap.add_argument("--no-headline", action="store_true",
+                    help="measure the variants only (profiling runs); the line then carries no value")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -707,6 +793,17 @@ def main(argv=None):
     dtac = tuple(int(v) for v in args.decode_tactic.split(","))
     refs = reference_rates(dev)
     _log(f"measured ceilings: {refs}")
+    names = list(VARIANTS) if args.variants == "all" else [v for v in args.variants.split(",") if v]
+    for v in names:
+        if v not in VARIANTS:
+            raise SystemExit(f"unknown variant {v!r}; known: {', '.join(VARIANTS)}")
+    if args.no_headline:
+        res = {"variants": measure_variants(names, args.steps, args.warmup, dev, refs, not args.no_cpu_baseline),
+               "measured_ceilings": refs, "steps": args.steps, "warmup": args.warmup}
+        if args.copy_probe_mib > 0:
+            copy_probe(args.copy_probe_mib, 3)
+        print(json.dumps(res), flush=True)
+        return 0
     head = measure(args.config, args.steps, args.warmup, dev, not args.no_cpu_baseline, mall_flush=True, tactic=tac,
                    weights=args.weights, rows_beside=not args.no_row_major, refs=refs)
     res = {
@@ -730,6 +827,8 @@ def main(argv=None):
         dec = measure(args.decode_config, max(args.steps, 20), args.warmup, dev, False, mall_flush=True, tactic=dtac,
                       weights=args.weights, rows_beside=not args.no_row_major, refs=refs)
         res["decode"] = {"metric_value_tokens_per_s": dec.pop("value"), **dec}
+    if names:
+        res["variants"] = measure_variants(names, args.steps, args.warmup, dev, refs, not args.no_cpu_baseline)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, 3)
     print(json.dumps(res), flush=True)
