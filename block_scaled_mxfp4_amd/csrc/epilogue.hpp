@@ -43,24 +43,24 @@ __device__ __forceinline__ SituK situ_item(const GemmArgs& a, int l) {
   return situ_consts(ag, au, __builtin_bit_cast(float, ((cp)a.beta)[l]), __builtin_bit_cast(float, ((cp)a.lbeta)[l]));
 }
 
-// Four consecutive bf16 of a row as floats.
-__device__ __forceinline__ void load_bf16x4(const uint16_t* p, float v[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  v[0] = bf16_to_f32(w.x & 0xffffu);
-  v[1] = bf16_to_f32(w.x >> 16);
-  v[2] = bf16_to_f32(w.y & 0xffffu);
-  v[3] = bf16_to_f32(w.y >> 16);
+// A pair's LoRA delta at four gate columns and the matching four up columns
+// (I further), as bf16 bits.
+struct DeltaPiece {
+  uint2 g, u;
+};
+__device__ __forceinline__ DeltaPiece load_delta(const uint16_t* drow, int I) {
+  return DeltaPiece{*reinterpret_cast<const uint2*>(drow), *reinterpret_cast<const uint2*>(drow + I)};
 }
 
 // The activation inputs of four gate/up column pairs: the accumulators, plus
-// with a LoRA delta (drow = the pair's delta row at the first gate column;
-// up columns I further) the delta divided by alpha.
-__device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* drow, int I, const float ag4[4],
-                                           const float au4[4], float xg[4], float xu[4]) {
+// with a LoRA delta the delta piece divided by alpha.
+__device__ __forceinline__ void act_inputs_of(const ActItem& it, const DeltaPiece& d, const float ag4[4],
+                                              const float au4[4], float xg[4], float xu[4]) {
   if (it.lora) {
-    float dg[4], du[4];
-    load_bf16x4(drow, dg);
-    load_bf16x4(drow + I, du);
+    const float dg[4] = {bf16_to_f32(d.g.x & 0xffffu), bf16_to_f32(d.g.x >> 16), bf16_to_f32(d.g.y & 0xffffu),
+                         bf16_to_f32(d.g.y >> 16)};
+    const float du[4] = {bf16_to_f32(d.u.x & 0xffffu), bf16_to_f32(d.u.x >> 16), bf16_to_f32(d.u.y & 0xffffu),
+                         bf16_to_f32(d.u.y >> 16)};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       xg[e] = dg[e] != 0.0f ? __builtin_fmaf(dg[e], it.rag, ag4[e]) : ag4[e];
@@ -73,6 +73,13 @@ __device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* dr
       xu[e] = au4[e];
     }
   }
+}
+
+// The same with the delta read here (drow = the pair's delta row at the first
+// gate column).
+__device__ __forceinline__ void act_inputs(const ActItem& it, const uint16_t* drow, int I, const float ag4[4],
+                                           const float au4[4], float xg[4], float xu[4]) {
+  act_inputs_of(it, it.lora ? load_delta(drow, I) : DeltaPiece{}, ag4, au4, xg, xu);
 }
 
 // E4M3 code (one byte of `codes`, hardware decode, exact) times 2^(sc - 127), as bf16 bits.

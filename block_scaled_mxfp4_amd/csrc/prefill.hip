@@ -282,13 +282,39 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
     const bool bridges = GEN && (ai.lora || a.lora_out);   // uniform
     const v4i hr = rsrc4(static_cast<uint8_t*>(a.out) + (size_t)x.p0 * I, (uint32_t)(TOK * I));
     const v4i sr = rsrc4(a.out_scale + (size_t)x.p0 * (I / 32), (uint32_t)(TOK * (I / 32)));
+    // the pairs' expanded indices (the rows of their LoRA deltas and down-LoRA
+    // inputs), then every delta piece of the call, requested together: read
+    // one by one beside the h stores, each would wait out its own latency
+    // (without branches per piece: rows outside the group read pair 0's
+    // entries, which are never used)
+    int64_t jt[2] = {0, 0};
+    DeltaPiece dl[2][NG / 2][2];
+    if constexpr (GEN) {
+      if (bridges) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bool ok = tt < ntt && x.p0 + 32 * wm + 16 * tt + r < x.p1;
+          const int pv = a.perm[ok ? x.p0 + 32 * wm + 16 * tt + r : 0];
+          jt[tt] = ok ? pv : 0;
+        }
+      }
+      if (ai.lora) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int blk = 0; blk < NG / 2; ++blk)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              dl[tt][blk][h2] = load_delta(a.lora_delta + jt[tt] * (2 * I) + n0 + 16 * NG * wn + 32 * blk +
+                                               16 * h2 + 4 * g, I);
+      }
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt >= ntt) break;                          // uniform: a tile of padding rows only
       const int pr = 32 * wm + 16 * tt + r;          // row within the m-tile
       const bool valid = x.p0 + pr < x.p1;
-      // the pair's expanded index: the row of its LoRA delta and down-LoRA input
-      const int64_t j = (bridges && valid) ? (int64_t)a.perm[x.p0 + pr] : 0;
+      const int64_t j = jt[tt];
 #pragma unroll
       for (int blk = 0; blk < NG / 2; ++blk) {     // NG / 2 32-column MXFP8 blocks per wave
         // h = q * blb with q = act_q (SiTU: blb = b*lb, else 1): the block
@@ -309,7 +335,7 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
             float xg[4], xu[4];
             const float ag4[4] = {gv[0], gv[1], gv[2], gv[3]};
             const float au4[4] = {uv[0], uv[1], uv[2], uv[3]};
-            act_inputs(ai, a.lora_delta + j * (2 * I) + col0 + 16 * h2 + 4 * g, I, ag4, au4, xg, xu);
+            act_inputs_of(ai, dl[tt][blk][h2], ag4, au4, xg, xu);
 #pragma unroll
             for (int e = 0; e < 4; ++e) qv[h2][e] = act_q(xg[e], xu[e], ai.k);
           } else {
@@ -360,6 +386,22 @@ __device__ __forceinline__ void pf_epilogue(const GemmArgs& a, const PfItem& x, 
           *reinterpret_cast<uint2*>(lrow + 16) = e4m3x4_to_bf16x4(packed[1], (int)code);
         }
       }
+    }
+    if constexpr (GEN) {
+      // every delta piece counts as read here, on every path (those of a token
+      // tile of padding rows are not read above; without a delta nothing was
+      // requested and nothing is waited for): the compiler then waits for them
+      // here, behind nothing, instead of waiting for every request in flight
+      // (the next item's stages) where it next writes their registers
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int blk = 0; blk < NG / 2; ++blk)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const DeltaPiece& dp = dl[tt][blk][h2];
+            asm volatile("" ::"v"(dp.g.x), "v"(dp.g.y), "v"(dp.u.x), "v"(dp.u.y));
+          }
     }
   } else {
     // y rows leave through LDS: a 16-token x 64-column block of the wave's
