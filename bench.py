@@ -35,6 +35,14 @@ kernel (algorithmic bytes or flops per launch over its average duration),
 per-stage times, and the CPU oracle timed on a bounded sample of the same
 workload.
 
+    python bench.py --no-headline --variants all | NAME,NAME,...
+
+times the layer's variants at full size (the fused decode kernel, NVFP4
+weights, the LoRA bridges, SwiGLU and SwigluBias, the EP16 shard and an
+uneven EP shard; VARIANTS below), each with its dominant kernel's roofline
+and the oracle on a small sample of its batch; without --no-headline they
+are added to the line under "variants".
+
     python bench.py --summarize-stats DIR --workload W --command "..."
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --workload W --stage S --command "..."
     python bench.py --summarize-pmc DIR --workload W --command "..."
