@@ -71,7 +71,9 @@ def run_layer(inp, spec, *, mode=None, out_dtype="f32", tactic=(-1, -1), prequan
     if tiled:
         d["w1"], d["w1_scale"] = B.situ_moe_tile_weights(d["w1"], d["w1_scale"])
         d["w2"], d["w2_scale"] = B.situ_moe_tile_weights(d["w2"], d["w2_scale"])
-    if inp.get("gate_up_lora_delta") is not None:
+    if isinstance(inp.get("gate_up_lora_delta"), torch.Tensor):   # already on the device
+        d["gate_up_lora_delta"] = inp["gate_up_lora_delta"]
+    elif inp.get("gate_up_lora_delta") is not None:
         d["gate_up_lora_delta"] = dev(np.asarray(inp["gate_up_lora_delta"]).reshape(T * k, 2 * I))
     if lora_out:   # filled with a pattern the layer must overwrite everywhere
         d["activation_lora_input"] = torch.full((T * k, I), float("nan"), dtype=torch.bfloat16, device="cuda")

@@ -21,7 +21,7 @@ import synthetic as S
 from oracle import formats as F
 from oracle import moe as M
 
-from gpu_helpers import gpu_h, layer_check, parity, run_layer
+from gpu_helpers import check_h, config_inputs, gpu_h, layer_check, oracle_out, parity, run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,65 @@ def test_lora_bridges(name, mode, tactic):
     a, *_ = run_layer(zero, spec, mode=mode, tactic=tactic)
     b, *_ = run_layer(dict(inp, gate_up_lora_delta=None), spec, mode=mode, tactic=tactic)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_lora_bridges_full_size_ep8_prefill():
+    """The LoRA bridges on the EP8 prefill shard at full size (32768 tokens,
+    T*k = 524288 pairs: the bf16 delta is 6.4 GB and the down-LoRA input 3.2
+    GB, so the rows of the last pairs lie beyond 2^31 and 2^32 bytes), in the
+    launch the benchmark times.  The delta is zero except for eight tokens,
+    four of them the last ones with a local slot; the oracle runs on those
+    eight tokens alone (the layer is independent per token), and the GPU's h
+    rows of their pairs, taken from the full batch's permuted order, must be
+    valid element by element and give the output within the bar through the
+    oracle's FC2 and combine.  Their down-LoRA rows equal h, the rows of
+    their pairs outside the shard and the last rows of the buffer are +0."""
+    inp = config_inputs(4)
+    spec = inp["spec"]
+    T, k, I, mode = spec["T"], spec["k"], spec["I"], spec["mode"]
+    counts, offsets, perm, inv = M.route(inp["topk_ids"], spec["off"], spec["E_l"])
+    has_local = np.nonzero((inv.reshape(T, k) >= 0).any(axis=1))[0]
+    rng = np.random.default_rng(404)
+    tok = np.unique(np.concatenate([has_local[-4:], rng.choice(has_local[:-4], 4, replace=False)]))
+    n = tok.size
+    rows = S.bf16_truncate(rng.standard_normal((n * k, 2 * I)).astype(np.float32) * 0.5)
+    j_rows = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    assert int(j_rows.max()) * 2 * I * 2 > 2 ** 32
+    delta = torch.zeros((T * k, 2 * I), dtype=torch.bfloat16, device="cuda")
+    delta[torch.from_numpy(j_rows).cuda()] = torch.from_numpy(rows.view(np.int16)).cuda().view(torch.bfloat16)
+    got, plan, ws, d = run_layer(dict(inp, gate_up_lora_delta=delta), spec, mode=mode, lora_out=True)
+    del delta
+    P = int(offsets[-1])
+    hg = gpu_h(plan, ws, P, I, mode)
+
+    # the eight tokens as a batch of their own
+    sub = dict(inp, gate_up_lora_delta=rows)
+    for key in ("hidden_states", "topk_ids", "topk_weights", "topk_packed"):
+        if inp.get(key) is not None:
+            sub[key] = np.ascontiguousarray(inp[key][tok])
+    spec_sub = dict(spec, T=n)
+    ref = oracle_out(sub, spec_sub, mode=mode, keep=True)
+    # the sub-batch's pair p' is the full batch's pair inv[tok*k + s]
+    full_of = np.full(int(ref["offsets"][-1]), -1, np.int64)
+    sub_inv = ref["inv"].reshape(n, k)
+    loc = sub_inv >= 0
+    full_of[sub_inv[loc]] = inv.reshape(T, k)[tok][loc]
+    assert np.all(full_of >= 0)
+    hg_sub = {key: v[full_of] for key, v in hg.items()}
+    check_h(hg_sub, sub, spec_sub, ref, mode, "EP8 prefill LoRA, 8 tokens")
+    cond = oracle_out(sub, spec_sub, mode=mode, h_given=hg_sub["vals"])
+    parity(got[tok], cond["out"], "EP8 prefill LoRA, 8 tokens vs oracle FC2 + combine of the GPU's h")
+
+    # down-LoRA rows: h of the local pairs, +0 elsewhere (the sampled tokens'
+    # pairs and the buffer's last 4096 rows)
+    lo = d["activation_lora_input"]
+    check_j = np.unique(np.concatenate([j_rows, np.arange(T * k - 4096, T * k)]))
+    got_rows = lo[torch.from_numpy(check_j).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    p_of = inv[check_j]
+    np.testing.assert_array_equal(F.bf16_to_f64(got_rows[p_of >= 0]), hg["vals"][p_of[p_of >= 0]])
+    assert np.all(got_rows[p_of < 0] == 0)
+    print(f"EP8 prefill LoRA: {n} tokens, {int(loc.sum())} local pairs, {int((p_of >= 0).sum())} local and "
+          f"{int((p_of < 0).sum())} other down-LoRA rows checked", flush=True)
 
 
 @pytest.mark.parametrize("activation", ["situ", "swiglu_bias"])
