@@ -87,6 +87,21 @@ def test_lora_bridges(name, mode, tactic):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("cfg,overrides", [(1, {"weight_format": "nvfp4"}), (2, {"weight_format": "nvfp4"}),
+                                           (2, {"activation": "swiglu_bias"})])
+def test_decode_variants_full_size(cfg, overrides):
+    """NVFP4 weights on the TP8 and EP8 decode shards and SwigluBias on the
+    EP8 decode shard at full size, in the planner's tactics (the 16-row
+    decode kernels with K split): every token's h valid element by element
+    and the output within the whole bar, against the oracle's FC2 and combine
+    of the GPU's h and against the plain oracle."""
+    spec = S.spec_of(dict(S.spec_of(cfg), **overrides))
+    inp = S.generate(spec)
+    got, plan, ws, _ = run_layer(inp, spec)
+    layer_check(got, inp, spec, spec["mode"], plan, ws, raw_required=True,
+                what=f"{spec['name']} {overrides} all {spec['T']} tokens")
+
+
 def test_lora_bridges_full_size_ep8_prefill():
     """The LoRA bridges on the EP8 prefill shard at full size (32768 tokens,
     T*k = 524288 pairs: the bf16 delta is 6.4 GB and the down-LoRA input 3.2
