@@ -87,6 +87,47 @@ def test_lora_bridges(name, mode, tactic):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("name,shard,mode,tactic,tiled", [("decode", dict(E_l=6, off=1), "w4a16", (0, 16), False),
+                                                          ("prefill", {}, "w4a8", (4, 20), True)])
+def test_graph_replay_with_lora_bridges(name, shard, mode, tactic, tiled):
+    """The step with the LoRA bridges and SwigluBias captured into a HIP
+    graph (the zeroing of the down-LoRA rows outside the shard is a kernel,
+    not a memset node): every replay, with eager work between replays, gives
+    the eager output and down-LoRA rows bit for bit, the rows outside the
+    shard rewritten as +0."""
+    spec = S.spec_of(dict(SHAPES[name], **shard, activation="swiglu_bias", lora=True))
+    inp = S.generate(spec)
+    eager, plan, ws, d = run_layer(inp, spec, mode=mode, tactic=tactic, lora_out=True, tiled=tiled)
+    eager_rows = d["activation_lora_input"].clone()
+    prob = B.make_problem(num_tokens=spec["T"], hidden_size=spec["H"], intermediate_size=spec["I"],
+                          num_experts=spec["E_g"], local_expert_offset=spec["off"],
+                          local_num_experts=spec["E_l"], top_k=spec["k"], act_mode=mode,
+                          topk_packed=inp.get("topk_packed") is not None, out_dtype="f32", tactic=tactic,
+                          activation="swiglu_bias", weight_format="mxfp4_tiled" if tiled else "mxfp4")
+    ts = B.make_tensors(prob, **d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        B.situ_moe_run(plan, ts, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.situ_moe_run(plan, ts, ws)
+    inv = M.route(inp["topk_ids"], spec["off"], spec["E_l"])[3]
+    assert np.any(inv < 0) and np.any(inv >= 0)
+    for rep in range(3):
+        d["out"].fill_(float("nan"))
+        d["activation_lora_input"].fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda") * 3.0     # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        got = d["out"].float().cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep}"
+        assert torch.equal(d["activation_lora_input"].view(torch.int16), eager_rows.view(torch.int16)), f"rows {rep}"
+        del junk
+
+
 @pytest.mark.parametrize("cfg,overrides", [(1, {"weight_format": "nvfp4"}), (2, {"weight_format": "nvfp4"}),
                                            (2, {"activation": "swiglu_bias"})])
 def test_decode_variants_full_size(cfg, overrides):
